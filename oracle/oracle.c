@@ -1,0 +1,276 @@
+/*
+ * Oracle for the gated ReLU linear-attention token mixer: a plain, slow,
+ * fp64 CPU implementation of what the GPU path computes.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load or call this library.  It shares no
+ * code, header, table or helper with the HIP library; neither includes the
+ * other.
+ *
+ * Sources (pages, sections):
+ *  [V2]  "SANA-Video 2.0: Hybrid Linear Attention with Attention Residuals for
+ *        Efficient Video Generation" (arXiv 2607.21553), Section 2, paragraph
+ *        "Gated linear attention", Eq. (1): state, denominator with +eps,
+ *        sigmoid output gate.
+ *  [V1]  "SANA-Video: Efficient Video Generation with Block Linear Diffusion
+ *        Transformer" (paper notes), Section 3.2 "Linear Attention with RoPE":
+ *        phi = ReLU; RoPE applied after ReLU, in the numerator only; the
+ *        denominator keeps the un-rotated phi; layout (B, N, H, D).
+ *  [V1c] same page, Section 3.4 "Block Linear Attention with Constant-Memory
+ *        KV Cache": the causal form carries the running sum of states
+ *        phi(K)^T V and the running sum of phi(K) across blocks.
+ *
+ * Readings where the pages are silent (each one is listed in the design
+ * notes of the repository):
+ *  - 3D RoPE: d is split (d/4, 3d/8, 3d/8) over the (t, h, w) axes, in that
+ *    order; on each axis a independent rotary rotation of adjacent pairs
+ *    (2i, 2i+1) of that axis' slice by angle pos_a * theta^(-2i/d_a).
+ *    theta <= 0 turns the rotation off (identity).
+ *  - positions are integer grid indices; token n of a [T, Hs, Ws] grid has
+ *    t = n / (Hs*Ws), h = (n / Ws) % Hs, w = n % Ws; pos0[] shifts them.
+ *  - eps is added to the dot product (den = phi(q).z + eps).
+ *  - the gate g has the shape of the output; sigma(x) = 1 / (1 + exp(-x)).
+ *  - block-causal: blocks of F latent frames; a token of block b uses the
+ *    state and normaliser summed over every token of blocks 0..b (its own
+ *    block included, so attention inside a block is bidirectional).
+ *
+ * Arithmetic: inputs arrive as float (every bf16 value is exact in float);
+ * everything is computed and returned in double.  Sums run in increasing
+ * token order.  OpenMP only distributes independent (batch, head) or
+ * (batch, token) work; it never splits a sum.
+ */
+#include <math.h>
+#include <stdint.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+#include <stdlib.h>
+#include <string.h>
+
+#define ORA_OK 0
+#define ORA_BAD_ARG 1
+#define ORA_NO_MEM 2
+
+/* Token n of a t-major [T, Hs, Ws] latent grid -> (t, h, w) ([V1] Section 3.3
+ * pseudocode reshapes (B, T*H*W, D) to (B, T, H, W, D): t slowest, w fastest). */
+static void grid_position(int64_t n, int64_t Hs, int64_t Ws, const int64_t *pos0,
+                          int64_t pos[3]) {
+  pos[0] = n / (Hs * Ws);
+  pos[1] = (n / Ws) % Hs;
+  pos[2] = n % Ws;
+  if (pos0) {
+    pos[0] += pos0[0];
+    pos[1] += pos0[1];
+    pos[2] += pos0[2];
+  }
+}
+
+/* 3D rotary embedding of one feature vector x (length d) at grid position
+ * pos = (t, h, w), written to y (y may not alias x). */
+void ora_rope(const double *x, double *y, int64_t d, const int64_t pos[3], double theta) {
+  int64_t width[3] = {d / 4, 3 * d / 8, 3 * d / 8};
+  int64_t offset = 0;
+  if (!(theta > 0.0)) {
+    memcpy(y, x, (size_t)d * sizeof(double));
+    return;
+  }
+  for (int a = 0; a < 3; ++a) {
+    int64_t da = width[a];
+    for (int64_t i = 0; i < da / 2; ++i) {
+      double freq = pow(theta, -2.0 * (double)i / (double)da);
+      double angle = (double)pos[a] * freq;
+      double c = cos(angle), s = sin(angle);
+      double x0 = x[offset + 2 * i], x1 = x[offset + 2 * i + 1];
+      y[offset + 2 * i] = x0 * c - x1 * s;
+      y[offset + 2 * i + 1] = x0 * s + x1 * c;
+    }
+    offset += da;
+  }
+}
+
+static int check_shape(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, int64_t d,
+                       int64_t F) {
+  if (B < 1 || H < 1 || T < 1 || Hs < 1 || Ws < 1) return ORA_BAD_ARG;
+  if (d < 16 || d % 16 != 0) return ORA_BAD_ARG;
+  if (F < 0 || (F > 0 && T % F != 0)) return ORA_BAD_ARG;
+  return ORA_OK;
+}
+
+/* Number of temporal blocks: F = 0 (or F = T) is the non-causal operator. */
+int64_t ora_num_blocks(int64_t T, int64_t F) { return (F <= 0) ? 1 : T / F; }
+
+/*
+ * State and normaliser ([V1] Section 3.2 pseudocode steps 1-4, [V2] Eq. 1):
+ *   z        = sum_n phi(k_n)
+ *   S[p][e]  = sum_n RoPE_n(phi(k_n))[p] * v_n[e]        (d x d, rows = key dim)
+ * In block-causal mode ([V1c]) the values written for block b are the sums
+ * over every token of blocks 0..b.
+ *
+ * k, v : [B, N, H, d] float, N = T*Hs*Ws
+ * S    : [B, H, nb, d, d] double (output)   z : [B, H, nb, d] double (output)
+ */
+int ora_state(const float *k, const float *v, int64_t B, int64_t H, int64_t T, int64_t Hs,
+              int64_t Ws, int64_t d, int64_t F, double theta, const int64_t *pos0, double *S,
+              double *z) {
+  if (!k || !v || !S || !z) return ORA_BAD_ARG;
+  int rc = check_shape(B, H, T, Hs, Ws, d, F);
+  if (rc) return rc;
+  const int64_t N = T * Hs * Ws;
+  const int64_t nb = ora_num_blocks(T, F);
+  const int64_t tokens_per_block = N / nb;
+  int failed = 0;
+
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  for (int64_t b = 0; b < B; ++b) {
+    for (int64_t h = 0; h < H; ++h) {
+      double *Sacc = (double *)calloc((size_t)(d * d), sizeof(double));
+      double *zacc = (double *)calloc((size_t)d, sizeof(double));
+      double *phik = (double *)malloc((size_t)d * sizeof(double));
+      double *rotk = (double *)malloc((size_t)d * sizeof(double));
+      double *vrow = (double *)malloc((size_t)d * sizeof(double));
+      if (!Sacc || !zacc || !phik || !rotk || !vrow) {
+#pragma omp atomic write
+        failed = 1;
+      } else {
+        for (int64_t n = 0; n < N; ++n) {
+          const float *kn = k + ((b * N + n) * H + h) * d;
+          const float *vn = v + ((b * N + n) * H + h) * d;
+          int64_t pos[3];
+          grid_position(n, Hs, Ws, pos0, pos);
+          for (int64_t p = 0; p < d; ++p) {
+            double x = (double)kn[p];
+            phik[p] = x > 0.0 ? x : 0.0; /* phi = ReLU */
+            vrow[p] = (double)vn[p];
+          }
+          ora_rope(phik, rotk, d, pos, theta); /* RoPE after ReLU, numerator only */
+          for (int64_t p = 0; p < d; ++p) {
+            zacc[p] += phik[p]; /* normaliser: un-rotated phi(k) */
+            for (int64_t e = 0; e < d; ++e) Sacc[p * d + e] += rotk[p] * vrow[e];
+          }
+          if ((n + 1) % tokens_per_block == 0) { /* end of a temporal block */
+            int64_t blk = n / tokens_per_block;
+            double *Sout = S + ((b * H + h) * nb + blk) * d * d;
+            double *zout = z + ((b * H + h) * nb + blk) * d;
+            memcpy(Sout, Sacc, (size_t)(d * d) * sizeof(double));
+            memcpy(zout, zacc, (size_t)d * sizeof(double));
+          }
+        }
+      }
+      free(Sacc);
+      free(zacc);
+      free(phik);
+      free(rotk);
+      free(vrow);
+    }
+  }
+  return failed ? ORA_NO_MEM : ORA_OK;
+}
+
+/*
+ * Output for a list of tokens ([V1] Section 3.2 steps 3-5 with the gate of
+ * [V2] Eq. 1):
+ *   num[e] = sum_p RoPE_i(phi(q_i))[p] * S[p][e]
+ *   den    = sum_p phi(q_i)[p] * z[p] + eps
+ *   out[e] = num[e] / den * sigma(g_i[e])
+ * using the state of the token's block (block-causal) or the single state.
+ *
+ * q, g   : [B, N, H, d] float
+ * S, z   : as written by ora_state
+ * tokens : ntok token indices in [0, N), or NULL for all N tokens in order
+ * out    : [B, ntok, H, d] double
+ */
+int ora_apply(const float *q, const float *g, const double *S, const double *z, int64_t B,
+              int64_t H, int64_t T, int64_t Hs, int64_t Ws, int64_t d, int64_t F, double theta,
+              double eps, const int64_t *pos0, const int64_t *tokens, int64_t ntok,
+              double *out) {
+  if (!q || !g || !S || !z || !out) return ORA_BAD_ARG;
+  int rc = check_shape(B, H, T, Hs, Ws, d, F);
+  if (rc) return rc;
+  const int64_t N = T * Hs * Ws;
+  const int64_t nb = ora_num_blocks(T, F);
+  const int64_t tokens_per_block = N / nb;
+  if (!tokens) ntok = N;
+  if (ntok < 0) return ORA_BAD_ARG;
+  for (int64_t j = 0; tokens && j < ntok; ++j)
+    if (tokens[j] < 0 || tokens[j] >= N) return ORA_BAD_ARG;
+  int failed = 0;
+
+#pragma omp parallel for collapse(2) schedule(dynamic, 64)
+  for (int64_t b = 0; b < B; ++b) {
+    for (int64_t j = 0; j < ntok; ++j) {
+      double *phiq = (double *)malloc((size_t)d * sizeof(double));
+      double *rotq = (double *)malloc((size_t)d * sizeof(double));
+      if (!phiq || !rotq) {
+#pragma omp atomic write
+        failed = 1;
+      } else {
+        int64_t n = tokens ? tokens[j] : j;
+        int64_t blk = n / tokens_per_block;
+        int64_t pos[3];
+        grid_position(n, Hs, Ws, pos0, pos);
+        for (int64_t h = 0; h < H; ++h) {
+          const float *qn = q + ((b * N + n) * H + h) * d;
+          const float *gn = g + ((b * N + n) * H + h) * d;
+          const double *Sh = S + ((b * H + h) * nb + blk) * d * d;
+          const double *zh = z + ((b * H + h) * nb + blk) * d;
+          double *on = out + ((b * ntok + j) * H + h) * d;
+          for (int64_t p = 0; p < d; ++p) {
+            double x = (double)qn[p];
+            phiq[p] = x > 0.0 ? x : 0.0;
+          }
+          ora_rope(phiq, rotq, d, pos, theta);
+          double den = 0.0;
+          for (int64_t p = 0; p < d; ++p) den += phiq[p] * zh[p];
+          den += eps;
+          for (int64_t e = 0; e < d; ++e) {
+            double num = 0.0;
+            for (int64_t p = 0; p < d; ++p) num += rotq[p] * Sh[p * d + e];
+            double gate = 1.0 / (1.0 + exp(-(double)gn[e]));
+            on[e] = num / den * gate;
+          }
+        }
+      }
+      free(phiq);
+      free(rotq);
+    }
+  }
+  return failed ? ORA_NO_MEM : ORA_OK;
+}
+
+/* Whole operator: ora_state followed by ora_apply over every token.
+ * out : [B, N, H, d] double. */
+int ora_forward(const float *q, const float *k, const float *v, const float *g, int64_t B,
+                int64_t H, int64_t T, int64_t Hs, int64_t Ws, int64_t d, int64_t F,
+                double theta, double eps, const int64_t *pos0, double *out) {
+  int rc = check_shape(B, H, T, Hs, Ws, d, F);
+  if (rc) return rc;
+  const int64_t nb = ora_num_blocks(T, F);
+  double *S = (double *)malloc((size_t)(B * H * nb * d * d) * sizeof(double));
+  double *z = (double *)malloc((size_t)(B * H * nb * d) * sizeof(double));
+  if (!S || !z) {
+    free(S);
+    free(z);
+    return ORA_NO_MEM;
+  }
+  rc = ora_state(k, v, B, H, T, Hs, Ws, d, F, theta, pos0, S, z);
+  if (rc == ORA_OK)
+    rc = ora_apply(q, g, S, z, B, H, T, Hs, Ws, d, F, theta, eps, pos0, NULL, 0, out);
+  free(S);
+  free(z);
+  return rc;
+}
+
+/* Number of threads OpenMP will use (reported by the benchmark's CPU leg). */
+int ora_num_threads(void) {
+  int n = 1;
+#pragma omp parallel
+  {
+#pragma omp single
+    {
+#ifdef _OPENMP
+      n = omp_get_num_threads();
+#endif
+    }
+  }
+  return n;
+}

@@ -1,0 +1,411 @@
+"""Pins of the fp64 oracle against facts fixed by the pages and by mathematics.
+
+No GPU.  Each test names the passage or identity it relies on.  Pages:
+[V2] "SANA-Video 2.0" (arXiv 2607.21553), Section 2, Eq. (1);
+[V1] "SANA-Video" notes page, Section 3.2 (ReLU, RoPE after ReLU in the
+numerator only, pseudocode) and Section 3.4 (block-causal carry).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from relu_linear_attention_amd.inputs import host_inputs, round_to_bf16
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# An independent brute-force form, O(N^2), written with complex arithmetic:
+# out_i = sum_j (RoPE(phi(q_i)) . RoPE(phi(k_j))) v_j / (sum_j phi(q_i).phi(k_j) + eps)
+#         * sigmoid(g_i)
+# (the kernelised attention that the linear form re-associates, [V1] Section
+# 3.2).  RoPE here multiplies each adjacent pair, read as a complex number
+# x[2i] + i x[2i+1], by exp(i * pos_a * theta^(-2i/d_a)).
+# ---------------------------------------------------------------------------
+def _positions(T, Hs, Ws, pos0=(0, 0, 0)):
+    n = np.arange(T * Hs * Ws)
+    return np.stack([n // (Hs * Ws) + pos0[0], (n // Ws) % Hs + pos0[1], n % Ws + pos0[2]], 1)
+
+
+def _rope_complex(x, pos, theta):
+    """x: [N, d] real, pos: [N, 3] -> [N, d] rotated."""
+    N, d = x.shape
+    if theta <= 0:
+        return x.copy()
+    widths = [d // 4, 3 * d // 8, 3 * d // 8]
+    out = np.empty_like(x)
+    o = 0
+    for a, da in enumerate(widths):
+        xs = x[:, o:o + da]
+        zc = xs[:, 0::2] + 1j * xs[:, 1::2]
+        freqs = theta ** (-2.0 * np.arange(da // 2) / da)
+        zc = zc * np.exp(1j * pos[:, a:a + 1] * freqs[None, :])
+        out[:, o:o + da:2] = zc.real
+        out[:, o + 1:o + da:2] = zc.imag
+        o += da
+    return out
+
+
+def brute_force(q, k, v, g, grid, F=0, theta=10000.0, eps=1e-6, pos0=(0, 0, 0)):
+    B, N, H, d = q.shape
+    T, Hs, Ws = grid
+    pos = _positions(T, Hs, Ws, pos0)
+    blk = np.zeros(N, dtype=np.int64) if F <= 0 else pos[:, 0] - pos0[0]
+    blk = blk // (F if F > 0 else 1)
+    allowed = blk[None, :] <= blk[:, None]  # [i, j]: j visible from i
+    out = np.empty((B, N, H, d))
+    for b in range(B):
+        for h in range(H):
+            pq = np.maximum(q[b, :, h].astype(np.float64), 0.0)
+            pk = np.maximum(k[b, :, h].astype(np.float64), 0.0)
+            rq, rk = _rope_complex(pq, pos, theta), _rope_complex(pk, pos, theta)
+            A = (rq @ rk.T) * allowed
+            D = (pq @ pk.T) * allowed
+            num = A @ v[b, :, h].astype(np.float64)
+            den = D.sum(1) + eps
+            gate = 1.0 / (1.0 + np.exp(-g[b, :, h].astype(np.float64)))
+            out[b, :, h] = num / den[:, None] * gate
+    return out
+
+
+def _rel_err(a, ref, floor=1e-3):
+    return float(np.max(np.abs(a - ref) / (np.abs(ref) + floor)))
+
+
+# ---------------------------------------------------------------------------
+# worked examples (tests/golden)
+# ---------------------------------------------------------------------------
+def _load_fixture(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        fx = json.load(f)
+    T, Hs, Ws = fx["grid"]
+    N, H, d = T * Hs * Ws, fx["H"], fx["d"]
+    arrs = {}
+    for key in "qkvg":
+        a = np.zeros((1, N, H, d), dtype=np.float32)
+        for tok, feat, val in fx["inputs"][key]:
+            a[0, tok, 0, feat] = val
+        arrs[key] = a
+    return fx, arrs
+
+
+def _expected(entries, shape):
+    e = np.zeros(shape)
+    for tok, feat, val, _expr in entries:
+        e[0, tok, 0, feat] = val
+    return e
+
+
+def test_worked_example_noncausal():
+    fx, a = _load_fixture("worked_example_noncausal.json")
+    out = oracle.forward(a["q"], a["k"], a["v"], a["g"], fx["grid"], 0, fx["theta"], fx["eps"])
+    np.testing.assert_allclose(out, _expected(fx["expected"], out.shape), rtol=1e-12, atol=1e-14)
+
+
+def test_worked_example_block_causal():
+    fx, a = _load_fixture("worked_example_block_causal.json")
+    out = oracle.forward(a["q"], a["k"], a["v"], a["g"], fx["grid"], fx["frames_per_block"],
+                         fx["theta"], fx["eps"])
+    np.testing.assert_allclose(out, _expected(fx["expected"], out.shape), rtol=1e-12, atol=1e-14)
+    nc = oracle.forward(a["q"], a["k"], a["v"], a["g"], fx["grid"], 0, fx["theta"], fx["eps"])
+    np.testing.assert_allclose(nc, _expected(fx["expected_noncausal"], nc.shape), rtol=1e-12,
+                               atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# brute force O(N^2) on tiny inputs
+# ---------------------------------------------------------------------------
+BRUTE_CASES = [
+    # (B, T, Hs, Ws, H, d, theta, F)
+    (1, 2, 4, 4, 2, 32, 10000.0, 0),  # the tiny fp32 workload's shape
+    (2, 3, 2, 4, 3, 16, 10000.0, 0),
+    (1, 4, 4, 4, 2, 64, 100.0, 0),
+    (1, 4, 3, 2, 1, 48, 7.0, 0),  # a strong rotation on every pair
+    (1, 4, 2, 3, 2, 32, 10000.0, 1),
+    (2, 4, 3, 3, 2, 16, 50.0, 2),
+    (1, 3, 3, 1, 1, 112, 10000.0, 3),  # F = T: one block
+]
+
+
+@pytest.mark.parametrize("B,T,Hs,Ws,H,d,theta,F", BRUTE_CASES)
+def test_oracle_matches_brute_force(B, T, Hs, Ws, H, d, theta, F):
+    x = host_inputs(B, T, Hs, Ws, H, d, "f32", seed=11 + d + T)
+    grid = (T, Hs, Ws)
+    got = oracle.forward(x["q"], x["k"], x["v"], x["g"], grid, F, theta, 1e-6)
+    ref = brute_force(x["q"], x["k"], x["v"], x["g"], grid, F, theta, 1e-6)
+    assert _rel_err(got, ref, 1e-12) < 1e-9
+
+
+def test_oracle_state_matches_brute_force_state():
+    # S and z on their own: S = sum_n RoPE(phi(k_n))^T v_n (rows = key dim).
+    T, Hs, Ws, H, d = 2, 3, 2, 2, 32
+    x = host_inputs(1, T, Hs, Ws, H, d, "f32", seed=5)
+    S, z = oracle.state(x["k"], x["v"], (T, Hs, Ws), 0, 10000.0)
+    pos = _positions(T, Hs, Ws)
+    for h in range(H):
+        pk = np.maximum(x["k"][0, :, h].astype(np.float64), 0)
+        rk = _rope_complex(pk, pos, 10000.0)
+        np.testing.assert_allclose(S[0, h, 0], rk.T @ x["v"][0, :, h].astype(np.float64),
+                                   rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(z[0, h, 0], pk.sum(0), rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# RoPE closed forms
+# ---------------------------------------------------------------------------
+def test_rope_unit_vector_closed_form():
+    # x = e_{o_a} at pos_a = 1 rotates pair 0 of axis a by 1 rad.
+    d = 32
+    offsets = {0: 0, 1: 8, 2: 20}
+    for axis, off in offsets.items():
+        x = np.zeros(d)
+        x[off] = 1.0
+        pos = [0, 0, 0]
+        pos[axis] = 1
+        y = oracle.rope(x, pos, 10000.0)
+        expect = np.zeros(d)
+        expect[off], expect[off + 1] = math.cos(1.0), math.sin(1.0)
+        np.testing.assert_allclose(y, expect, atol=1e-15)
+
+
+def test_rope_pair_frequencies():
+    # d=32: t slice has 4 pairs with frequencies 10000^(-2i/8) = 10^-i;
+    # h slice has 6 pairs with 10^(-2i/3).  Pair i of a slice rotated at pos 1
+    # maps (1, 0) to (cos w_i, sin w_i); for the second slot (0, 1) maps to
+    # (-sin w_i, cos w_i).
+    d = 32
+    for axis, off, width, freqs in [
+        (0, 0, 8, [1.0, 0.1, 0.01, 0.001]),
+        (1, 8, 12, [10 ** (-2 * i / 3) for i in range(6)]),
+        (2, 20, 12, [10 ** (-2 * i / 3) for i in range(6)]),
+    ]:
+        for i, w in enumerate(freqs):
+            pos = [0, 0, 0]
+            pos[axis] = 3
+            x = np.zeros(d)
+            x[off + 2 * i + 1] = 1.0
+            y = oracle.rope(x, pos, 10000.0)
+            expect = np.zeros(d)
+            expect[off + 2 * i] = -math.sin(3 * w)
+            expect[off + 2 * i + 1] = math.cos(3 * w)
+            np.testing.assert_allclose(y, expect, atol=1e-14)
+
+
+def test_rope_axis_isolation_and_norm():
+    rng = np.random.default_rng(3)
+    d = 128
+    x = rng.standard_normal(d)
+    y = oracle.rope(x, (0, 1, 0), 10000.0)  # only the h slice [32, 80) moves
+    np.testing.assert_array_equal(y[:32], x[:32])
+    np.testing.assert_array_equal(y[80:], x[80:])
+    assert np.max(np.abs(y[32:80] - x[32:80])) > 1e-3
+    for pos in [(0, 0, 0), (5, 17, 33), (240, 44, 79)]:
+        y = oracle.rope(x, pos, 10000.0)
+        assert abs(np.linalg.norm(y) - np.linalg.norm(x)) < 1e-12
+    np.testing.assert_array_equal(oracle.rope(x, (0, 0, 0), 10000.0), x)
+
+
+def test_rope_large_angle():
+    # t = 240 (the 60 s workload): the rotation is still exact to fp64.
+    d = 128
+    x = np.zeros(d)
+    x[0] = 1.0
+    y = oracle.rope(x, (240, 0, 0), 10000.0)
+    assert abs(y[0] - math.cos(240.0)) < 1e-13 and abs(y[1] - math.sin(240.0)) < 1e-13
+
+
+# ---------------------------------------------------------------------------
+# identities of the whole operator
+# ---------------------------------------------------------------------------
+def _plain_linear_attention(q, k, v, g, eps):
+    """ReLU linear attention without positions, in matrix form:
+    phi(Q) (phi(K)^T V) / (phi(Q) sum phi(K) + eps) * sigmoid(G)."""
+    B, N, H, d = q.shape
+    out = np.empty((B, N, H, d))
+    for b in range(B):
+        for h in range(H):
+            pq = np.maximum(q[b, :, h].astype(np.float64), 0)
+            pk = np.maximum(k[b, :, h].astype(np.float64), 0)
+            kv = pk.T @ v[b, :, h].astype(np.float64)
+            den = pq @ pk.sum(0) + eps
+            out[b, :, h] = (pq @ kv) / den[:, None] / (1 + np.exp(-g[b, :, h].astype(np.float64)))
+    return out
+
+
+def test_no_rotation_reduces_to_plain_relu_linear_attention():
+    x = host_inputs(2, 2, 3, 5, 3, 64, "f32", seed=7)
+    got = oracle.forward(x["q"], x["k"], x["v"], x["g"], (2, 3, 5), 0, 0.0, 1e-6)
+    ref = _plain_linear_attention(x["q"], x["k"], x["v"], x["g"], 1e-6)
+    assert _rel_err(got, ref, 1e-12) < 1e-10
+
+
+def test_permutation_equivariance_without_rotation():
+    x = host_inputs(1, 2, 4, 4, 2, 32, "f32", seed=8)
+    grid = (2, 4, 4)
+    perm = np.random.default_rng(0).permutation(32)
+    out = oracle.forward(x["q"], x["k"], x["v"], x["g"], grid, 0, 0.0)
+    xp = {n: a[:, perm] for n, a in x.items()}
+    outp = oracle.forward(xp["q"], xp["k"], xp["v"], xp["g"], grid, 0, 0.0)
+    np.testing.assert_allclose(outp, out[:, perm], rtol=1e-11, atol=1e-14)
+
+
+def test_rotation_breaks_permutation_equivariance():
+    # guard: with the rotation on, the same permutation must change the result
+    x = host_inputs(1, 2, 4, 4, 2, 32, "f32", seed=8)
+    grid = (2, 4, 4)
+    perm = np.random.default_rng(0).permutation(32)
+    out = oracle.forward(x["q"], x["k"], x["v"], x["g"], grid, 0, 10000.0)
+    xp = {n: a[:, perm] for n, a in x.items()}
+    outp = oracle.forward(xp["q"], xp["k"], xp["v"], xp["g"], grid, 0, 10000.0)
+    assert np.max(np.abs(outp - out[:, perm])) > 1e-4
+
+
+def test_relative_position_invariance():
+    # shifting every token's (t, h, w) by the same offset leaves outputs unchanged
+    x = host_inputs(1, 3, 2, 4, 2, 32, "f32", seed=9)
+    grid = (3, 2, 4)
+    a = oracle.forward(x["q"], x["k"], x["v"], x["g"], grid, 0, 100.0)
+    b = oracle.forward(x["q"], x["k"], x["v"], x["g"], grid, 0, 100.0, pos0=(7, 11, 13))
+    assert _rel_err(b, a, 1e-12) < 1e-9
+
+
+def test_scale_invariance_and_linearity():
+    x = host_inputs(1, 2, 3, 3, 2, 32, "f32", seed=10)
+    grid = (2, 3, 3)
+    base = oracle.forward(x["q"], x["k"], x["v"], x["g"], grid, 0, 10000.0, eps=0.0)
+    sc = oracle.forward(4.0 * x["q"], 0.25 * x["k"], x["v"], x["g"], grid, 0, 10000.0, eps=0.0)
+    np.testing.assert_allclose(sc, base, rtol=1e-10, atol=1e-13)
+    lin = oracle.forward(x["q"], x["k"], -8.0 * x["v"], x["g"], grid, 0, 10000.0, eps=0.0)
+    np.testing.assert_allclose(lin, -8.0 * base, rtol=1e-11, atol=1e-13)
+
+
+def test_gate():
+    x = host_inputs(1, 2, 2, 2, 2, 16, "f32", seed=12)
+    grid = (2, 2, 2)
+    zero = np.zeros_like(x["g"])
+    half = oracle.forward(x["q"], x["k"], x["v"], zero, grid)
+    full = oracle.forward(x["q"], x["k"], x["v"], zero + 1e4, grid)  # sigmoid = 1
+    np.testing.assert_allclose(half, 0.5 * full, rtol=1e-15, atol=0)
+    gated = oracle.forward(x["q"], x["k"], x["v"], x["g"], grid)
+    sig = 1.0 / (1.0 + np.exp(-x["g"].astype(np.float64)))
+    np.testing.assert_allclose(gated, full * sig, rtol=1e-13, atol=1e-16)
+
+
+def test_single_token_closed_form():
+    # N = 1: the rotation cancels in phi_r(q).phi_r(k) (same position):
+    # out = v * sigmoid(g) * s / (s + eps), s = phi(q).phi(k)
+    rng = np.random.default_rng(13)
+    d = 32
+    q, k, v, g = (rng.standard_normal((1, 1, 1, d)).astype(np.float32) for _ in range(4))
+    s = float(np.maximum(q, 0).astype(np.float64).ravel() @ np.maximum(k, 0).astype(np.float64).ravel())
+    for pos0 in [(0, 0, 0), (5, 3, 7)]:
+        out = oracle.forward(q, k, v, g, (1, 1, 1), 0, 10000.0, 1e-6, pos0=pos0)
+        ref = v.astype(np.float64) / (1 + np.exp(-g.astype(np.float64))) * s / (s + 1e-6)
+        np.testing.assert_allclose(out, ref, rtol=1e-12)
+
+
+def test_degenerate_rows_are_exact_zeros():
+    x = host_inputs(1, 2, 3, 3, 2, 32, "f32", seed=14)
+    grid = (2, 3, 3)
+    q = x["q"].copy()
+    q[0, 4, 1] = -np.abs(q[0, 4, 1]) - 0.1  # all-negative query row
+    out = oracle.forward(q, x["k"], x["v"], x["g"], grid)
+    assert np.all(out[0, 4, 1] == 0.0)
+    k_neg = -np.abs(x["k"]) - 0.1  # every key negative -> S = 0, z = 0
+    out = oracle.forward(x["q"], k_neg, x["v"], x["g"], grid)
+    assert np.all(out == 0.0)
+    out = oracle.forward(x["q"], x["k"], np.zeros_like(x["v"]), x["g"], grid)
+    assert np.all(out == 0.0)
+
+
+# ---------------------------------------------------------------------------
+# block-causal structure ([V1] Section 3.4)
+# ---------------------------------------------------------------------------
+def test_block_causal_last_block_equals_noncausal():
+    x = host_inputs(1, 6, 3, 2, 2, 32, "f32", seed=15)
+    grid = (6, 3, 2)
+    nc = oracle.forward(x["q"], x["k"], x["v"], x["g"], grid, 0)
+    bc = oracle.forward(x["q"], x["k"], x["v"], x["g"], grid, 2)
+    last = slice(4 * 6, 6 * 6)
+    assert _rel_err(bc[:, last], nc[:, last], 1e-12) < 1e-10
+    assert np.max(np.abs(bc[:, :24] - nc[:, :24])) > 1e-4  # earlier blocks differ
+
+
+def test_block_causal_equals_truncated_grid():
+    # block b equals the non-causal operator on the first (b+1)*F frames
+    T, Hs, Ws, F = 6, 2, 3, 2
+    x = host_inputs(1, T, Hs, Ws, 2, 16, "f32", seed=16)
+    bc = oracle.forward(x["q"], x["k"], x["v"], x["g"], (T, Hs, Ws), F)
+    per_frame = Hs * Ws
+    for b in range(T // F):
+        n1 = (b + 1) * F * per_frame
+        n0 = b * F * per_frame
+        sub = {n: a[:, :n1] for n, a in x.items()}
+        nc = oracle.forward(sub["q"], sub["k"], sub["v"], sub["g"], ((b + 1) * F, Hs, Ws), 0)
+        assert _rel_err(bc[:, n0:n1], nc[:, n0:n1], 1e-12) < 1e-10
+
+
+def test_block_causal_one_block_is_noncausal():
+    x = host_inputs(1, 3, 2, 2, 2, 16, "f32", seed=17)
+    a = oracle.forward(x["q"], x["k"], x["v"], x["g"], (3, 2, 2), 3)
+    b = oracle.forward(x["q"], x["k"], x["v"], x["g"], (3, 2, 2), 0)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_block_states_are_running_sums():
+    T, Hs, Ws, F = 4, 2, 2, 1
+    x = host_inputs(1, T, Hs, Ws, 1, 16, "f32", seed=18)
+    S, z = oracle.state(x["k"], x["v"], (T, Hs, Ws), F, 10000.0)
+    S1, z1 = oracle.state(x["k"], x["v"], (T, Hs, Ws), 0, 10000.0)
+    np.testing.assert_allclose(S[0, 0, -1], S1[0, 0, 0], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(z[0, 0, -1], z1[0, 0, 0], rtol=1e-14)
+    # first block alone = state of the first frame's grid
+    S0, z0 = oracle.state(x["k"][:, :4], x["v"][:, :4], (1, Hs, Ws), 0, 10000.0)
+    np.testing.assert_allclose(S[0, 0, 0], S0[0, 0, 0], rtol=1e-14, atol=1e-15)
+
+
+def test_apply_token_subset_matches_full():
+    x = host_inputs(1, 2, 3, 4, 2, 32, "f32", seed=19)
+    grid = (2, 3, 4)
+    full = oracle.forward(x["q"], x["k"], x["v"], x["g"], grid, 1)
+    S, z = oracle.state(x["k"], x["v"], grid, 1)
+    toks = np.array([23, 0, 11, 12, 5])
+    sub = oracle.apply(x["q"], x["g"], S, z, grid, 1, tokens=toks)
+    np.testing.assert_array_equal(sub, full[:, toks])
+
+
+def test_oracle_rejects_bad_shapes():
+    x = host_inputs(1, 2, 2, 2, 1, 16, "f32", seed=0)
+    with pytest.raises(RuntimeError):
+        oracle.forward(x["q"], x["k"], x["v"], x["g"], (2, 2, 2), 3)  # F does not divide T
+
+
+# ---------------------------------------------------------------------------
+# input generator
+# ---------------------------------------------------------------------------
+def test_bf16_rounding_is_round_to_nearest_even():
+    import torch
+
+    rng = np.random.default_rng(0)
+    x = (rng.standard_normal(100000) * np.exp(rng.uniform(-20, 20, 100000))).astype(np.float32)
+    # ties: values exactly halfway between two bf16 numbers
+    ties = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8)], dtype=np.float32)
+    x = np.concatenate([x, ties])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(round_to_bf16(x), ref)
+    np.testing.assert_array_equal(round_to_bf16(ties), np.array([1.0, 1.0 + 2.0 ** -6, -1.0],
+                                                                dtype=np.float32))
+
+
+def test_host_inputs_are_seeded():
+    a = host_inputs(1, 2, 2, 2, 2, 16, "bf16", seed=3)
+    b = host_inputs(1, 2, 2, 2, 2, 16, "bf16", seed=3)
+    c = host_inputs(1, 2, 2, 2, 2, 16, "bf16", seed=4)
+    for n in "qkvg":
+        np.testing.assert_array_equal(a[n], b[n])
+        assert not np.array_equal(a[n], c[n])
+        np.testing.assert_array_equal(round_to_bf16(a[n]), a[n])
