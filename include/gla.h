@@ -1,0 +1,159 @@
+/*
+ * gla.h - C ABI of libgla.so, the gated ReLU linear-attention token mixer on
+ * AMD MI355X (CDNA4, gfx950).
+ *
+ * The operator (per batch b and head h; phi = ReLU; RoPE = 3D rotary
+ * embedding over the (t, h, w) latent grid):
+ *
+ *   S   = sum_n RoPE_n(phi(k_n))^T v_n          d x d, rows = key feature
+ *   z   = sum_n phi(k_n)                         d
+ *   o_i = (RoPE_i(phi(q_i)) S) / (phi(q_i) . z + eps)  *  sigmoid(g_i)
+ *
+ * Sources: "SANA-Video 2.0: Hybrid Linear Attention with Attention Residuals
+ * for Efficient Video Generation" (arXiv 2607.21553), Section 2, paragraph
+ * "Gated linear attention", Eq. (1) (the +eps denominator and the sigmoid
+ * output gate g); "SANA-Video: Efficient Video Generation with Block Linear
+ * Diffusion Transformer" (paper notes), Section 3.2 "Linear Attention with
+ * RoPE" (ReLU feature map, RoPE applied after ReLU and only in the
+ * numerator, tensors laid out (B, N, H, D)) and Section 3.4 "Block Linear
+ * Attention with Constant-Memory KV Cache" (the running sums of phi(K)^T V
+ * and phi(K) carried across temporal blocks).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout.  q, k, v, g and out are dense [B, N, H, d] arrays (d fastest),
+ *   N = T * Hs * Ws, tokens in t-major order: token n sits at
+ *   t = n / (Hs*Ws), h = (n / Ws) % Hs, w = n % Ws.
+ * Element type.  GLA_BF16: every tensor is bfloat16 (raw 16-bit storage);
+ *   GLA_F32: every tensor is float.  Arithmetic is fp32 in both cases
+ *   (bf16 matrix-core products accumulate in fp32); bf16 outputs are rounded
+ *   to nearest-even once, at the store.
+ * Positions and RoPE.  d is split (d/4, 3d/8, 3d/8) over (t, h, w); on each
+ *   axis the adjacent feature pairs (2i, 2i+1) of that axis' slice rotate by
+ *   pos_axis * rope_theta^(-2i/d_axis).  rope_theta <= 0 disables the
+ *   rotation.  Positions are the integer grid indices starting at 0.
+ * Supported sizes.  B, H, T, Hs, Ws >= 1; 16 <= d <= 128 with d % 16 == 0.
+ *   bf16 with d = 64 or d = 128 runs on the matrix-core kernels; every other
+ *   supported case runs on the vector kernels.
+ * Memory.  Every tensor pointer is device memory owned by the caller; the
+ *   library neither frees nor keeps any of them.  out may not overlap an
+ *   input.
+ * Streams.  All work is enqueued on `stream` (NULL = the null stream) with
+ *   no host synchronisation; GLA_OK means "enqueued".  Errors raised by a
+ *   kernel at run time surface at the caller's next synchronisation.
+ * Errors.  Arguments are validated on the host before any HIP call; a
+ *   failing call enqueues nothing.  gla_last_error() returns a description
+ *   of the last failure on the calling thread.  No C++ exception crosses
+ *   this interface.
+ * Determinism.  For identical inputs, shapes and device, results are
+ *   bitwise identical run to run (fixed-order reductions, no float atomics).
+ */
+#ifndef GLA_H
+#define GLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *hipStream_t;
+
+typedef enum {
+  GLA_OK = 0,
+  GLA_ERR_INVALID_ARG = 1, /* a null pointer, a bad size, overlapping out */
+  GLA_ERR_UNSUPPORTED = 2, /* valid arguments the library cannot run */
+  GLA_ERR_ALLOC = 3,       /* workspace allocation failed */
+  GLA_ERR_HIP = 4          /* a HIP runtime call or a launch failed */
+} gla_status;
+
+typedef enum { GLA_BF16 = 0, GLA_F32 = 1 } gla_dtype;
+
+/*
+ * Non-causal operator ("SANA-Video 2.0" Eq. (1) without beta, RMSNorm and
+ * W_o; "SANA-Video" Section 3.2).  Every token reads the state and
+ * normaliser of all N tokens of its (batch, head).
+ * The workspace is taken stream-ordered on `stream` (hipMallocAsync) and
+ * released the same way; GLA_ERR_ALLOC if that fails.
+ */
+gla_status gla_forward(const void *q, const void *k, const void *v, const void *g, void *out,
+                       int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, int64_t d,
+                       float rope_theta, float eps, gla_dtype dtype, hipStream_t stream);
+
+/*
+ * Block-causal operator ("SANA-Video" Section 3.4): the T latent frames form
+ * T / frames_per_block temporal blocks of frames_per_block * Hs * Ws
+ * consecutive tokens.  A token of block b reads the state and normaliser
+ * summed over every token of blocks 0..b (its own block included, so
+ * attention within a block is bidirectional).  Positions stay absolute.
+ * frames_per_block must divide T; frames_per_block == T gives gla_forward.
+ */
+gla_status gla_block_causal_forward(const void *q, const void *k, const void *v, const void *g,
+                                    void *out, int64_t B, int64_t H, int64_t T, int64_t Hs,
+                                    int64_t Ws, int64_t d, int64_t frames_per_block,
+                                    float rope_theta, float eps, gla_dtype dtype,
+                                    hipStream_t stream);
+
+/*
+ * Workspace size in bytes for one call with these sizes on the current
+ * device (frames_per_block = 0: non-causal).  The size depends on the
+ * device's compute-unit count.  Writes *bytes; GLA_ERR_INVALID_ARG on bad
+ * sizes.
+ */
+gla_status gla_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws,
+                               int64_t d, int64_t frames_per_block, gla_dtype dtype,
+                               size_t *bytes);
+
+/*
+ * Either operator with a caller-owned workspace (device memory, at least
+ * gla_workspace_bytes() bytes, 256-byte aligned); frames_per_block = 0 is
+ * the non-causal operator.  Allocates nothing.  Calls that share a
+ * workspace must be ordered on one stream.
+ */
+gla_status gla_forward_ws(const void *q, const void *k, const void *v, const void *g, void *out,
+                          int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, int64_t d,
+                          int64_t frames_per_block, float rope_theta, float eps, gla_dtype dtype,
+                          void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Diagnostic export of the state and normaliser ("SANA-Video" Section 3.2
+ * steps 3-4, Section 3.4 cache): S_out [B, H, nb, d, d] and z_out
+ * [B, H, nb, d] as float (device memory), nb = T / frames_per_block (1 when
+ * frames_per_block = 0).  Block b holds the sums over blocks 0..b.  These
+ * are the fp32 values the output stage reads (before any bf16 rounding).
+ */
+gla_status gla_state(const void *k, const void *v, float *S_out, float *z_out, int64_t B,
+                     int64_t H, int64_t T, int64_t Hs, int64_t Ws, int64_t d,
+                     int64_t frames_per_block, float rope_theta, gla_dtype dtype,
+                     hipStream_t stream);
+
+/* Static description of a status code. */
+const char *gla_status_string(gla_status status);
+
+/* Description of the last failure on the calling thread ("" if none). */
+const char *gla_last_error(void);
+
+/*
+ * Stage timing.  While enabled, every launch the library makes is bracketed
+ * by HIP events recorded on the launch stream.  gla_profile_read() waits for
+ * the recorded events and returns, per stage, the number of launches and
+ * their summed duration in milliseconds.  Stages: 0 rope table, 1 state
+ * partials, 2 reduce/prefix, 3 apply.  Enabling (or disabling) clears the
+ * record.  Meant for one thread at a time.
+ */
+#define GLA_NUM_STAGES 4
+gla_status gla_profile_enable(int enable);
+gla_status gla_profile_read(int64_t launches[GLA_NUM_STAGES], double total_ms[GLA_NUM_STAGES]);
+const char *gla_stage_name(int stage);
+
+/* Which kernels a call with these sizes would run: 1 the matrix-core
+ * kernels (bf16, d = 64 or 128, and a latent grid whose spatial RoPE rows
+ * fit in LDS), 0 the vector kernels, -1 invalid sizes. */
+int gla_uses_matrix_cores(int64_t T, int64_t Hs, int64_t Ws, int64_t d, gla_dtype dtype);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GLA_H */

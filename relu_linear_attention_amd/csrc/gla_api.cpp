@@ -1,0 +1,463 @@
+// Host side of libgla.so: argument validation, work decomposition, workspace
+// handling, stage timing and the C entry points declared in include/gla.h.
+//
+// The operator and its sources are described in include/gla.h ("SANA-Video
+// 2.0" Section 2 Eq. (1); "SANA-Video" Sections 3.2 and 3.4).
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "../../include/gla.h"
+#include "gla_internal.h"
+
+using gla::Plan;
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+gla_status fail(gla_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+gla_status hip_fail(hipError_t e, const char *what) {
+  return fail(GLA_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t *out) { return !__builtin_mul_overflow(a, b, out); }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ---------------------------------------------------------------- devices
+std::mutex g_dev_mu;
+std::vector<int> g_cu_count;  // per device id, 0 = unknown
+
+gla_status device_cus(int *cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if ((int)g_cu_count.size() <= dev) g_cu_count.resize(dev + 1, 0);
+  if (g_cu_count[dev] == 0) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(multiprocessor count)");
+    g_cu_count[dev] = n > 0 ? n : 1;
+  }
+  *cus = g_cu_count[dev];
+  return GLA_OK;
+}
+
+// ---------------------------------------------------------------- validation
+gla_status check_sizes(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, int64_t d,
+                       int64_t F, gla_dtype dtype) {
+  if (B < 1 || H < 1 || T < 1 || Hs < 1 || Ws < 1)
+    return fail(GLA_ERR_INVALID_ARG, "B, H, T, Hs, Ws must be >= 1 (got %lld %lld %lld %lld %lld)",
+                (long long)B, (long long)H, (long long)T, (long long)Hs, (long long)Ws);
+  if (d < 16 || d > 128 || d % 16 != 0)
+    return fail(GLA_ERR_INVALID_ARG, "d must be a multiple of 16 in [16, 128] (got %lld)",
+                (long long)d);
+  if (F < 0) return fail(GLA_ERR_INVALID_ARG, "frames_per_block must be >= 0");
+  if (F > 0 && T % F != 0)
+    return fail(GLA_ERR_INVALID_ARG, "frames_per_block (%lld) must divide T (%lld)",
+                (long long)F, (long long)T);
+  if (dtype != GLA_BF16 && dtype != GLA_F32)
+    return fail(GLA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  int64_t hw, n, bn, bnh, elems, bytes;
+  if (!mul_ok(Hs, Ws, &hw) || !mul_ok(hw, T, &n) || !mul_ok(n, B, &bn) || !mul_ok(bn, H, &bnh) ||
+      !mul_ok(bnh, d, &elems) || !mul_ok(elems, 4, &bytes))
+    return fail(GLA_ERR_INVALID_ARG, "tensor size B*T*Hs*Ws*H*d overflows int64");
+  return GLA_OK;
+}
+
+bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb) {
+  uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+gla_status check_pointers(const void *q, const void *k, const void *v, const void *g,
+                          const void *out, size_t bytes) {
+  if (!q || !k || !v || !g || !out) return fail(GLA_ERR_INVALID_ARG, "null tensor pointer");
+  const void *ins[4] = {q, k, v, g};
+  const char *names[4] = {"q", "k", "v", "g"};
+  for (int i = 0; i < 4; ++i)
+    if (ranges_overlap(out, bytes, ins[i], bytes))
+      return fail(GLA_ERR_INVALID_ARG, "out overlaps input %s", names[i]);
+  return GLA_OK;
+}
+
+// ---------------------------------------------------------------- planning
+// aligned16: every tensor pointer is 16-byte aligned (the matrix-core
+// kernels move 16-byte vectors).
+gla_status make_plan(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, int64_t d,
+                     int64_t F, gla_dtype dtype, float theta, float eps, int cus, bool aligned16,
+                     Plan *p) {
+  gla_status st = check_sizes(B, H, T, Hs, Ws, d, F, dtype);
+  if (st != GLA_OK) return st;
+  Plan P{};
+  P.B = B; P.H = H; P.T = T; P.Hs = Hs; P.Ws = Ws; P.d = d;
+  P.F = (F == 0) ? T : F;
+  P.nb = T / P.F;
+  P.N = T * Hs * Ws;
+  P.L = P.F * Hs * Ws;
+  P.units = B * H * P.nb;
+  P.bf16 = (dtype == GLA_BF16);
+  P.theta = theta;
+  P.eps = eps;
+
+  // RoPE table: T*(d/8) + Hs*(3d/16) + Ws*(3d/16) (cos, sin) entries.
+  const int64_t pt = d / 8, ph = 3 * d / 16, pw = 3 * d / 16;
+  P.tab_t_off = 0;
+  P.tab_h_off = T * pt;
+  P.tab_w_off = P.tab_h_off + Hs * ph;
+  P.tab_entries = P.tab_w_off + Ws * pw;
+
+  // Matrix-core kernels keep the rows of the table they touch in LDS; the
+  // spatial rows must fit next to at least two temporal rows.
+  const int64_t spatial_entries = Hs * ph + Ws * pw;
+  P.mfma = aligned16 && P.bf16 && (d == 64 || d == 128) &&
+           spatial_entries + 2 * pt <= std::min(gla::kStateTabEntries, gla::kApplyTabEntries);
+
+  const int64_t hw = Hs * Ws;
+  const int64_t tile_s = P.mfma ? gla::kStateTile : 16;
+  const int64_t tile_a = P.mfma ? gla::kApplyTile * 8 : 16;
+
+  // State stage: about two workgroups per compute unit in total.
+  const int64_t target_state = 2 * (int64_t)cus;
+  int64_t C = std::max<int64_t>(1, std::min(ceil_div(target_state, P.units), ceil_div(P.L, 256)));
+  int64_t Lc = round_up(ceil_div(P.L, C), tile_s);
+  if (P.mfma) {
+    // temporal rows of a chunk: at most ceil(Lc / hw) + 1
+    int64_t max_rows = (gla::kStateTabEntries - spatial_entries) / pt;
+    int64_t max_len = std::max<int64_t>(tile_s, ((max_rows - 1) * hw) / tile_s * tile_s);
+    Lc = std::min(Lc, max_len);
+  }
+  P.Lc = Lc;
+  P.C = ceil_div(P.L, Lc);
+
+  // Apply stage: about four workgroups per compute unit, 128..4096 tokens each.
+  const int64_t target_apply = 4 * (int64_t)cus;
+  int64_t Lr = round_up(ceil_div(P.units * P.L, target_apply), tile_a);
+  Lr = std::max<int64_t>(tile_a, std::min<int64_t>(Lr, 4096));
+  if (P.mfma) {
+    int64_t max_rows = (gla::kApplyTabEntries - spatial_entries) / pt;
+    int64_t max_len = std::max<int64_t>(tile_a, ((max_rows - 1) * hw) / tile_a * tile_a);
+    Lr = std::min(Lr, max_len);
+  }
+  Lr = std::min(Lr, round_up(P.L, tile_a));
+  P.Lr = Lr;
+  P.R = ceil_div(P.L, Lr);
+
+  if (P.mfma) {
+    // LDS of the two matrix-core kernels must fit the 160 KiB of a CU
+    auto slice = [&](int64_t len) { return spatial_entries + (ceil_div(len, hw) + 1) * pt; };
+    const int64_t lds_state = 3 * d * 128 + slice(P.Lc) * 8;
+    const int64_t lds_apply = d * d * 4 + (d / 32) * 64 * 16 + slice(P.Lr) * 8;
+    if (std::max(lds_state, lds_apply) > 160 * 1024) return fail(GLA_ERR_UNSUPPORTED,
+        "internal: LDS plan of %lld bytes exceeds the CU", (long long)std::max(lds_state, lds_apply));
+  }
+  const int64_t max_grid = 0x7fffffff;
+  if (P.units * P.C > max_grid || P.units * P.R > max_grid || B * H > max_grid)
+    return fail(GLA_ERR_UNSUPPORTED, "too many (batch, head, block) units for one launch");
+
+  // Workspace layout.
+  size_t off = 0;
+  P.off_tab = off;
+  off = align256(off + (size_t)P.tab_entries * sizeof(float2));
+  P.off_part = off;
+  off = align256(off + (size_t)P.units * P.C * gla::kPartialStride(d) * sizeof(float));
+  P.off_state = off;
+  off = align256(off + (size_t)P.units * gla::kPartialStride(d) * sizeof(float));
+  P.off_frag = off;
+  if (P.mfma) off = align256(off + (size_t)P.units * 2 * d * d * sizeof(uint16_t));
+  P.total_bytes = off;
+  *p = P;
+  return GLA_OK;
+}
+
+// ---------------------------------------------------------------- profiling
+struct StageRecord {
+  int stage;
+  hipEvent_t start, stop;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<StageRecord> g_prof;
+
+const char *kStageNames[GLA_NUM_STAGES] = {"rope_table", "state_partials", "reduce_prefix",
+                                           "apply"};
+
+void prof_clear_locked() {
+  for (auto &r : g_prof) {
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+  }
+  g_prof.clear();
+}
+
+// Runs one launch, bracketed by events when timing is enabled.
+template <class F>
+gla_status timed_launch(int stage, hipStream_t stream, const char *what, F &&launch) {
+  bool on;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    on = g_prof_on;
+  }
+  StageRecord rec{stage, nullptr, nullptr};
+  if (on) {
+    hipError_t e = hipEventCreate(&rec.start);
+    if (e == hipSuccess) e = hipEventCreate(&rec.stop);
+    if (e == hipSuccess) e = hipEventRecord(rec.start, stream);
+    if (e != hipSuccess) return hip_fail(e, "stage timing event");
+  }
+  hipError_t e = launch();
+  if (e != hipSuccess) {
+    if (on) {
+      (void)hipEventDestroy(rec.start);
+      (void)hipEventDestroy(rec.stop);
+    }
+    return hip_fail(e, what);
+  }
+  if (on) {
+    e = hipEventRecord(rec.stop, stream);
+    if (e != hipSuccess) return hip_fail(e, "stage timing event");
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof.push_back(rec);
+  }
+  return GLA_OK;
+}
+
+// ---------------------------------------------------------------- execution
+// Enqueues every stage of the operator on `stream`, with workspace `ws`.
+// With `apply == false` only the state is computed (gla_state).
+gla_status run_plan(const Plan &P, const void *q, const void *k, const void *v, const void *g,
+                    void *out, void *ws, hipStream_t stream, bool apply) {
+  char *base = (char *)ws;
+  float2 *tab = (float2 *)(base + P.off_tab);
+  float *part = (float *)(base + P.off_part);
+  float *states = (float *)(base + P.off_state);
+  uint16_t *frags = P.mfma ? (uint16_t *)(base + P.off_frag) : nullptr;
+
+  gla_status st = timed_launch(0, stream, "rope table kernel",
+                               [&] { return gla::launch_rope_table(P, tab, stream); });
+  if (st != GLA_OK) return st;
+  st = timed_launch(1, stream, "state kernel", [&] {
+    return P.mfma ? gla::launch_state_mfma(P, k, v, tab, part, stream)
+                  : gla::launch_state_generic(P, k, v, tab, part, stream);
+  });
+  if (st != GLA_OK) return st;
+  st = timed_launch(2, stream, "reduce kernel", [&] {
+    return gla::launch_reduce(P, part, states, apply ? frags : nullptr, stream);
+  });
+  if (st != GLA_OK) return st;
+  if (!apply) return GLA_OK;
+  return timed_launch(3, stream, "apply kernel", [&] {
+    return P.mfma ? gla::launch_apply_mfma(P, q, g, states, frags, tab, out, stream)
+                  : gla::launch_apply_generic(P, q, g, states, tab, out, stream);
+  });
+}
+
+gla_status forward_impl(const void *q, const void *k, const void *v, const void *g, void *out,
+                        int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, int64_t d,
+                        int64_t F, float theta, float eps, gla_dtype dtype, void *ws,
+                        size_t ws_bytes, bool own_ws, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  gla_status st = check_sizes(B, H, T, Hs, Ws, d, F, dtype);
+  if (st != GLA_OK) return st;
+  if (!std::isfinite(theta)) return fail(GLA_ERR_INVALID_ARG, "rope_theta must be finite");
+  if (!std::isfinite(eps) || eps < 0.f)
+    return fail(GLA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  const size_t bytes = (size_t)(B * T * Hs * Ws * H * d) * (dtype == GLA_BF16 ? 2 : 4);
+  st = check_pointers(q, k, v, g, out, bytes);
+  if (st != GLA_OK) return st;
+  if (!own_ws && (ws == nullptr || ((uintptr_t)ws & 255) != 0))
+    return fail(GLA_ERR_INVALID_ARG, "workspace must be a non-null, 256-byte aligned pointer");
+  int cus = 0;
+  st = device_cus(&cus);
+  if (st != GLA_OK) return st;
+  const bool aligned16 = (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)g |
+                          (uintptr_t)out) & 15) == 0;
+  Plan P;
+  st = make_plan(B, H, T, Hs, Ws, d, F, dtype, theta, eps, cus, aligned16, &P);
+  if (st != GLA_OK) return st;
+  if (!own_ws) {
+    if (ws_bytes < P.total_bytes)
+      return fail(GLA_ERR_INVALID_ARG, "workspace too small: %zu bytes given, %zu needed", ws_bytes,
+                  P.total_bytes);
+    return run_plan(P, q, k, v, g, out, ws, stream, true);
+  }
+  void *mem = nullptr;
+  hipError_t e = hipMallocAsync(&mem, P.total_bytes, stream);
+  if (e != hipSuccess || mem == nullptr) {
+    (void)hipGetLastError();
+    return fail(GLA_ERR_ALLOC, "hipMallocAsync of %zu workspace bytes failed: %s", P.total_bytes,
+                hipGetErrorString(e));
+  }
+  st = run_plan(P, q, k, v, g, out, mem, stream, true);
+  e = hipFreeAsync(mem, stream);
+  if (st == GLA_OK && e != hipSuccess) return hip_fail(e, "hipFreeAsync");
+  return st;
+}
+
+}  // namespace
+
+// ===================================================================== C ABI
+extern "C" {
+
+gla_status gla_forward(const void *q, const void *k, const void *v, const void *g, void *out,
+                       int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, int64_t d,
+                       float rope_theta, float eps, gla_dtype dtype, hipStream_t stream) {
+  return forward_impl(q, k, v, g, out, B, H, T, Hs, Ws, d, 0, rope_theta, eps, dtype, nullptr, 0,
+                      true, stream);
+}
+
+gla_status gla_block_causal_forward(const void *q, const void *k, const void *v, const void *g,
+                                    void *out, int64_t B, int64_t H, int64_t T, int64_t Hs,
+                                    int64_t Ws, int64_t d, int64_t frames_per_block,
+                                    float rope_theta, float eps, gla_dtype dtype,
+                                    hipStream_t stream) {
+  if (frames_per_block < 1) {
+    g_last_error[0] = '\0';
+    return fail(GLA_ERR_INVALID_ARG, "frames_per_block must be >= 1 (got %lld)",
+                (long long)frames_per_block);
+  }
+  return forward_impl(q, k, v, g, out, B, H, T, Hs, Ws, d, frames_per_block, rope_theta, eps,
+                      dtype, nullptr, 0, true, stream);
+}
+
+gla_status gla_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws,
+                               int64_t d, int64_t frames_per_block, gla_dtype dtype,
+                               size_t *bytes) {
+  g_last_error[0] = '\0';
+  if (!bytes) return fail(GLA_ERR_INVALID_ARG, "bytes must not be null");
+  gla_status st = check_sizes(B, H, T, Hs, Ws, d, frames_per_block, dtype);
+  if (st != GLA_OK) return st;
+  int cus = 0;
+  st = device_cus(&cus);
+  if (st != GLA_OK) return st;
+  // the larger of the two kernel families' needs (unaligned tensors fall
+  // back to the vector kernels, whose chunking differs)
+  Plan P, Pv;
+  st = make_plan(B, H, T, Hs, Ws, d, frames_per_block, dtype, 10000.f, 0.f, cus, true, &P);
+  if (st != GLA_OK) return st;
+  st = make_plan(B, H, T, Hs, Ws, d, frames_per_block, dtype, 10000.f, 0.f, cus, false, &Pv);
+  if (st != GLA_OK) return st;
+  *bytes = std::max(P.total_bytes, Pv.total_bytes);
+  return GLA_OK;
+}
+
+gla_status gla_forward_ws(const void *q, const void *k, const void *v, const void *g, void *out,
+                          int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, int64_t d,
+                          int64_t frames_per_block, float rope_theta, float eps, gla_dtype dtype,
+                          void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  return forward_impl(q, k, v, g, out, B, H, T, Hs, Ws, d, frames_per_block, rope_theta, eps,
+                      dtype, workspace, workspace_bytes, false, stream);
+}
+
+gla_status gla_state(const void *k, const void *v, float *S_out, float *z_out, int64_t B,
+                     int64_t H, int64_t T, int64_t Hs, int64_t Ws, int64_t d,
+                     int64_t frames_per_block, float rope_theta, gla_dtype dtype,
+                     hipStream_t stream) {
+  g_last_error[0] = '\0';
+  gla_status st = check_sizes(B, H, T, Hs, Ws, d, frames_per_block, dtype);
+  if (st != GLA_OK) return st;
+  if (!k || !v || !S_out || !z_out) return fail(GLA_ERR_INVALID_ARG, "null pointer");
+  if (!std::isfinite(rope_theta)) return fail(GLA_ERR_INVALID_ARG, "rope_theta must be finite");
+  int cus = 0;
+  st = device_cus(&cus);
+  if (st != GLA_OK) return st;
+  const bool aligned16 = (((uintptr_t)k | (uintptr_t)v) & 15) == 0;
+  Plan P;
+  st = make_plan(B, H, T, Hs, Ws, d, frames_per_block, dtype, rope_theta, 0.f, cus, aligned16,
+                 &P);
+  if (st != GLA_OK) return st;
+  void *mem = nullptr;
+  hipError_t e = hipMallocAsync(&mem, P.total_bytes, stream);
+  if (e != hipSuccess || mem == nullptr) {
+    (void)hipGetLastError();
+    return fail(GLA_ERR_ALLOC, "hipMallocAsync of %zu workspace bytes failed", P.total_bytes);
+  }
+  st = run_plan(P, nullptr, k, v, nullptr, nullptr, mem, stream, false);
+  if (st == GLA_OK) {
+    // states are [units][d*d + d]; unpack to S [units][d][d] and z [units][d]
+    const float *states = (const float *)((char *)mem + P.off_state);
+    const size_t stride = (size_t)gla::kPartialStride(d) * sizeof(float);
+    e = hipMemcpy2DAsync(S_out, (size_t)d * d * sizeof(float), states, stride,
+                         (size_t)d * d * sizeof(float), (size_t)P.units, hipMemcpyDeviceToDevice,
+                         stream);
+    if (e == hipSuccess)
+      e = hipMemcpy2DAsync(z_out, (size_t)d * sizeof(float), states + d * d, stride,
+                           (size_t)d * sizeof(float), (size_t)P.units, hipMemcpyDeviceToDevice,
+                           stream);
+    if (e != hipSuccess) st = hip_fail(e, "state export copy");
+  }
+  e = hipFreeAsync(mem, stream);
+  if (st == GLA_OK && e != hipSuccess) return hip_fail(e, "hipFreeAsync");
+  return st;
+}
+
+const char *gla_status_string(gla_status status) {
+  switch (status) {
+    case GLA_OK: return "success";
+    case GLA_ERR_INVALID_ARG: return "invalid argument";
+    case GLA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case GLA_ERR_ALLOC: return "workspace allocation failed";
+    case GLA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char *gla_last_error(void) { return g_last_error; }
+
+gla_status gla_profile_enable(int enable) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  prof_clear_locked();
+  g_prof_on = enable != 0;
+  return GLA_OK;
+}
+
+gla_status gla_profile_read(int64_t launches[GLA_NUM_STAGES], double total_ms[GLA_NUM_STAGES]) {
+  g_last_error[0] = '\0';
+  if (!launches || !total_ms) return fail(GLA_ERR_INVALID_ARG, "null output array");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (int s = 0; s < GLA_NUM_STAGES; ++s) {
+    launches[s] = 0;
+    total_ms[s] = 0.0;
+  }
+  for (auto &r : g_prof) {
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    launches[r.stage] += 1;
+    total_ms[r.stage] += ms;
+  }
+  return GLA_OK;
+}
+
+const char *gla_stage_name(int stage) {
+  if (stage < 0 || stage >= GLA_NUM_STAGES) return "";
+  return kStageNames[stage];
+}
+
+int gla_uses_matrix_cores(int64_t T, int64_t Hs, int64_t Ws, int64_t d, gla_dtype dtype) {
+  Plan P;
+  if (make_plan(1, 1, T, Hs, Ws, d, 0, dtype, 10000.f, 0.f, 1, true, &P) != GLA_OK) return -1;
+  return P.mfma ? 1 : 0;
+}
+
+}  // extern "C"

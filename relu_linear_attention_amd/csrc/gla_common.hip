@@ -1,0 +1,118 @@
+// Kernels shared by both paths: the RoPE table and the fixed-order reduce /
+// block prefix of the state partials.
+//
+// "SANA-Video" notes page, Section 3.2: RoPE rotates phi(q) and phi(k) in the
+// numerator; Section 3.4: a block reads the running sums of the states and
+// normalisers of all earlier blocks plus its own.
+
+#include <hip/hip_runtime.h>
+
+#include "gla_internal.h"
+
+namespace gla {
+namespace {
+
+// One (cos, sin) entry per (axis, position, pair).  The angle
+// pos * theta^(-2i/d_axis) and its cosine and sine are evaluated in fp64 and
+// rounded once to fp32, so large positions (t up to several hundred) keep
+// full fp32 accuracy.  theta <= 0 gives the identity rotation (1, 0).
+__global__ __launch_bounds__(kBlock) void rope_table_kernel(float2 *__restrict__ tab, int64_t T,
+                                                            int64_t Hs, int64_t Ws, int d,
+                                                            double theta) {
+  const int64_t pt = d / 8, ph = 3 * d / 16, pw = 3 * d / 16;
+  const int64_t nt = T * pt, nh = Hs * ph, nw = Ws * pw;
+  const int64_t total = nt + nh + nw;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    int64_t pos, pair, width;
+    if (i < nt) {
+      pos = i / pt; pair = i % pt; width = d / 4;
+    } else if (i < nt + nh) {
+      pos = (i - nt) / ph; pair = (i - nt) % ph; width = 3 * d / 8;
+    } else {
+      pos = (i - nt - nh) / pw; pair = (i - nt - nh) % pw; width = 3 * d / 8;
+    }
+    float2 cs = make_float2(1.f, 0.f);
+    if (theta > 0.0) {
+      double freq = pow(theta, -2.0 * (double)pair / (double)width);
+      double angle = (double)pos * freq;
+      cs = make_float2((float)cos(angle), (float)sin(angle));
+    }
+    tab[i] = cs;
+  }
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  __bf16 h = (__bf16)x;  // round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// Sum of the C chunk partials of every unit, in chunk order, followed by the
+// inclusive prefix over the nb temporal blocks of a (batch, head), in block
+// order.  One thread owns four consecutive floats of the d*d + d state
+// vector; no two threads touch the same output, so the result is the same on
+// every run.
+//
+// frags (optional): S as the A operand of the 16x16x32 bf16 matrix-core
+// instruction for S^T (rows = output feature e, columns = key feature p), in
+// two parts S ~ hi + lo (hi = S rounded to bf16, lo = the remainder rounded
+// to bf16).  Fragment (et, ks) = 64 lanes x 8 values, lane
+// l = e%16 + 16*((p%32)/8), slot p%8, fragment index et*(d/32) + ks; the d*d
+// lo values follow the d*d hi values of a unit.
+__global__ __launch_bounds__(kBlock) void reduce_prefix_kernel(
+    const float *__restrict__ partials, float *__restrict__ states, uint16_t *__restrict__ frags,
+    int64_t nb, int64_t C, int d) {
+  const int64_t stride = (int64_t)d * d + d;
+  const int64_t bh = blockIdx.x;
+  const int64_t i4 = ((int64_t)blockIdx.y * blockDim.x + threadIdx.x) * 4;
+  if (i4 >= stride) return;
+  float4 run = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int64_t blk = 0; blk < nb; ++blk) {
+    const int64_t unit = bh * nb + blk;
+    const float *src = partials + unit * C * stride + i4;
+    for (int64_t c = 0; c < C; ++c) {
+      float4 x = *reinterpret_cast<const float4 *>(src + c * stride);
+      run.x += x.x;
+      run.y += x.y;
+      run.z += x.z;
+      run.w += x.w;
+    }
+    *reinterpret_cast<float4 *>(states + unit * stride + i4) = run;
+    if (frags != nullptr && i4 < (int64_t)d * d) {
+      const int p = (int)(i4 / d), e0 = (int)(i4 % d);
+      const float vals[4] = {run.x, run.y, run.z, run.w};
+      uint16_t *base = frags + unit * (int64_t)d * d * 2;
+      for (int r = 0; r < 4; ++r) {
+        const int e = e0 + r;
+        const int et = e / 16, ks = p / 32;
+        const int lane = (e % 16) + 16 * ((p % 32) / 8);
+        const int64_t off = (((int64_t)et * (d / 32) + ks) * 64 + lane) * 8 + (p % 8);
+        const __bf16 hi = (__bf16)vals[r];
+        base[off] = __builtin_bit_cast(uint16_t, hi);
+        base[(int64_t)d * d + off] = f32_to_bf16_bits(vals[r] - (float)hi);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rope_table(const Plan &p, float2 *tab, hipStream_t stream) {
+  int64_t blocks = (p.tab_entries + kBlock - 1) / kBlock;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, stream, tab, p.T,
+                     p.Hs, p.Ws, (int)p.d, (double)p.theta);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce(const Plan &p, const float *partials, float *states, uint16_t *frags,
+                         hipStream_t stream) {
+  const int64_t stride = kPartialStride(p.d);
+  const int64_t per_block = (int64_t)kBlock * 4;
+  dim3 grid((unsigned)(p.B * p.H), (unsigned)((stride + per_block - 1) / per_block));
+  hipLaunchKernelGGL(reduce_prefix_kernel, grid, dim3(kBlock), 0, stream, partials, states, frags,
+                     p.nb, p.C, (int)p.d);
+  return hipGetLastError();
+}
+
+}  // namespace gla

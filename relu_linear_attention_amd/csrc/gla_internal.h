@@ -1,0 +1,89 @@
+// Internal declarations shared by the host launcher (gla_api.cpp) and the
+// kernel translation units.  Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gla {
+
+// Work decomposition of one call, computed on the host.
+//
+// A "unit" is one (batch, head, temporal block); the non-causal operator is
+// the one-block case.  The state stage splits each unit's L tokens into C
+// chunks of Lc tokens (the last one ragged) and writes one fp32 partial
+// (S_c, z_c) per chunk; the reduce stage sums the partials of a unit in chunk
+// order and runs the inclusive prefix over the blocks of a (batch, head) in
+// block order; the apply stage splits each unit's tokens into R ranges of Lr
+// tokens.
+struct Plan {
+  int64_t B, H, T, Hs, Ws, d;
+  int64_t F;      // frames per block (== T when non-causal)
+  int64_t nb;     // temporal blocks per (batch, head)
+  int64_t N;      // tokens per batch entry, T*Hs*Ws
+  int64_t L;      // tokens per block
+  int64_t units;  // B*H*nb
+  int64_t C, Lc;  // state chunks per unit, tokens per chunk
+  int64_t R, Lr;  // apply ranges per unit, tokens per range
+  bool bf16;      // element type of q, k, v, g, out
+  bool mfma;      // matrix-core kernels (bf16, d = 64 or 128)
+  float theta, eps;
+  int64_t tab_entries;  // RoPE table entries (cos, sin pairs)
+  int64_t tab_t_off, tab_h_off, tab_w_off;  // entry offsets of the axis tables
+  // workspace layout, byte offsets
+  size_t off_tab, off_part, off_state, off_frag, total_bytes;
+};
+
+constexpr int kBlock = 256;          // threads per workgroup for every kernel
+constexpr int64_t kStateTile = 64;   // tokens per step of the matrix-core state kernel
+constexpr int64_t kApplyTile = 16;   // tokens per wave step of the matrix-core apply kernel (8 waves)
+constexpr int64_t kPartialStride(int64_t d) { return d * d + d; }
+
+// LDS budget of the RoPE table slice kept by the matrix-core kernels
+// (float2 entries).
+constexpr int64_t kStateTabEntries = 6144;  // 48 KiB
+constexpr int64_t kApplyTabEntries = 5120;  // 40 KiB
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error.  All enqueue on `stream`.
+
+// RoPE table: cos/sin per (axis, position, pair), computed in fp64 and
+// stored as float2.
+hipError_t launch_rope_table(const Plan &p, float2 *tab, hipStream_t stream);
+
+// State partials, vector kernels (any supported d, bf16 or f32).
+hipError_t launch_state_generic(const Plan &p, const void *k, const void *v, const float2 *tab,
+                                float *partials, hipStream_t stream);
+// Fixed-order reduce of the partials plus the inclusive block prefix.
+// Writes fp32 states [units][d*d + d] and, for the matrix-core path, the
+// bf16 hi/lo operand fragments of S^T [units][2][d*d].
+hipError_t launch_reduce(const Plan &p, const float *partials, float *states,
+                         uint16_t *frags, hipStream_t stream);
+// Output stage, vector kernels.
+hipError_t launch_apply_generic(const Plan &p, const void *q, const void *g, const float *states,
+                                const float2 *tab, void *out, hipStream_t stream);
+
+// Matrix-core kernels (bf16, d = 64 or 128).
+hipError_t launch_state_mfma(const Plan &p, const void *k, const void *v, const float2 *tab,
+                             float *partials, hipStream_t stream);
+hipError_t launch_apply_mfma(const Plan &p, const void *q, const void *g, const float *states,
+                             const uint16_t *frags, const float2 *tab, void *out,
+                             hipStream_t stream);
+
+// ------------------------------------------------------------ device helpers
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Token index -> (t, h, w) of the t-major latent grid.
+__device__ __forceinline__ void grid_pos(int64_t n, int64_t Hs, int64_t Ws, int &t, int &h,
+                                         int &w) {
+  int64_t hw = Hs * Ws;
+  t = (int)(n / hw);
+  int64_t r = n - (int64_t)t * hw;
+  h = (int)(r / Ws);
+  w = (int)(r - (int64_t)h * Ws);
+}
+
+}  // namespace gla

@@ -1,0 +1,529 @@
+// Matrix-core kernels of the operator for bf16 tensors with head size 64 or
+// 128 (gfx950, v_mfma_f32_32x32x16_bf16, fp32 accumulation).
+//
+//   state:  S_c = sum_{n in chunk} RoPE_n(phi(k_n))^T v_n,  z_c = sum phi(k_n)
+//   apply:  o_i = (RoPE_i(phi(q_i)) S) / (phi(q_i) . z + eps) * sigmoid(g_i)
+//
+// "SANA-Video" notes page, Section 3.2 (phi = ReLU, RoPE after ReLU for the
+// numerator only, un-rotated denominator); "SANA-Video 2.0" Section 2
+// Eq. (1) (+eps, sigmoid output gate).
+//
+// Operand layout of v_mfma_f32_32x32x16_bf16 used throughout (lane l of a
+// 64-wide wave, eight bf16 per operand register group):
+//   A (32 x 16):  lane l holds A[l % 32][8*(l/32) + j], j = 0..7
+//   B (16 x 32):  lane l holds B[8*(l/32) + j][l % 32]
+//   C (32 x 32):  lane l, value i holds C[8*(i/4) + 4*(l/32) + i%4][l % 32]
+//
+// The contraction of the state is over tokens, so k and v are staged in LDS
+// transposed (feature-major); the contraction of the apply stage is over
+// features, so q is loaded straight from HBM in the B layout.
+
+#include <hip/hip_runtime.h>
+
+#include "gla_internal.h"
+
+namespace gla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+struct MArgs {
+  int64_t N, H, Hs, Ws;
+  int64_t nb, L, C, Lc, R, Lr;
+  int64_t tab_h_off;  // global entry offset of the h rows (the w rows follow)
+  float eps;
+};
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 f = {lo, hi};
+  bf16x2 h = __builtin_convertvector(f, bf16x2);  // round to nearest even
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// ReLU of two packed bf16 values: a bf16 is negative exactly when its sign
+// bit is set, so a signed 16-bit max with 0 keeps x >= 0 and maps x < 0
+// (and -0) to +0.
+__device__ __forceinline__ uint32_t relu_bf16x2(uint32_t x) {
+  s16x2 v = __builtin_bit_cast(s16x2, x);
+  s16x2 zero = {0, 0};
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(v, zero));
+}
+
+__device__ __forceinline__ float lo_bf16(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+// Split two floats into packed bf16 hi parts (round to nearest even) and
+// packed bf16 lo parts, the rounded remainders: x ~ hi + lo to about 16
+// significant bits.
+__device__ __forceinline__ void split_bf16x2(float x0, float x1, uint32_t &hi, uint32_t &lo) {
+  hi = pack_bf16x2(x0, x1);
+  lo = pack_bf16x2(x0 - lo_bf16(hi), x1 - hi_bf16(hi));
+}
+
+// Feature pair P0 (a multiple of 4) -> axis (0 t, 1 h, 2 w) and the pair's
+// index within that axis.  For d = 64 and 128 a group of four pairs never
+// straddles two axes.
+template <int D>
+__device__ __forceinline__ void pair_axis(int P0, int &axis, int &pia) {
+  constexpr int pt = D / 8, ph = 3 * D / 16;
+  if (P0 < pt) {
+    axis = 0; pia = P0;
+  } else if (P0 < pt + ph) {
+    axis = 1; pia = P0 - pt;
+  } else {
+    axis = 2; pia = P0 - pt - ph;
+  }
+}
+
+// LDS copy of the RoPE table rows a workgroup touches: the h rows and the w
+// rows (both whole), then the temporal rows t_lo..t_hi of its token range.
+template <int D>
+struct TabSlice {
+  int sp_entries;  // (Hs + Ws) * 3D/16
+  int Hs;
+  int t_lo;
+  __device__ __forceinline__ int index(int axis, int pia, int t, int h, int w) const {
+    constexpr int ph = 3 * D / 16;
+    if (axis == 0) return sp_entries + (t - t_lo) * (D / 8) + pia;
+    if (axis == 1) return h * ph + pia;
+    return Hs * ph + w * ph + pia;
+  }
+};
+
+template <int D>
+__device__ TabSlice<D> load_tab_slice(float2 *s_tab, const float2 *__restrict__ tab,
+                                      const MArgs &a, int64_t n_begin, int64_t n_end) {
+  constexpr int ph = 3 * D / 16;
+  const int64_t hw = a.Hs * a.Ws;
+  TabSlice<D> ts;
+  ts.Hs = (int)a.Hs;
+  ts.sp_entries = (int)((a.Hs + a.Ws) * ph);
+  ts.t_lo = (int)(n_begin / hw);
+  const int t_hi = (int)((n_end - 1) / hw);
+  const int nt = (t_hi - ts.t_lo + 1) * (D / 8);
+  for (int i = threadIdx.x; i < ts.sp_entries; i += blockDim.x) s_tab[i] = tab[a.tab_h_off + i];
+  for (int i = threadIdx.x; i < nt; i += blockDim.x)
+    s_tab[ts.sp_entries + i] = tab[(int64_t)ts.t_lo * (D / 8) + i];
+  return ts;
+}
+
+// Rotate four adjacent pairs x[0..7] by the (cos, sin) entries cs[0..3].
+__device__ __forceinline__ void rotate4(float *x, const float2 *cs) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float2 c = cs[i];
+    const float x0 = x[2 * i], x1 = x[2 * i + 1];
+    x[2 * i] = x0 * c.x - x1 * c.y;
+    x[2 * i + 1] = x0 * c.y + x1 * c.x;
+  }
+}
+
+// ---------------------------------------------------------------- state
+
+// Byte offset of (row, slot) in a transposed operand array of kStateTile
+// bf16 slots per row (128 bytes).  16-byte units are XOR-swizzled by the row
+// so that the eight rows read by eight consecutive lanes of a fragment load
+// hit eight different bank groups; whole units move, so every fragment still
+// reads its eight tokens in slot order.
+__device__ __forceinline__ int kt_off(int row, int slot) {
+  const int unit = slot >> 3, within = slot & 7;
+  const int phys = unit ^ ((row & 7) ^ ((row >> 3) & 7));
+  return row * 128 + phys * 16 + within * 2;
+}
+
+template <int D>
+struct StateCfg {
+  static constexpr int FPT = D / 8;                  // threads per token row (16 B each)
+  static constexpr int TPP = kBlock / FPT;           // tokens per load pass
+  static constexpr int R = (int)kStateTile / TPP;    // passes per tile
+  static constexpr int TILES = (D / 32) * (D / 32);  // 32x32 output tiles of S
+  static constexpr int TPW = TILES / 4;              // tiles per wave
+  static constexpr int OP_BYTES = D * 128;           // one transposed operand array
+};
+
+// One workgroup per (unit, chunk).  Each 64-token step: 256 threads load the
+// k and v rows (16 B per thread per row, whole rows per instruction), apply
+// ReLU (and accumulate z) and RoPE to k in fp32, write RoPE(phi(k))^T split
+// into bf16 hi + lo parts, and v^T (exact in bf16), into LDS, then each wave
+// accumulates its share of the 32x32 tiles of S = hi^T v + lo^T v on the
+// matrix cores.  The next step's rows are fetched into registers while the
+// matrix cores run.
+template <int D>
+__global__ __launch_bounds__(kBlock) void state_mfma_kernel(const uint16_t *__restrict__ k,
+                                                            const uint16_t *__restrict__ v,
+                                                            const float2 *__restrict__ tab,
+                                                            float *__restrict__ partials,
+                                                            MArgs a) {
+  using Cfg = StateCfg<D>;
+  constexpr int FPT = Cfg::FPT, TPP = Cfg::TPP, R = Cfg::R;
+  extern __shared__ __align__(16) unsigned char lds[];
+  unsigned char *s_kt = lds;                      // RoPE(phi(k))^T, bf16 hi part
+  unsigned char *s_kl = lds + Cfg::OP_BYTES;      // bf16 lo part
+  unsigned char *s_vt = lds + 2 * Cfg::OP_BYTES;  // v^T
+  float2 *s_tab = reinterpret_cast<float2 *>(lds + 3 * Cfg::OP_BYTES);
+
+  const int64_t wg = blockIdx.x;
+  const int64_t unit = wg / a.C, c = wg % a.C;
+  const int64_t bh = unit / a.nb, blk = unit % a.nb;
+  const int64_t b = bh / a.H, hd = bh % a.H;
+  const int64_t n_begin = blk * a.L + c * a.Lc;
+  const int64_t n_end = min(n_begin + a.Lc, (blk + 1) * a.L);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+
+  const TabSlice<D> ts = load_tab_slice<D>(s_tab, tab, a, n_begin, n_end);
+
+  const int fc = tid % FPT, tg = tid / FPT;
+  int axis, pia;
+  pair_axis<D>(4 * fc, axis, pia);
+
+  uint4 kr[R], vr[R];
+  auto load_rows = [&](int64_t n0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t n = n0 + tg + TPP * r;
+      if (n < n_end) {
+        const int64_t off = ((b * a.N + n) * a.H + hd) * D + 8 * fc;
+        kr[r] = *reinterpret_cast<const uint4 *>(k + off);
+        vr[r] = *reinterpret_cast<const uint4 *>(v + off);
+      } else {
+        kr[r] = make_uint4(0, 0, 0, 0);
+        vr[r] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+
+  f32x16 acc[Cfg::TPW];
+#pragma unroll
+  for (int t = 0; t < Cfg::TPW; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
+  float zacc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) zacc[j] = 0.f;
+
+  // output tiles of this wave
+  int tile_p[Cfg::TPW], tile_e[Cfg::TPW];
+#pragma unroll
+  for (int t = 0; t < Cfg::TPW; ++t) {
+    const int idx = wave * Cfg::TPW + t;  // 0 .. TILES-1
+    if (D == 128) {
+      tile_p[t] = 2 * (wave >> 1) + (t >> 1);
+      tile_e[t] = 2 * (wave & 1) + (t & 1);
+    } else {
+      tile_p[t] = idx >> 1;
+      tile_e[t] = idx & 1;
+    }
+  }
+
+  load_rows(n_begin);
+  for (int64_t n0 = n_begin; n0 < n_end; n0 += kStateTile) {
+    __syncthreads();  // the previous step's fragment reads are done
+    float rk[R][8];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      int64_t n = n0 + tg + TPP * r;
+      if (n >= n_end) n = n_end - 1;  // position only; the row itself is zero
+      int t, h, w;
+      grid_pos(n, a.Hs, a.Ws, t, h, w);
+      const uint32_t kw[4] = {kr[r].x, kr[r].y, kr[r].z, kr[r].w};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t x = relu_bf16x2(kw[m]);
+        rk[r][2 * m] = lo_bf16(x);
+        rk[r][2 * m + 1] = hi_bf16(x);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) zacc[j] += rk[r][j];
+      const float2 *cs = s_tab + ts.index(axis, pia, t, h, w);
+      float2 c4[4] = {cs[0], cs[1], cs[2], cs[3]};
+      rotate4(rk[r], c4);
+    }
+    // transposed writes: feature row 8*fc + j, slots R*tg .. R*tg + R - 1
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = 8 * fc + j;
+      if constexpr (R == 4) {
+        uint2 wk, wl;
+        split_bf16x2(rk[0][j], rk[1][j], wk.x, wl.x);
+        split_bf16x2(rk[2][j], rk[3][j], wk.y, wl.y);
+        const uint32_t v0 = (&vr[0].x)[j >> 1], v1 = (&vr[1].x)[j >> 1];
+        const uint32_t v2 = (&vr[2].x)[j >> 1], v3 = (&vr[3].x)[j >> 1];
+        uint2 wv;
+        if (j & 1) {
+          wv = make_uint2((v0 >> 16) | (v1 & 0xffff0000u), (v2 >> 16) | (v3 & 0xffff0000u));
+        } else {
+          wv = make_uint2((v0 & 0xffffu) | (v1 << 16), (v2 & 0xffffu) | (v3 << 16));
+        }
+        *reinterpret_cast<uint2 *>(s_kt + kt_off(row, 4 * tg)) = wk;
+        *reinterpret_cast<uint2 *>(s_kl + kt_off(row, 4 * tg)) = wl;
+        *reinterpret_cast<uint2 *>(s_vt + kt_off(row, 4 * tg)) = wv;
+      } else {
+        static_assert(R == 2, "state tile layout");
+        uint32_t wk, wl;
+        split_bf16x2(rk[0][j], rk[1][j], wk, wl);
+        const uint32_t v0 = (&vr[0].x)[j >> 1], v1 = (&vr[1].x)[j >> 1];
+        const uint32_t wv =
+            (j & 1) ? ((v0 >> 16) | (v1 & 0xffff0000u)) : ((v0 & 0xffffu) | (v1 << 16));
+        *reinterpret_cast<uint32_t *>(s_kt + kt_off(row, 2 * tg)) = wk;
+        *reinterpret_cast<uint32_t *>(s_kl + kt_off(row, 2 * tg)) = wl;
+        *reinterpret_cast<uint32_t *>(s_vt + kt_off(row, 2 * tg)) = wv;
+      }
+    }
+    if (n0 + kStateTile < n_end) load_rows(n0 + kStateTile);
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < (int)kStateTile / 16; ++ks) {
+      const int slot = 16 * ks + 8 * (lane >> 5);
+#pragma unroll
+      for (int t = 0; t < Cfg::TPW; ++t) {
+        const int ka = kt_off(32 * tile_p[t] + (lane & 31), slot);
+        const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(s_kt + ka);
+        const bf16x8 fl = *reinterpret_cast<const bf16x8 *>(s_kl + ka);
+        const bf16x8 fb = *reinterpret_cast<const bf16x8 *>(
+            s_vt + kt_off(32 * tile_e[t] + (lane & 31), slot));
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fl, fb, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc[t], 0, 0, 0);
+      }
+    }
+  }
+
+  // S_c, row-major: lanes 0..31 write 32 consecutive floats of one row
+  float *dst = partials + wg * (int64_t)(D * D + D);
+#pragma unroll
+  for (int t = 0; t < Cfg::TPW; ++t) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int p = 32 * tile_p[t] + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+      const int e = 32 * tile_e[t] + (lane & 31);
+      dst[p * D + e] = acc[t][i];
+    }
+  }
+  // z_c: per-thread sums over its tokens, then a fixed-order sum over the
+  // TPP token groups
+  __syncthreads();
+  float *zs = reinterpret_cast<float *>(lds);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) zs[tg * D + 8 * fc + j] = zacc[j];
+  __syncthreads();
+  if (tid < D) {
+    float s = 0.f;
+    for (int gidx = 0; gidx < TPP; ++gidx) s += zs[gidx * D + tid];
+    dst[D * D + tid] = s;
+  }
+}
+
+// ---------------------------------------------------------------- apply
+
+// 16x16x32 bf16 matrix-core layout used by the apply stage:
+//   A (16 x 32):  lane l holds A[l % 16][8*(l/16) + j], j = 0..7
+//   B (32 x 16):  lane l holds B[8*(l/16) + j][l % 16]
+//   C (16 x 16):  lane l, value i holds C[4*(l/16) + i][l % 16]
+//
+// One workgroup (8 waves) per (unit, token range); each wave takes 16-token
+// tiles.  LDS holds the unit's S^T as bf16 A fragments in two parts, S ~
+// S_hi + S_lo (written by the reduce stage), the A fragments of the
+// denominator (rows 0, 4, 8, 12 carry z rounded to bf16 and rows 1, 5, 9, 13
+// the bf16 rounding of the remainder, so C values 0 and 1 of every lane sum
+// to phi(q).z), and the RoPE table rows of the range.  Per tile and
+// 32-feature step a lane loads 16 B of its token's q row; ReLU(q) is exact in
+// bf16 and is the B operand of the denominator; RoPE(ReLU(q)) is split into
+// bf16 hi + lo parts, and the numerator accumulates hi*S_hi + lo*S_hi +
+// hi*S_lo in fp32, which carries about 16 significant bits of every operand.
+// The epilogue divides by the denominator, applies the sigmoid gate and
+// stores 8 B of bf16 output per 16-feature tile.
+constexpr int kApplyThreads = 512;
+
+template <int D>
+__global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ g,
+    const float *__restrict__ states, const uint16_t *__restrict__ frags,
+    const float2 *__restrict__ tab, uint16_t *__restrict__ out, MArgs a) {
+  constexpr int KS = D / 32;  // 32-feature contraction steps
+  constexpr int ET = D / 16;  // 16-feature output tiles
+  constexpr int NW = kApplyThreads / 64;
+  extern __shared__ __align__(16) unsigned char lds[];
+  bf16x8 *s_afh = reinterpret_cast<bf16x8 *>(lds);  // ET*KS fragments x 64 lanes
+  bf16x8 *s_afl = s_afh + ET * KS * 64;
+  bf16x8 *s_zf = s_afl + ET * KS * 64;  // KS fragments x 64 lanes
+  float2 *s_tab = reinterpret_cast<float2 *>(s_zf + KS * 64);
+
+  const int64_t wg = blockIdx.x;
+  const int64_t unit = wg / a.R, r = wg % a.R;
+  const int64_t bh = unit / a.nb, blk = unit % a.nb;
+  const int64_t b = bh / a.H, hd = bh % a.H;
+  const int64_t n_begin = blk * a.L + r * a.Lr;
+  const int64_t n_end = min(n_begin + a.Lr, (blk + 1) * a.L);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+
+  {
+    const uint4 *src = reinterpret_cast<const uint4 *>(frags + unit * (int64_t)D * D * 2);
+    uint4 *dstf = reinterpret_cast<uint4 *>(s_afh);  // hi then lo, contiguous
+    for (int i = tid; i < D * D * 2 / 8; i += kApplyThreads) dstf[i] = src[i];
+    const float *zsrc = states + unit * (int64_t)(D * D + D) + D * D;
+    for (int i = tid; i < KS * 64; i += kApplyThreads) {
+      const int ks = i >> 6, l = i & 63, row = l & 15;
+      bf16x8 f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f[j] = (__bf16)0.f;
+      if ((row & 3) < 2) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float zv = zsrc[32 * ks + 8 * (l >> 4) + j];
+          const __bf16 zh = (__bf16)zv;
+          f[j] = (row & 1) ? (__bf16)(zv - (float)zh) : zh;
+        }
+      }
+      s_zf[i] = f;
+    }
+  }
+  const TabSlice<D> ts = load_tab_slice<D>(s_tab, tab, a, n_begin, n_end);
+  __syncthreads();
+
+  const int nl = lane & 15, kg = lane >> 4;
+  for (int64_t tile = n_begin + 16 * wave; tile < n_end; tile += 16 * NW) {
+    // keep the (loop-invariant) LDS fragment reads inside the loop: hoisting
+    // all of them would need 256 registers per lane
+    asm volatile("" ::: "memory");
+    const int64_t n = tile + nl;
+    const bool valid = n < n_end;
+    const int64_t nc = valid ? n : n_end - 1;
+    int t, h, w;
+    grid_pos(nc, a.Hs, a.Ws, t, h, w);
+    const int64_t rowoff = ((b * a.N + nc) * a.H + hd) * D;
+
+    uint4 qraw[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qraw[ks] = valid ? *reinterpret_cast<const uint4 *>(q + rowoff + 32 * ks + 8 * kg)
+                       : make_uint4(0, 0, 0, 0);
+    uint2 graw[ET];
+#pragma unroll
+    for (int et = 0; et < ET; ++et)
+      graw[et] = valid ? *reinterpret_cast<const uint2 *>(g + rowoff + 16 * et + 4 * kg)
+                       : make_uint2(0, 0);
+
+    f32x4 acc[ET], accd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int et = 0; et < ET; ++et) acc[et] = accd;
+
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint32_t qw[4] = {relu_bf16x2(qraw[ks].x), relu_bf16x2(qraw[ks].y),
+                              relu_bf16x2(qraw[ks].z), relu_bf16x2(qraw[ks].w)};
+      const bf16x8 bden = __builtin_bit_cast(bf16x8, make_uint4(qw[0], qw[1], qw[2], qw[3]));
+      float x[8];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        x[2 * m] = lo_bf16(qw[m]);
+        x[2 * m + 1] = hi_bf16(qw[m]);
+      }
+      int axis, pia;
+      pair_axis<D>(16 * ks + 4 * kg, axis, pia);
+      const float2 *cs = s_tab + ts.index(axis, pia, t, h, w);
+      float2 c4[4] = {cs[0], cs[1], cs[2], cs[3]};
+      rotate4(x, c4);
+      uint32_t hw4[4], lw4[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) split_bf16x2(x[2 * m], x[2 * m + 1], hw4[m], lw4[m]);
+      const bf16x8 bh = __builtin_bit_cast(bf16x8, make_uint4(hw4[0], hw4[1], hw4[2], hw4[3]));
+      const bf16x8 bl = __builtin_bit_cast(bf16x8, make_uint4(lw4[0], lw4[1], lw4[2], lw4[3]));
+      accd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s_zf[ks * 64 + lane], bden, accd, 0, 0, 0);
+#pragma unroll
+      for (int et = 0; et < ET; ++et) {
+        const bf16x8 ah = s_afh[(et * KS + ks) * 64 + lane];
+        const bf16x8 al = s_afl[(et * KS + ks) * 64 + lane];
+        acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc[et], 0, 0, 0);
+        acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc[et], 0, 0, 0);
+        acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[et], 0, 0, 0);
+      }
+    }
+
+    const float den = accd[0] + accd[1] + a.eps;
+#pragma unroll
+    for (int et = 0; et < ET; ++et) {
+      const float gv[4] = {lo_bf16(graw[et].x), hi_bf16(graw[et].x), lo_bf16(graw[et].y),
+                           hi_bf16(graw[et].y)};
+      float o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // num / den * sigmoid(g) = num / (den * (1 + exp(-g)))
+        const float e = __expf(-gv[i]);
+        o[i] = acc[et][i] * __builtin_amdgcn_rcpf(__builtin_fmaf(den, e, den));
+      }
+      if (valid)
+        *reinterpret_cast<uint2 *>(out + rowoff + 16 * et + 4 * kg) =
+            make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+    }
+  }
+}
+
+MArgs make_margs(const Plan &p) {
+  MArgs a;
+  a.N = p.N; a.H = p.H; a.Hs = p.Hs; a.Ws = p.Ws;
+  a.nb = p.nb; a.L = p.L; a.C = p.C; a.Lc = p.Lc; a.R = p.R; a.Lr = p.Lr;
+  a.tab_h_off = p.tab_h_off;
+  a.eps = p.eps;
+  return a;
+}
+
+// LDS entries of the RoPE table slice for a token range of at most `len`
+// tokens: the spatial rows plus the temporal rows it can span.
+int64_t tab_slice_entries(const Plan &p, int64_t len) {
+  const int64_t hw = p.Hs * p.Ws;
+  const int64_t rows = (len + hw - 1) / hw + 1;
+  return (p.Hs + p.Ws) * (3 * p.d / 16) + rows * (p.d / 8);
+}
+
+template <int D>
+hipError_t state_d(const Plan &p, const void *k, const void *v, const float2 *tab, float *part,
+                   hipStream_t stream) {
+  const size_t lds = 3 * StateCfg<D>::OP_BYTES + tab_slice_entries(p, p.Lc) * sizeof(float2);
+  auto kern = state_mfma_kernel<D>;
+  hipError_t e = hipFuncSetAttribute((const void *)kern,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(p.units * p.C)), dim3(kBlock), lds, stream,
+                     (const uint16_t *)k, (const uint16_t *)v, tab, part, make_margs(p));
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t apply_d(const Plan &p, const void *q, const void *g, const float *states,
+                   const uint16_t *frags, const float2 *tab, void *out, hipStream_t stream) {
+  const size_t lds = (size_t)D * D * 2 * 2 + (size_t)(D / 32) * 64 * 16 +
+                     tab_slice_entries(p, p.Lr) * sizeof(float2);
+  auto kern = apply_mfma_kernel<D>;
+  hipError_t e = hipFuncSetAttribute((const void *)kern,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(p.units * p.R)), dim3(kApplyThreads), lds, stream,
+                     (const uint16_t *)q, (const uint16_t *)g, states, frags, tab, (uint16_t *)out,
+                     make_margs(p));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_state_mfma(const Plan &p, const void *k, const void *v, const float2 *tab,
+                             float *partials, hipStream_t stream) {
+  if (p.d == 128) return state_d<128>(p, k, v, tab, partials, stream);
+  if (p.d == 64) return state_d<64>(p, k, v, tab, partials, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_apply_mfma(const Plan &p, const void *q, const void *g, const float *states,
+                             const uint16_t *frags, const float2 *tab, void *out,
+                             hipStream_t stream) {
+  if (p.d == 128) return apply_d<128>(p, q, g, states, frags, tab, out, stream);
+  if (p.d == 64) return apply_d<64>(p, q, g, states, frags, tab, out, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gla

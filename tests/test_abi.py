@@ -1,0 +1,128 @@
+"""The C ABI without a GPU: the library loads, exports every symbol that
+include/gla.h declares, and rejects bad arguments on the host before any HIP
+call.  No compute call is made here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from relu_linear_attention_amd import gla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gla.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gla.LIB_PATH):
+        from relu_linear_attention_amd import build
+
+        build.build()
+    return gla.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gla_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert sorted(gla.EXPORTS) == _declared_functions()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code, text in [(0, "success"), (1, "invalid argument"), (2, "unsupported configuration"),
+                       (3, "workspace allocation failed"), (4, "HIP runtime error")]:
+        assert gla.status_string(code) == text
+    assert gla.status_string(99) == "unknown status"
+
+
+FAKE = 1 << 20  # a non-null address; validation fails before anything reads it
+
+
+def _fwd(lib, ptrs=(FAKE, FAKE * 3, FAKE * 5, FAKE * 7, FAKE * 9), B=1, H=2, T=2, Hs=4, Ws=4,
+         d=32, theta=10000.0, eps=1e-6, dtype=gla.GLA_BF16):
+    p = [ctypes.c_void_p(x) if x else None for x in ptrs]
+    return lib.gla_forward(*p, B, H, T, Hs, Ws, d, theta, eps, dtype, None)
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(d=24), "d must be"),
+    (dict(d=144), "d must be"),
+    (dict(d=0), "d must be"),
+    (dict(B=0), ">= 1"),
+    (dict(T=-1), ">= 1"),
+    (dict(Ws=0), ">= 1"),
+    (dict(dtype=7), "dtype"),
+    (dict(eps=-1.0), "eps"),
+    (dict(eps=float("nan")), "eps"),
+    (dict(theta=float("inf")), "rope_theta"),
+    (dict(B=1 << 20, H=1 << 20, T=1 << 20, Hs=1 << 20, Ws=1), "overflow"),
+    (dict(ptrs=(0, FAKE, FAKE * 2, FAKE * 3, FAKE * 4)), "null"),
+    (dict(ptrs=(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, 0)), "null"),
+    (dict(ptrs=(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 2 + 64)), "overlaps input k"),
+    (dict(ptrs=(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE)), "overlaps input q"),
+])
+def test_forward_rejects_bad_arguments(lib, kw, needle):
+    assert _fwd(lib, **kw) == gla.GLA_ERR_INVALID_ARG
+    assert needle in gla.gla_last_error()
+
+
+def test_block_causal_rejects_bad_blocks(lib):
+    p = [ctypes.c_void_p(FAKE * i) for i in (1, 3, 5, 7, 9)]
+    assert lib.gla_block_causal_forward(*p, 1, 2, 6, 4, 4, 32, 4, 1e4, 1e-6, 0, None) == 1
+    assert "divide" in gla.gla_last_error()
+    assert lib.gla_block_causal_forward(*p, 1, 2, 6, 4, 4, 32, 0, 1e4, 1e-6, 0, None) == 1
+    assert ">= 1" in gla.gla_last_error()
+
+
+def test_forward_ws_rejects_bad_workspace(lib):
+    p = [ctypes.c_void_p(FAKE * i) for i in (1, 3, 5, 7, 9)]
+    assert lib.gla_forward_ws(*p, 1, 2, 2, 4, 4, 32, 0, 1e4, 1e-6, 0, None, 1 << 20, None) == 1
+    assert "workspace" in gla.gla_last_error()
+    assert lib.gla_forward_ws(*p, 1, 2, 2, 4, 4, 32, 0, 1e4, 1e-6, 0, ctypes.c_void_p(FAKE + 8),
+                              1 << 20, None) == 1
+    assert "aligned" in gla.gla_last_error()
+    assert lib.gla_forward_ws(*p, 1, 2, 6, 4, 4, 32, 4, 1e4, 1e-6, 0, ctypes.c_void_p(FAKE * 11),
+                              1 << 20, None) == 1
+
+
+def test_state_rejects_bad_arguments(lib):
+    k, v = ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE * 2)
+    assert lib.gla_state(k, v, None, ctypes.c_void_p(FAKE * 3), 1, 1, 2, 2, 2, 32, 0, 1e4, 0,
+                         None) == 1
+    assert lib.gla_state(k, v, ctypes.c_void_p(FAKE * 3), ctypes.c_void_p(FAKE * 4), 1, 1, 2, 2, 2,
+                         40, 0, 1e4, 0, None) == 1
+
+
+def test_workspace_query_rejects_bad_sizes(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.gla_workspace_bytes(1, 1, 3, 2, 2, 128, 2, 0, ctypes.byref(n)) == 1
+    assert lib.gla_workspace_bytes(1, 1, 3, 2, 2, 128, 0, 0, None) == 1
+
+
+def test_kernel_family_selection(lib):
+    # bf16 with d = 64 / 128 runs on the matrix cores; fp32 and other d on vector kernels
+    assert gla.gla_uses_matrix_cores(21, 45, 80, 128, gla.GLA_BF16) == 1
+    assert gla.gla_uses_matrix_cores(21, 45, 80, 64, gla.GLA_BF16) == 1
+    assert gla.gla_uses_matrix_cores(2, 4, 4, 32, gla.GLA_BF16) == 0
+    assert gla.gla_uses_matrix_cores(2, 4, 4, 128, gla.GLA_F32) == 0
+    assert gla.gla_uses_matrix_cores(2, 4, 4, 112, gla.GLA_BF16) == 0
+    # spatial RoPE rows that do not fit in LDS fall back to the vector kernels
+    assert gla.gla_uses_matrix_cores(2, 200, 200, 128, gla.GLA_BF16) == 0
+    assert gla.gla_uses_matrix_cores(2, 4, 4, 40, gla.GLA_BF16) == -1
+
+
+def test_profile_read_without_records(lib):
+    gla.gla_profile_enable(True)
+    rec = gla.gla_profile_read()
+    assert set(rec) == {"rope_table", "state_partials", "reduce_prefix", "apply"}
+    assert all(v == (0, 0.0) for v in rec.values())
+    gla.gla_profile_enable(False)

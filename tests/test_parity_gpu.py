@@ -1,0 +1,196 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Every test here runs on an MI355X; inputs are the seeded synthetic tensors of
+relu_linear_attention_amd.inputs.  The bar is max |gpu - oracle| /
+(|oracle| + 1e-3) <= 1e-4 for fp32 tensors and <= 1e-2 for bf16 tensors.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from relu_linear_attention_amd import gla
+from relu_linear_attention_amd.inputs import host_inputs
+from tests.gpu_util import TOL, have_gpu, max_rel_err, rel_l2, to_device, to_host_f32
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
+
+# name, B, T, Hs, Ws, H, d, dtype, frames_per_block, theta
+CASES = [
+    ("tiny_f32", 1, 2, 4, 4, 2, 32, "f32", 0, 1e4),  # the tiny fp32 workload
+    ("f32_d128", 1, 3, 5, 7, 2, 128, "f32", 0, 1e4),
+    ("f32_d64_block_causal", 2, 4, 3, 5, 3, 64, "f32", 2, 1e4),
+    ("f32_d16", 1, 2, 3, 5, 2, 16, "f32", 0, 1e4),
+    ("bf16_d128_ragged", 1, 4, 9, 13, 3, 128, "bf16", 0, 1e4),
+    ("bf16_d128_batch2", 2, 3, 5, 7, 2, 128, "bf16", 0, 1e4),
+    ("bf16_d128_many_chunks", 1, 8, 16, 20, 4, 128, "bf16", 0, 1e4),
+    ("bf16_d64", 1, 5, 8, 9, 4, 64, "bf16", 0, 1e4),
+    ("bf16_d32_vector", 1, 3, 6, 6, 2, 32, "bf16", 0, 1e4),
+    ("bf16_d112_vector", 1, 2, 5, 5, 2, 112, "bf16", 0, 1e4),
+    ("bf16_d128_blocks_F2", 1, 6, 5, 7, 2, 128, "bf16", 2, 1e4),
+    ("bf16_d128_blocks_F1", 1, 4, 6, 6, 2, 128, "bf16", 1, 1e4),
+    ("bf16_d64_blocks_FT", 1, 4, 6, 6, 2, 64, "bf16", 4, 1e4),
+    ("bf16_d128_blocks_batch2", 2, 6, 8, 9, 3, 128, "bf16", 3, 1e4),
+    ("bf16_d128_no_rotation", 1, 3, 5, 7, 2, 128, "bf16", 0, 0.0),
+    ("bf16_d128_single_token", 1, 1, 1, 1, 3, 128, "bf16", 0, 1e4),
+    ("bf16_d128_many_frames", 1, 64, 2, 3, 1, 128, "bf16", 0, 1e4),
+    ("bf16_d128_strong_rotation", 1, 3, 4, 5, 2, 128, "bf16", 0, 7.0),
+]
+
+
+def _run(x, case, out_dtype=None):
+    import torch
+
+    name, B, T, Hs, Ws, H, d, dtype, F, theta = case
+    dev = to_device(x, dtype)
+    out = torch.empty_like(dev["q"])
+    grid = (T, Hs, Ws)
+    if F:
+        gla.gla_block_causal_forward(dev["q"], dev["k"], dev["v"], dev["g"], out, grid, F, theta,
+                                     1e-6)
+    else:
+        gla.gla_forward(dev["q"], dev["k"], dev["v"], dev["g"], out, grid, theta, 1e-6)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_parity_with_oracle(case):
+    name, B, T, Hs, Ws, H, d, dtype, F, theta = case
+    x = host_inputs(B, T, Hs, Ws, H, d, dtype, seed=100 + len(name))
+    print(f"case {name}: B={B} grid={T}x{Hs}x{Ws} H={H} d={d} {dtype} F={F}", flush=True)
+    got = to_host_f32(_run(x, case))
+    ref = oracle.forward(x["q"], x["k"], x["v"], x["g"], (T, Hs, Ws), F, theta, 1e-6)
+    err = max_rel_err(got, ref)
+    print(f"  max rel err {err:.3e}  rel l2 {rel_l2(got, ref):.3e}", flush=True)
+    assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("d,dtype,F", [(128, "bf16", 0), (64, "bf16", 2), (32, "f32", 0),
+                                       (128, "f32", 3)])
+def test_state_export_matches_oracle(d, dtype, F):
+    import torch
+
+    B, T, Hs, Ws, H = 1, 6, 7, 9, 2
+    x = host_inputs(B, T, Hs, Ws, H, d, dtype, seed=7)
+    dev = to_device(x, dtype)
+    nb = oracle.num_blocks(T, F)
+    S = torch.empty((B, H, nb, d, d), dtype=torch.float32, device="cuda")
+    z = torch.empty((B, H, nb, d), dtype=torch.float32, device="cuda")
+    gla.gla_state(dev["k"], dev["v"], S, z, (T, Hs, Ws), F, 1e4)
+    torch.cuda.synchronize()
+    Sr, zr = oracle.state(x["k"], x["v"], (T, Hs, Ws), F, 1e4)
+    s_tol = 4e-3 if dtype == "bf16" else 1e-5
+    serr = np.max(np.abs(S.cpu().numpy() - Sr)) / np.max(np.abs(Sr))
+    zerr = np.max(np.abs(z.cpu().numpy() - zr) / (np.abs(zr) + 1e-6))
+    print(f"S err {serr:.3e}  z err {zerr:.3e}")
+    assert serr <= s_tol
+    assert zerr <= 1e-5
+
+
+@pytest.mark.parametrize("d,dtype,F", [(128, "bf16", 0), (128, "bf16", 2), (32, "f32", 0)])
+def test_bitwise_determinism(d, dtype, F):
+    case = ("det", 1, 6, 8, 9, 3, d, dtype, F, 1e4)
+    x = host_inputs(1, 6, 8, 9, 3, d, dtype, seed=3)
+    import torch
+
+    a = _run(x, case)
+    b = _run(x, case)
+    bits = torch.int16 if a.dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(a.view(bits), b.view(bits))
+
+
+def test_forward_ws_matches_forward():
+    import torch
+
+    B, T, Hs, Ws, H, d = 1, 5, 6, 7, 2, 128
+    x = host_inputs(B, T, Hs, Ws, H, d, "bf16", seed=4)
+    dev = to_device(x, "bf16")
+    for F in (0, 1):
+        ref = torch.empty_like(dev["q"])
+        if F:
+            gla.gla_block_causal_forward(dev["q"], dev["k"], dev["v"], dev["g"], ref,
+                                         (T, Hs, Ws), F)
+        else:
+            gla.gla_forward(dev["q"], dev["k"], dev["v"], dev["g"], ref, (T, Hs, Ws))
+        nbytes = gla.gla_workspace_bytes(B, H, T, Hs, Ws, d, F, gla.GLA_BF16)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(dev["q"])
+        gla.gla_forward_ws(dev["q"], dev["k"], dev["v"], dev["g"], out, (T, Hs, Ws), ws, F)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+        small = torch.empty(nbytes - 256, dtype=torch.uint8, device="cuda")
+        with pytest.raises(gla.GlaError):
+            gla.gla_forward_ws(dev["q"], dev["k"], dev["v"], dev["g"], out, (T, Hs, Ws), small, F)
+
+
+def test_unaligned_tensors_use_vector_kernels():
+    # tensors that start 2 bytes into an allocation cannot take 16-byte loads
+    import torch
+
+    B, T, Hs, Ws, H, d = 1, 3, 5, 7, 2, 128
+    x = host_inputs(B, T, Hs, Ws, H, d, "bf16", seed=5)
+    n = B * T * Hs * Ws * H * d
+    ts = {}
+    for name, a in x.items():
+        buf = torch.empty(n + 1, dtype=torch.bfloat16, device="cuda")
+        t = buf[1:].view(B, T * Hs * Ws, H, d)
+        t.copy_(torch.from_numpy(a).to(torch.bfloat16))
+        ts[name] = t
+    obuf = torch.empty(n + 1, dtype=torch.bfloat16, device="cuda")
+    out = obuf[1:].view(B, T * Hs * Ws, H, d)
+    gla.gla_forward(ts["q"], ts["k"], ts["v"], ts["g"], out, (T, Hs, Ws))
+    torch.cuda.synchronize()
+    ref = oracle.forward(x["q"], x["k"], x["v"], x["g"], (T, Hs, Ws))
+    assert max_rel_err(to_host_f32(out), ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (64, "f32")])
+def test_degenerate_rows_are_exact_zeros(d, dtype):
+    case = ("deg", 1, 2, 5, 6, 2, d, dtype, 0, 1e4)
+    x = host_inputs(1, 2, 5, 6, 2, d, dtype, seed=6)
+    x["q"][0, 17, 1] = -np.abs(x["q"][0, 17, 1]) - 0.5  # all-negative query row
+    x["q"][0, 40, 0] = 0.0
+    out = to_host_f32(_run(x, case))
+    assert np.all(out[0, 17, 1] == 0.0) and np.all(out[0, 40, 0] == 0.0)
+    x["v"][:] = 0.0
+    assert np.all(to_host_f32(_run(x, case)) == 0.0)
+
+
+def test_block_causal_last_block_equals_noncausal():
+    T, Hs, Ws, H, d, F = 6, 6, 7, 2, 128, 2
+    x = host_inputs(1, T, Hs, Ws, H, d, "bf16", seed=8)
+    nc = to_host_f32(_run(x, ("nc", 1, T, Hs, Ws, H, d, "bf16", 0, 1e4)))
+    bc = to_host_f32(_run(x, ("bc", 1, T, Hs, Ws, H, d, "bf16", F, 1e4)))
+    last = slice((T - F) * Hs * Ws, T * Hs * Ws)
+    assert max_rel_err(bc[:, last], nc[:, last]) <= TOL["bf16"]
+
+
+def test_non_default_stream():
+    import torch
+
+    x = host_inputs(1, 3, 5, 7, 2, 128, "bf16", seed=9)
+    case = ("s", 1, 3, 5, 7, 2, 128, "bf16", 0, 1e4)
+    ref = _run(x, case)
+    dev = to_device(x, "bf16")
+    s = torch.cuda.Stream()
+    out = torch.empty_like(dev["q"])
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        gla.gla_forward(dev["q"], dev["k"], dev["v"], dev["g"], out, (3, 5, 7), stream=s)
+    s.synchronize()
+    assert torch.equal(out, ref)
+
+
+def test_stage_timing_records_every_launch():
+    import torch
+
+    x = host_inputs(1, 3, 5, 7, 2, 128, "bf16", seed=10)
+    dev = to_device(x, "bf16")
+    out = torch.empty_like(dev["q"])
+    gla.gla_profile_enable(True)
+    for _ in range(3):
+        gla.gla_forward(dev["q"], dev["k"], dev["v"], dev["g"], out, (3, 5, 7))
+    rec = gla.gla_profile_read()
+    gla.gla_profile_enable(False)
+    assert all(n == 3 and ms > 0 for n, ms in rec.values()), rec
