@@ -1,0 +1,221 @@
+"""Throughput of the gated ReLU linear-attention token mixer on one MI355X.
+
+One step = one call of the whole operator (RoPE table, state partials,
+reduce/prefix, apply) over one batch of synthetic inputs already resident in
+HBM, through the C ABI (gla_forward_ws with a pre-allocated workspace).
+
+    python bench.py [--steps K] [--warmup W] [--workload 720p_81f]
+
+Prints one JSON line: tokens/s of the whole job, the per-stage launch times
+(HIP events on the launch stream, recorded by the library around each
+kernel), the HBM roofline of the dominant kernel, and the fp64 oracle timed on
+the host cores as a CPU baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
+DEFAULT_WORKLOAD = "720p_81f"
+MFMA_SOURCES = ("relu_linear_attention_amd/csrc/gla_mfma.hip",
+                "relu_linear_attention_amd/csrc/gla_common.hip")
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for rel in MFMA_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of each kernel from the committed rocprofv3
+    counter summary, or {} when there is none or the kernels have changed
+    since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return {}
+    digest, scale_f, scale_w, kernels = None, None, None, {}
+    with open(path) as f:
+        for line in f:
+            parts = line.split()
+            if not parts or parts[0].startswith("#"):
+                continue
+            if parts[0] == "source_digest":
+                digest = parts[1]
+            elif parts[0] == "copy_scale_fetch":
+                scale_f = float(parts[1])
+            elif parts[0] == "copy_scale_write":
+                scale_w = float(parts[1])
+            elif parts[0] == "kernel":
+                kernels[parts[1]] = (float(parts[2]), float(parts[3]))
+    if digest != source_digest() or scale_f is None or scale_w is None:
+        return {}
+    return {k: (fk * scale_f + wk * scale_w) * 1024.0 for k, (fk, wk) in kernels.items()}
+
+
+def cpu_baseline(w, dev_inputs):
+    """The fp64 oracle, as it stands, on one full forward of the workload."""
+    import oracle
+
+    host = {n: t.float().cpu().numpy() for n, t in dev_inputs.items()}
+    t0 = time.perf_counter()
+    out = oracle.forward(host["q"], host["k"], host["v"], host["g"], w.grid,
+                         w.frames_per_block, w.theta, w.eps)
+    dt = time.perf_counter() - t0
+    del out, host
+    return {
+        "value": w.B * w.N / dt,
+        "unit": "tokens/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"one full fp64 forward of the {w.name} layer ({w.B}x{w.N} tokens, "
+                   f"{w.H} heads, d={w.d}) on the host, inputs copied from HBM; "
+                   f"{dt:.2f} s"),
+    }
+
+
+def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
+    """A plain device-to-device copy of known size, for scaling the HBM
+    counters (FETCH_SIZE, WRITE_SIZE) of the kernels."""
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / reps
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps,
+                      "ms": ms, "GBps_read_plus_write": 2 * nbytes / ms / 1e6}))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the operator is "
+              "benchmarked at one GPU's share; see the sharding notes in DESIGN.md",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    from relu_linear_attention_amd import gla
+    from relu_linear_attention_amd.inputs import WORKLOADS, device_inputs_for
+
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration()
+        return 0
+
+    w = WORKLOADS[args.workload]
+    x = device_inputs_for(w)
+    q, k, v, g = x["q"], x["k"], x["v"], x["g"]
+    out = torch.empty_like(q)
+    dtype_code = gla.GLA_BF16 if w.dtype == "bf16" else gla.GLA_F32
+    ws = torch.empty(gla.gla_workspace_bytes(w.B, w.H, w.T, w.Hs, w.Ws, w.d, w.frames_per_block,
+                                             dtype_code), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        gla.gla_forward_ws(q, k, v, g, out, w.grid, ws, w.frames_per_block, w.theta, w.eps,
+                           stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, each kernel bracketed by HIP events on `stream`
+    gla.gla_profile_enable(True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stages = gla.gla_profile_read()
+    gla.gla_profile_enable(False)
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+    tokens = w.B * w.N
+    elem = w.B * w.N * w.H * w.d * w.elem_bytes
+    algo_bytes = {"state_partials": 2 * elem, "apply": 3 * elem}
+
+    stage_ms = {name: (ms / n if n else None) for name, (n, ms) in stages.items()}
+    dominant = max(("state_partials", "apply"), key=lambda s: stages[s][1])
+    dom_ms = stage_ms[dominant]
+    achieved = algo_bytes[dominant] / (dom_ms * 1e-3) / 1e9
+    mfma = gla.gla_uses_matrix_cores(w.T, w.Hs, w.Ws, w.d, dtype_code) == 1
+    kernel_names = {"state_partials": "state_mfma_kernel" if mfma else "state_vector_kernel",
+                    "apply": "apply_mfma_kernel" if mfma else "apply_vector_kernel"}
+    traffic = measured_traffic(w.name).get(kernel_names[dominant])
+
+    result = {
+        "metric": "GLA fwd tokens/s at 720p/81f (32 heads, d=128, bf16) + % of HBM roofline",
+        "value": tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "Hs": w.Hs, "Ws": w.Ws, "N": w.N,
+                   "H": w.H, "d": w.d, "frames_per_block": w.frames_per_block,
+                   "rope_theta": w.theta, "eps": w.eps, "seed": w.seed,
+                   "kernels": "matrix-core" if mfma else "vector"},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": kernel_names[dominant],
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBPS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": algo_bytes[dominant],
+        },
+        "stages_ms": stage_ms,
+        "path": {
+            "algorithmic_bytes_per_step": 5 * elem,
+            "GBps": 5 * elem / (ms_per_step * 1e-3) / 1e9,
+            "frac_of_peak": 5 * elem / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "wall_s": wall,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, x)
+    print(json.dumps(result))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
