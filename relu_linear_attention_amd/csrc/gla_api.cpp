@@ -128,7 +128,8 @@ gla_status make_plan(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, in
   // Matrix-core kernels keep the rows of the table they touch in LDS; the
   // spatial rows must fit next to at least two temporal rows.
   const int64_t spatial_entries = Hs * ph + Ws * pw;
-  P.mfma = aligned16 && P.bf16 && (d == 64 || d == 128) &&
+  // (token indices and positions are 32-bit in the matrix-core kernels)
+  P.mfma = aligned16 && P.bf16 && (d == 64 || d == 128) && P.N < ((int64_t)1 << 31) &&
            spatial_entries + 2 * pt <= std::min(gla::kStateTabEntries, gla::kApplyTabEntries);
 
   const int64_t hw = Hs * Ws;
@@ -165,7 +166,7 @@ gla_status make_plan(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, in
     // LDS of the two matrix-core kernels must fit the 160 KiB of a CU
     auto slice = [&](int64_t len) { return spatial_entries + (ceil_div(len, hw) + 1) * pt; };
     const int64_t lds_state = 3 * d * 128 + slice(P.Lc) * 8;
-    const int64_t lds_apply = d * d * 4 + (d / 32) * 64 * 16 + slice(P.Lr) * 8;
+    const int64_t lds_apply = d * d * 4 + (d / 32) * 64 * 16 + 8 * 16 * (2 * d + 32) + slice(P.Lr) * 8;
     if (std::max(lds_state, lds_apply) > 160 * 1024) return fail(GLA_ERR_UNSUPPORTED,
         "internal: LDS plan of %lld bytes exceeds the CU", (long long)std::max(lds_state, lds_apply));
   }

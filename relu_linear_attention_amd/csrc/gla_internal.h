@@ -71,6 +71,22 @@ hipError_t launch_apply_mfma(const Plan &p, const void *q, const void *g, const 
                              const uint16_t *frags, const float2 *tab, void *out,
                              hipStream_t stream);
 
+// Division by a fixed divisor d >= 1 for dividends 0 <= n < 2^31, by a
+// multiply-high and a shift: with s = ceil(log2 d) and
+// m = floor(2^32 (2^s - d) / d) + 1, n / d = (mulhi(n, m) + n) >> s.
+struct FastDiv {
+  uint32_t d, m, s;
+  static FastDiv make(uint32_t d) {
+    uint32_t s = 0;
+    while ((1ull << s) < d) ++s;
+    uint32_t m = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << s) - d)) / d + 1);
+    return FastDiv{d, m, s};
+  }
+  __device__ __forceinline__ uint32_t div(uint32_t n) const {
+    return (__umulhi(n, m) + n) >> s;
+  }
+};
+
 // ------------------------------------------------------------ device helpers
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);

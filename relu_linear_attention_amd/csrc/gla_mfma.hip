@@ -36,8 +36,20 @@ struct MArgs {
   int64_t N, H, Hs, Ws;
   int64_t nb, L, C, Lc, R, Lr;
   int64_t tab_h_off;  // global entry offset of the h rows (the w rows follow)
+  FastDiv div_hw, div_w;  // by Hs*Ws and by Ws (token indices < 2^31)
   float eps;
 };
+
+// Token index (within a batch entry, < 2^31) -> (t, h, w) of the t-major grid.
+__device__ __forceinline__ void token_pos(const MArgs &a, int64_t n, int &t, int &h, int &w) {
+  const uint32_t u = (uint32_t)n;
+  const uint32_t tt = a.div_hw.div(u);
+  const uint32_t r = u - tt * a.div_hw.d;
+  const uint32_t hh = a.div_w.div(r);
+  t = (int)tt;
+  h = (int)hh;
+  w = (int)(r - hh * a.div_w.d);
+}
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   f32x2 f = {lo, hi};
@@ -230,7 +242,7 @@ __global__ __launch_bounds__(kBlock) void state_mfma_kernel(const uint16_t *__re
       int64_t n = n0 + tg + TPP * r;
       if (n >= n_end) n = n_end - 1;  // position only; the row itself is zero
       int t, h, w;
-      grid_pos(n, a.Hs, a.Ws, t, h, w);
+      token_pos(a, n, t, h, w);
       const uint32_t kw[4] = {kr[r].x, kr[r].y, kr[r].z, kr[r].w};
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
@@ -330,14 +342,28 @@ __global__ __launch_bounds__(kBlock) void state_mfma_kernel(const uint16_t *__re
 // S_hi + S_lo (written by the reduce stage), the A fragments of the
 // denominator (rows 0, 4, 8, 12 carry z rounded to bf16 and rows 1, 5, 9, 13
 // the bf16 rounding of the remainder, so C values 0 and 1 of every lane sum
-// to phi(q).z), and the RoPE table rows of the range.  Per tile and
-// 32-feature step a lane loads 16 B of its token's q row; ReLU(q) is exact in
-// bf16 and is the B operand of the denominator; RoPE(ReLU(q)) is split into
-// bf16 hi + lo parts, and the numerator accumulates hi*S_hi + lo*S_hi +
-// hi*S_lo in fp32, which carries about 16 significant bits of every operand.
-// The epilogue divides by the denominator, applies the sigmoid gate and
-// stores 8 B of bf16 output per 16-feature tile.
+// to phi(q).z), the RoPE table rows of the range, and one staging tile per
+// wave.  Per tile and 32-feature step a lane loads 16 B of its token's q row;
+// ReLU(q) is exact in bf16 and is the B operand of the denominator;
+// RoPE(ReLU(q)) is split into bf16 hi + lo parts, and the numerator
+// accumulates hi*S_hi + lo*S_hi + hi*S_lo in fp32, which carries about 16
+// significant bits of every operand.  The gate g is loaded as whole 256-B
+// rows into the staging tile, read back in the accumulator layout, combined
+// with num / den, written back in place as bf16, and the tile leaves as whole
+// 256-B rows: full-row accesses keep HBM efficient where 8-B pieces per token
+// do not.
 constexpr int kApplyThreads = 512;
+// per-wave LDS staging tile of the epilogue: 16 token rows of D bf16, rows
+// 2D + 32 bytes apart so that both the row-wise 16-B accesses and the
+// fragment-wise 8-B accesses spread over the banks
+template <int D>
+struct Stage {
+  static constexpr int kRowBytes = 2 * D + 32;
+  static constexpr int kBytes = 16 * kRowBytes;
+  static constexpr int kLanesPerRow = D / 8;             // 16 B per lane
+  static constexpr int kRowsPerPass = 64 / kLanesPerRow;  // token rows per instruction
+  static constexpr int kPasses = 16 / kRowsPerPass;
+};
 
 template <int D>
 __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
@@ -351,7 +377,9 @@ __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
   bf16x8 *s_afh = reinterpret_cast<bf16x8 *>(lds);  // ET*KS fragments x 64 lanes
   bf16x8 *s_afl = s_afh + ET * KS * 64;
   bf16x8 *s_zf = s_afl + ET * KS * 64;  // KS fragments x 64 lanes
-  float2 *s_tab = reinterpret_cast<float2 *>(s_zf + KS * 64);
+  using St = Stage<D>;
+  unsigned char *s_stage = reinterpret_cast<unsigned char *>(s_zf + KS * 64);  // NW tiles
+  float2 *s_tab = reinterpret_cast<float2 *>(s_stage + NW * St::kBytes);
 
   const int64_t wg = blockIdx.x;
   const int64_t unit = wg / a.R, r = wg % a.R;
@@ -387,80 +415,144 @@ __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
   __syncthreads();
 
   const int nl = lane & 15, kg = lane >> 4;
-  for (int64_t tile = n_begin + 16 * wave; tile < n_end; tile += 16 * NW) {
-    // keep the (loop-invariant) LDS fragment reads inside the loop: hoisting
-    // all of them would need 256 registers per lane
-    asm volatile("" ::: "memory");
+  // row-wise lane mapping of the staging tile: in pass i lane l covers token
+  // i*kRowsPerPass + l/kLanesPerRow, features 8*(l%kLanesPerRow)..+7
+  const int rl = lane / St::kLanesPerRow, rc = 8 * (lane % St::kLanesPerRow);
+  const int64_t row_stride = a.H * D;
+  // loads of one tile: q in the B-operand layout, g as whole rows
+  auto fetch = [&](int64_t tile, uint4 (&qraw)[KS], uint4 (&grow)[St::kPasses]) {
     const int64_t n = tile + nl;
     const bool valid = n < n_end;
-    const int64_t nc = valid ? n : n_end - 1;
-    int t, h, w;
-    grid_pos(nc, a.Hs, a.Ws, t, h, w);
-    const int64_t rowoff = ((b * a.N + nc) * a.H + hd) * D;
-
-    uint4 qraw[KS];
+    const int64_t rowoff = ((b * a.N + (valid ? n : n_end - 1)) * a.H + hd) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       qraw[ks] = valid ? *reinterpret_cast<const uint4 *>(q + rowoff + 32 * ks + 8 * kg)
                        : make_uint4(0, 0, 0, 0);
-    uint2 graw[ET];
+    const int64_t rows_base = ((b * a.N + tile) * a.H + hd) * D;
 #pragma unroll
-    for (int et = 0; et < ET; ++et)
-      graw[et] = valid ? *reinterpret_cast<const uint2 *>(g + rowoff + 16 * et + 4 * kg)
-                       : make_uint2(0, 0);
+    for (int i = 0; i < St::kPasses; ++i) {
+      const int tok = i * St::kRowsPerPass + rl;
+      grow[i] = (tile + tok < n_end)
+                    ? *reinterpret_cast<const uint4 *>(g + rows_base + tok * row_stride + rc)
+                    : make_uint4(0, 0, 0, 0);
+    }
+  };
+  // everything after the loads of one tile
+  auto process = [&](int64_t tile, const uint4 (&cq)[KS], const uint4 (&cg)[St::kPasses]) {
+      const int64_t n = tile + nl;
+      const bool valid = n < n_end;
+      int t, h, w;
+      token_pos(a, valid ? n : n_end - 1, t, h, w);
+      const int64_t rows_base = ((b * a.N + tile) * a.H + hd) * D;
 
-    f32x4 acc[ET], accd = {0.f, 0.f, 0.f, 0.f};
+      f32x4 acc[ET], accd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int et = 0; et < ET; ++et) acc[et] = accd;
+      for (int et = 0; et < ET; ++et) acc[et] = accd;
 
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint32_t qw[4] = {relu_bf16x2(qraw[ks].x), relu_bf16x2(qraw[ks].y),
-                              relu_bf16x2(qraw[ks].z), relu_bf16x2(qraw[ks].w)};
-      const bf16x8 bden = __builtin_bit_cast(bf16x8, make_uint4(qw[0], qw[1], qw[2], qw[3]));
-      float x[8];
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint32_t qw[4] = {relu_bf16x2(cq[ks].x), relu_bf16x2(cq[ks].y),
+                                relu_bf16x2(cq[ks].z), relu_bf16x2(cq[ks].w)};
+        const bf16x8 bden = __builtin_bit_cast(bf16x8, make_uint4(qw[0], qw[1], qw[2], qw[3]));
+        float x[8];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        x[2 * m] = lo_bf16(qw[m]);
-        x[2 * m + 1] = hi_bf16(qw[m]);
+        for (int m = 0; m < 4; ++m) {
+          x[2 * m] = lo_bf16(qw[m]);
+          x[2 * m + 1] = hi_bf16(qw[m]);
+        }
+        int axis, pia;
+        pair_axis<D>(16 * ks + 4 * kg, axis, pia);
+        const float2 *cs = s_tab + ts.index(axis, pia, t, h, w);
+        float2 c4[4] = {cs[0], cs[1], cs[2], cs[3]};
+        rotate4(x, c4);
+        uint32_t hw4[4], lw4[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) split_bf16x2(x[2 * m], x[2 * m + 1], hw4[m], lw4[m]);
+        const bf16x8 bh = __builtin_bit_cast(bf16x8, make_uint4(hw4[0], hw4[1], hw4[2], hw4[3]));
+        const bf16x8 bl = __builtin_bit_cast(bf16x8, make_uint4(lw4[0], lw4[1], lw4[2], lw4[3]));
+        accd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s_zf[ks * 64 + lane], bden, accd, 0, 0, 0);
+#pragma unroll
+        for (int et = 0; et < ET; ++et) {
+          const bf16x8 ah = s_afh[(et * KS + ks) * 64 + lane];
+          const bf16x8 al = s_afl[(et * KS + ks) * 64 + lane];
+          acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc[et], 0, 0, 0);
+          acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc[et], 0, 0, 0);
+          acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[et], 0, 0, 0);
+        }
       }
-      int axis, pia;
-      pair_axis<D>(16 * ks + 4 * kg, axis, pia);
-      const float2 *cs = s_tab + ts.index(axis, pia, t, h, w);
-      float2 c4[4] = {cs[0], cs[1], cs[2], cs[3]};
-      rotate4(x, c4);
-      uint32_t hw4[4], lw4[4];
+
+      const float den = accd[0] + accd[1] + a.eps;
+      unsigned char *stage = s_stage + wave * St::kBytes;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) split_bf16x2(x[2 * m], x[2 * m + 1], hw4[m], lw4[m]);
-      const bf16x8 bh = __builtin_bit_cast(bf16x8, make_uint4(hw4[0], hw4[1], hw4[2], hw4[3]));
-      const bf16x8 bl = __builtin_bit_cast(bf16x8, make_uint4(lw4[0], lw4[1], lw4[2], lw4[3]));
-      accd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s_zf[ks * 64 + lane], bden, accd, 0, 0, 0);
+      for (int i = 0; i < St::kPasses; ++i)
+        *reinterpret_cast<uint4 *>(stage + (i * St::kRowsPerPass + rl) * St::kRowBytes + 2 * rc) =
+            cg[i];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
       for (int et = 0; et < ET; ++et) {
-        const bf16x8 ah = s_afh[(et * KS + ks) * 64 + lane];
-        const bf16x8 al = s_afl[(et * KS + ks) * 64 + lane];
-        acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc[et], 0, 0, 0);
-        acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc[et], 0, 0, 0);
-        acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[et], 0, 0, 0);
+        uint2 *slot = reinterpret_cast<uint2 *>(stage + nl * St::kRowBytes + 2 * (16 * et + 4 * kg));
+        const uint2 gw = *slot;
+        const float gv[4] = {lo_bf16(gw.x), hi_bf16(gw.x), lo_bf16(gw.y), hi_bf16(gw.y)};
+        float o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // num / den * sigmoid(g) = num / (den * (1 + exp(-g)))
+          const float e = __expf(-gv[i]);
+          o[i] = acc[et][i] * __builtin_amdgcn_rcpf(__builtin_fmaf(den, e, den));
+        }
+        *slot = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
       }
-    }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int i = 0; i < St::kPasses; ++i) {
+        const int tok = i * St::kRowsPerPass + rl;
+        const uint4 ov = *reinterpret_cast<const uint4 *>(stage + tok * St::kRowBytes + 2 * rc);
+        if (tile + tok < n_end)
+          *reinterpret_cast<uint4 *>(out + rows_base + tok * row_stride + rc) = ov;
+      }
+      // the next tile's first staging writes must not overtake these reads
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
 
-    const float den = accd[0] + accd[1] + a.eps;
+  // Two tiles of loads stay in flight per wave: tile i computes while the
+  // loads of tiles i+1 and i+2 are outstanding.
+  constexpr int64_t kStep = 16 * NW;
+  uint4 qa[KS], ga[St::kPasses], qb[KS], gb[St::kPasses];
+  int64_t tile = n_begin + 16 * wave;
+  if (tile < n_end) fetch(tile, qa, ga);
+  if (tile + kStep < n_end) fetch(tile + kStep, qb, gb);
+  while (tile < n_end) {
+    // keep the (loop-invariant) LDS fragment reads inside the loop: hoisting
+    // all of them would need 256 registers per lane
+    asm volatile("" ::: "memory");
+    {
+      uint4 cq[KS], cg[St::kPasses];
 #pragma unroll
-    for (int et = 0; et < ET; ++et) {
-      const float gv[4] = {lo_bf16(graw[et].x), hi_bf16(graw[et].x), lo_bf16(graw[et].y),
-                           hi_bf16(graw[et].y)};
-      float o[4];
+      for (int ks = 0; ks < KS; ++ks) cq[ks] = qa[ks];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // num / den * sigmoid(g) = num / (den * (1 + exp(-g)))
-        const float e = __expf(-gv[i]);
-        o[i] = acc[et][i] * __builtin_amdgcn_rcpf(__builtin_fmaf(den, e, den));
-      }
-      if (valid)
-        *reinterpret_cast<uint2 *>(out + rowoff + 16 * et + 4 * kg) =
-            make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+      for (int i = 0; i < St::kPasses; ++i) cg[i] = ga[i];
+      if (tile + 2 * kStep < n_end) fetch(tile + 2 * kStep, qa, ga);
+      process(tile, cq, cg);
     }
+    tile += kStep;
+    if (tile >= n_end) break;
+    asm volatile("" ::: "memory");
+    {
+      uint4 cq[KS], cg[St::kPasses];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) cq[ks] = qb[ks];
+#pragma unroll
+      for (int i = 0; i < St::kPasses; ++i) cg[i] = gb[i];
+      if (tile + 2 * kStep < n_end) fetch(tile + 2 * kStep, qb, gb);
+      process(tile, cq, cg);
+    }
+    tile += kStep;
   }
 }
 
@@ -469,6 +561,8 @@ MArgs make_margs(const Plan &p) {
   a.N = p.N; a.H = p.H; a.Hs = p.Hs; a.Ws = p.Ws;
   a.nb = p.nb; a.L = p.L; a.C = p.C; a.Lc = p.Lc; a.R = p.R; a.Lr = p.Lr;
   a.tab_h_off = p.tab_h_off;
+  a.div_hw = FastDiv::make((uint32_t)(p.Hs * p.Ws));
+  a.div_w = FastDiv::make((uint32_t)p.Ws);
   a.eps = p.eps;
   return a;
 }
@@ -498,6 +592,7 @@ template <int D>
 hipError_t apply_d(const Plan &p, const void *q, const void *g, const float *states,
                    const uint16_t *frags, const float2 *tab, void *out, hipStream_t stream) {
   const size_t lds = (size_t)D * D * 2 * 2 + (size_t)(D / 32) * 64 * 16 +
+                     (size_t)(kApplyThreads / 64) * Stage<D>::kBytes +
                      tab_slice_entries(p, p.Lr) * sizeof(float2);
   auto kern = apply_mfma_kernel<D>;
   hipError_t e = hipFuncSetAttribute((const void *)kern,
