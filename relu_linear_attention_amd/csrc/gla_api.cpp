@@ -166,7 +166,7 @@ gla_status make_plan(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, in
     // LDS of the two matrix-core kernels must fit the 160 KiB of a CU
     auto slice = [&](int64_t len) { return spatial_entries + (ceil_div(len, hw) + 1) * pt; };
     const int64_t lds_state = 3 * d * 128 + slice(P.Lc) * 8;
-    const int64_t lds_apply = d * d * 4 + (d / 32) * 64 * 16 + 8 * 16 * (2 * d + 32) + slice(P.Lr) * 8;
+    const int64_t lds_apply = d * d * 4 + (d / 32) * 64 * 16 + 8 * 16 * (2 * d + 16) + slice(P.Lr) * 8;
     if (std::max(lds_state, lds_apply) > 160 * 1024) return fail(GLA_ERR_UNSUPPORTED,
         "internal: LDS plan of %lld bytes exceeds the CU", (long long)std::max(lds_state, lds_apply));
   }

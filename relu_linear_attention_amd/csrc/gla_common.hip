@@ -53,11 +53,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
 // vector; no two threads touch the same output, so the result is the same on
 // every run.
 //
-// frags (optional): S as the A operand of the 16x16x32 bf16 matrix-core
-// instruction for S^T (rows = output feature e, columns = key feature p), in
-// two parts S ~ hi + lo (hi = S rounded to bf16, lo = the remainder rounded
-// to bf16).  Fragment (et, ks) = 64 lanes x 8 values, lane
-// l = e%16 + 16*((p%32)/8), slot p%8, fragment index et*(d/32) + ks; the d*d
+// frags (optional): S in two bf16 parts, S ~ hi + lo (hi = S rounded to
+// bf16, lo = the remainder rounded to bf16), each row-major [p][e]; the d*d
 // lo values follow the d*d hi values of a unit.
 __global__ __launch_bounds__(kBlock) void reduce_prefix_kernel(
     const float *__restrict__ partials, float *__restrict__ states, uint16_t *__restrict__ frags,
@@ -79,18 +76,18 @@ __global__ __launch_bounds__(kBlock) void reduce_prefix_kernel(
     }
     *reinterpret_cast<float4 *>(states + unit * stride + i4) = run;
     if (frags != nullptr && i4 < (int64_t)d * d) {
-      const int p = (int)(i4 / d), e0 = (int)(i4 % d);
       const float vals[4] = {run.x, run.y, run.z, run.w};
-      uint16_t *base = frags + unit * (int64_t)d * d * 2;
+      uint16_t hi[4], lo[4];
       for (int r = 0; r < 4; ++r) {
-        const int e = e0 + r;
-        const int et = e / 16, ks = p / 32;
-        const int lane = (e % 16) + 16 * ((p % 32) / 8);
-        const int64_t off = (((int64_t)et * (d / 32) + ks) * 64 + lane) * 8 + (p % 8);
-        const __bf16 hi = (__bf16)vals[r];
-        base[off] = __builtin_bit_cast(uint16_t, hi);
-        base[(int64_t)d * d + off] = f32_to_bf16_bits(vals[r] - (float)hi);
+        const __bf16 h = (__bf16)vals[r];
+        hi[r] = __builtin_bit_cast(uint16_t, h);
+        lo[r] = f32_to_bf16_bits(vals[r] - (float)h);
       }
+      uint16_t *base = frags + unit * (int64_t)d * d * 2 + i4;
+      *reinterpret_cast<uint2 *>(base) =
+          make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
+      *reinterpret_cast<uint2 *>(base + (int64_t)d * d) =
+          make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
     }
   }
 }

@@ -56,8 +56,8 @@ hipError_t launch_rope_table(const Plan &p, float2 *tab, hipStream_t stream);
 hipError_t launch_state_generic(const Plan &p, const void *k, const void *v, const float2 *tab,
                                 float *partials, hipStream_t stream);
 // Fixed-order reduce of the partials plus the inclusive block prefix.
-// Writes fp32 states [units][d*d + d] and, for the matrix-core path, the
-// bf16 hi/lo operand fragments of S^T [units][2][d*d].
+// Writes fp32 states [units][d*d + d] and, for the matrix-core path, S as
+// row-major bf16 hi and lo parts [units][2][d][d].
 hipError_t launch_reduce(const Plan &p, const float *partials, float *states,
                          uint16_t *frags, hipStream_t stream);
 // Output stage, vector kernels.

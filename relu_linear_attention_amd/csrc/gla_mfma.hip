@@ -137,15 +137,19 @@ __device__ __forceinline__ void rotate4(float *x, const float2 *cs) {
 
 // ---------------------------------------------------------------- state
 
-// Byte offset of (row, slot) in a transposed operand array of kStateTile
-// bf16 slots per row (128 bytes).  16-byte units are XOR-swizzled by the row
-// so that the eight rows read by eight consecutive lanes of a fragment load
-// hit eight different bank groups; whole units move, so every fragment still
-// reads its eight tokens in slot order.
-__device__ __forceinline__ int kt_off(int row, int slot) {
-  const int unit = slot >> 3, within = slot & 7;
-  const int phys = unit ^ ((row & 7) ^ ((row >> 3) & 7));
-  return row * 128 + phys * 16 + within * 2;
+// Transposing LDS read of gfx950 (ds_read_b64_tr_b16).  Within each group of
+// 16 lanes, lane s supplies the address of a row of four 16-bit values
+// M[s][0..3], and lane i receives M[i/4 + 4k][i%4] for k = 0..3.  With lane
+// s pointing at row tok0 + s/4, column c0 + 4*(s%4) of a row-major
+// [token][feature] tile, lane i receives X[tok0 + k][c0 + i], k = 0..3: four
+// consecutive tokens of one feature, half of the eight a lane contributes to
+// a matrix-core operand whose contraction runs over tokens.  This read moves
+// 512 B in two LDS cycles, twice the rate of plain 16-B reads.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const unsigned char *p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4 *)(p));
+  return __builtin_bit_cast(uint2, r);
 }
 
 template <int D>
@@ -155,16 +159,29 @@ struct StateCfg {
   static constexpr int R = (int)kStateTile / TPP;    // passes per tile
   static constexpr int TILES = (D / 32) * (D / 32);  // 32x32 output tiles of S
   static constexpr int TPW = TILES / 4;              // tiles per wave
-  static constexpr int OP_BYTES = D * 128;           // one transposed operand array
+  static constexpr int ROW = 2 * D;                  // bytes per token row
+  static constexpr int OP_BYTES = (int)kStateTile * ROW;
+  // Operand tiles are row-major [token][feature] with the 16-byte units of a
+  // row XOR-permuted by the row index, so that the 16-B row writes and the
+  // 8-B transposing reads (4 rows x 64 B per 32 lanes) both spread over all
+  // banks.  The permutation depends on row bits that neither the token
+  // passes nor the k-steps of a read change.
+  static __device__ __forceinline__ int swz(int row) {
+    return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+  }
+  static __device__ __forceinline__ int off(int row, int unit) {
+    return row * ROW + ((unit ^ swz(row)) << 4);
+  }
 };
 
 // One workgroup per (unit, chunk).  Each 64-token step: 256 threads load the
 // k and v rows (16 B per thread per row, whole rows per instruction), apply
-// ReLU (and accumulate z) and RoPE to k in fp32, write RoPE(phi(k))^T split
-// into bf16 hi + lo parts, and v^T (exact in bf16), into LDS, then each wave
-// accumulates its share of the 32x32 tiles of S = hi^T v + lo^T v on the
-// matrix cores.  The next step's rows are fetched into registers while the
-// matrix cores run.
+// ReLU (accumulating z) and RoPE to k in fp32, and write RoPE(phi(k)) split
+// into bf16 hi + lo parts, and v (exact in bf16), as row-major tiles into
+// LDS.  Each wave then reads its operands transposed (four tokens of one
+// feature per lane and read) and accumulates its share of the 32x32 tiles of
+// S = hi^T v + lo^T v on the matrix cores.  The rows of the next step are in
+// flight in registers meanwhile.
 template <int D>
 __global__ __launch_bounds__(kBlock) void state_mfma_kernel(const uint16_t *__restrict__ k,
                                                             const uint16_t *__restrict__ v,
@@ -172,11 +189,11 @@ __global__ __launch_bounds__(kBlock) void state_mfma_kernel(const uint16_t *__re
                                                             float *__restrict__ partials,
                                                             MArgs a) {
   using Cfg = StateCfg<D>;
-  constexpr int FPT = Cfg::FPT, TPP = Cfg::TPP, R = Cfg::R;
+  constexpr int FPT = Cfg::FPT, TPP = Cfg::TPP, R = Cfg::R, ROW = Cfg::ROW;
   extern __shared__ __align__(16) unsigned char lds[];
-  unsigned char *s_kt = lds;                      // RoPE(phi(k))^T, bf16 hi part
+  unsigned char *s_kh = lds;                      // RoPE(phi(k)), bf16 hi part
   unsigned char *s_kl = lds + Cfg::OP_BYTES;      // bf16 lo part
-  unsigned char *s_vt = lds + 2 * Cfg::OP_BYTES;  // v^T
+  unsigned char *s_v = lds + 2 * Cfg::OP_BYTES;   // v
   float2 *s_tab = reinterpret_cast<float2 *>(lds + 3 * Cfg::OP_BYTES);
 
   const int64_t wg = blockIdx.x;
@@ -193,16 +210,45 @@ __global__ __launch_bounds__(kBlock) void state_mfma_kernel(const uint16_t *__re
   const int fc = tid % FPT, tg = tid / FPT;
   int axis, pia;
   pair_axis<D>(4 * fc, axis, pia);
+  // this thread's rows of a tile: tg + TPP*r, 16-byte unit fc
+  const int wr_off = Cfg::off(tg, fc);
 
+  // output tiles of this wave and their transposing-read offsets: lane l
+  // (group g = l/16, s = l%16) points at row 8*(g/2) + s/4 (+ 16*ks +
+  // 4*half), column 32*tile + 16*(g%2) + 4*(s%4)
+  int tile_p[Cfg::TPW], tile_e[Cfg::TPW], rd_p[Cfg::TPW], rd_e[Cfg::TPW];
+  {
+    const int g = lane >> 4, sl = lane & 15;
+    const int rrow = 8 * (g >> 1) + (sl >> 2);
+#pragma unroll
+    for (int t = 0; t < Cfg::TPW; ++t) {
+      if (D == 128) {
+        tile_p[t] = 2 * (wave >> 1) + (t >> 1);
+        tile_e[t] = 2 * (wave & 1) + (t & 1);
+      } else {
+        tile_p[t] = wave >> 1;
+        tile_e[t] = wave & 1;
+      }
+      const int cp = 32 * tile_p[t] + 16 * (g & 1) + 4 * (sl & 3);
+      const int ce = 32 * tile_e[t] + 16 * (g & 1) + 4 * (sl & 3);
+      rd_p[t] = Cfg::off(rrow, cp >> 3) + ((cp & 7) << 1);
+      rd_e[t] = Cfg::off(rrow, ce >> 3) + ((ce & 7) << 1);
+    }
+  }
+
+  // row pointers of this thread: token n_begin + tg (+ TPP*r, + 64 per step)
+  const int64_t row_elems = a.H * D;
+  const uint16_t *kp = k + ((b * a.N + n_begin + tg) * a.H + hd) * D + 8 * fc;
+  const uint16_t *vp = v + ((b * a.N + n_begin + tg) * a.H + hd) * D + 8 * fc;
   uint4 kr[R], vr[R];
   auto load_rows = [&](int64_t n0) {
+    const int64_t step = n0 - n_begin;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int64_t n = n0 + tg + TPP * r;
-      if (n < n_end) {
-        const int64_t off = ((b * a.N + n) * a.H + hd) * D + 8 * fc;
-        kr[r] = *reinterpret_cast<const uint4 *>(k + off);
-        vr[r] = *reinterpret_cast<const uint4 *>(v + off);
+      if (n0 + tg + TPP * r < n_end) {
+        const int64_t off = (step + TPP * r) * row_elems;
+        kr[r] = *reinterpret_cast<const uint4 *>(kp + off);
+        vr[r] = *reinterpret_cast<const uint4 *>(vp + off);
       } else {
         kr[r] = make_uint4(0, 0, 0, 0);
         vr[r] = make_uint4(0, 0, 0, 0);
@@ -219,24 +265,9 @@ __global__ __launch_bounds__(kBlock) void state_mfma_kernel(const uint16_t *__re
 #pragma unroll
   for (int j = 0; j < 8; ++j) zacc[j] = 0.f;
 
-  // output tiles of this wave
-  int tile_p[Cfg::TPW], tile_e[Cfg::TPW];
-#pragma unroll
-  for (int t = 0; t < Cfg::TPW; ++t) {
-    const int idx = wave * Cfg::TPW + t;  // 0 .. TILES-1
-    if (D == 128) {
-      tile_p[t] = 2 * (wave >> 1) + (t >> 1);
-      tile_e[t] = 2 * (wave & 1) + (t & 1);
-    } else {
-      tile_p[t] = idx >> 1;
-      tile_e[t] = idx & 1;
-    }
-  }
-
   load_rows(n_begin);
   for (int64_t n0 = n_begin; n0 < n_end; n0 += kStateTile) {
-    __syncthreads();  // the previous step's fragment reads are done
-    float rk[R][8];
+    __syncthreads();  // the previous step's operand reads are done
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       int64_t n = n0 + tg + TPP * r;
@@ -244,61 +275,41 @@ __global__ __launch_bounds__(kBlock) void state_mfma_kernel(const uint16_t *__re
       int t, h, w;
       token_pos(a, n, t, h, w);
       const uint32_t kw[4] = {kr[r].x, kr[r].y, kr[r].z, kr[r].w};
+      float x[8];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const uint32_t x = relu_bf16x2(kw[m]);
-        rk[r][2 * m] = lo_bf16(x);
-        rk[r][2 * m + 1] = hi_bf16(x);
+        const uint32_t rl = relu_bf16x2(kw[m]);
+        x[2 * m] = lo_bf16(rl);
+        x[2 * m + 1] = hi_bf16(rl);
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) zacc[j] += rk[r][j];
+      for (int j = 0; j < 8; ++j) zacc[j] += x[j];
       const float2 *cs = s_tab + ts.index(axis, pia, t, h, w);
       float2 c4[4] = {cs[0], cs[1], cs[2], cs[3]};
-      rotate4(rk[r], c4);
-    }
-    // transposed writes: feature row 8*fc + j, slots R*tg .. R*tg + R - 1
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = 8 * fc + j;
-      if constexpr (R == 4) {
-        uint2 wk, wl;
-        split_bf16x2(rk[0][j], rk[1][j], wk.x, wl.x);
-        split_bf16x2(rk[2][j], rk[3][j], wk.y, wl.y);
-        const uint32_t v0 = (&vr[0].x)[j >> 1], v1 = (&vr[1].x)[j >> 1];
-        const uint32_t v2 = (&vr[2].x)[j >> 1], v3 = (&vr[3].x)[j >> 1];
-        uint2 wv;
-        if (j & 1) {
-          wv = make_uint2((v0 >> 16) | (v1 & 0xffff0000u), (v2 >> 16) | (v3 & 0xffff0000u));
-        } else {
-          wv = make_uint2((v0 & 0xffffu) | (v1 << 16), (v2 & 0xffffu) | (v3 << 16));
-        }
-        *reinterpret_cast<uint2 *>(s_kt + kt_off(row, 4 * tg)) = wk;
-        *reinterpret_cast<uint2 *>(s_kl + kt_off(row, 4 * tg)) = wl;
-        *reinterpret_cast<uint2 *>(s_vt + kt_off(row, 4 * tg)) = wv;
-      } else {
-        static_assert(R == 2, "state tile layout");
-        uint32_t wk, wl;
-        split_bf16x2(rk[0][j], rk[1][j], wk, wl);
-        const uint32_t v0 = (&vr[0].x)[j >> 1], v1 = (&vr[1].x)[j >> 1];
-        const uint32_t wv =
-            (j & 1) ? ((v0 >> 16) | (v1 & 0xffff0000u)) : ((v0 & 0xffffu) | (v1 << 16));
-        *reinterpret_cast<uint32_t *>(s_kt + kt_off(row, 2 * tg)) = wk;
-        *reinterpret_cast<uint32_t *>(s_kl + kt_off(row, 2 * tg)) = wl;
-        *reinterpret_cast<uint32_t *>(s_vt + kt_off(row, 2 * tg)) = wv;
-      }
+      rotate4(x, c4);
+      uint4 hi, lo;
+      split_bf16x2(x[0], x[1], hi.x, lo.x);
+      split_bf16x2(x[2], x[3], hi.y, lo.y);
+      split_bf16x2(x[4], x[5], hi.z, lo.z);
+      split_bf16x2(x[6], x[7], hi.w, lo.w);
+      const int o = wr_off + r * TPP * ROW;
+      *reinterpret_cast<uint4 *>(s_kh + o) = hi;
+      *reinterpret_cast<uint4 *>(s_kl + o) = lo;
+      *reinterpret_cast<uint4 *>(s_v + o) = vr[r];
     }
     if (n0 + kStateTile < n_end) load_rows(n0 + kStateTile);
     __syncthreads();
 #pragma unroll
     for (int ks = 0; ks < (int)kStateTile / 16; ++ks) {
-      const int slot = 16 * ks + 8 * (lane >> 5);
 #pragma unroll
       for (int t = 0; t < Cfg::TPW; ++t) {
-        const int ka = kt_off(32 * tile_p[t] + (lane & 31), slot);
-        const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(s_kt + ka);
-        const bf16x8 fl = *reinterpret_cast<const bf16x8 *>(s_kl + ka);
-        const bf16x8 fb = *reinterpret_cast<const bf16x8 *>(
-            s_vt + kt_off(32 * tile_e[t] + (lane & 31), slot));
+        const int o0 = (16 * ks) * ROW, o1 = (16 * ks + 4) * ROW;
+        const uint2 h0 = lds_read_tr16(s_kh + rd_p[t] + o0), h1 = lds_read_tr16(s_kh + rd_p[t] + o1);
+        const uint2 l0 = lds_read_tr16(s_kl + rd_p[t] + o0), l1 = lds_read_tr16(s_kl + rd_p[t] + o1);
+        const uint2 v0 = lds_read_tr16(s_v + rd_e[t] + o0), v1 = lds_read_tr16(s_v + rd_e[t] + o1);
+        const bf16x8 fa = __builtin_bit_cast(bf16x8, make_uint4(h0.x, h0.y, h1.x, h1.y));
+        const bf16x8 fl = __builtin_bit_cast(bf16x8, make_uint4(l0.x, l0.y, l1.x, l1.y));
+        const bf16x8 fb = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
         acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fl, fb, acc[t], 0, 0, 0);
         acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc[t], 0, 0, 0);
       }
@@ -353,12 +364,33 @@ __global__ __launch_bounds__(kBlock) void state_mfma_kernel(const uint16_t *__re
 // 256-B rows: full-row accesses keep HBM efficient where 8-B pieces per token
 // do not.
 constexpr int kApplyThreads = 512;
+
+// LDS layout of the S parts in the apply stage: row-major [p][e] bf16 with
+// the 16-byte units of row p XOR-permuted by f(p).  The A operand of the
+// 16x16x32 instruction (S^T: rows e, columns p) is read with the transposing
+// LDS read: lane s of a 16-lane group points at row p0 + s/4, column
+// e0 + 4*(s%4), and lane i receives S[p0 + k][e0 + i], k = 0..3.  A read
+// touches rows p0..p0+3 and p0+8..p0+11 per 32 lanes, 32 B each; f gives
+// those eight rows distinct unit pairs, so a read covers all banks once.
+// f depends only on row bits that the k-step and half offsets (multiples of
+// 4 rows, bit 3 untouched) leave alone.
+template <int D>
+struct SRow {
+  static __device__ __forceinline__ int f(int row) {
+    return D == 128 ? 2 * ((row & 3) + 4 * ((row >> 3) & 1))
+                    : 2 * (((row >> 1) & 1) + 2 * ((row >> 3) & 1));
+  }
+  static __device__ __forceinline__ int off(int row, int unit) {
+    return row * (2 * D) + ((unit ^ f(row)) << 4);
+  }
+};
 // per-wave LDS staging tile of the epilogue: 16 token rows of D bf16, rows
-// 2D + 32 bytes apart so that both the row-wise 16-B accesses and the
-// fragment-wise 8-B accesses spread over the banks
+// 2D + 16 bytes apart (an odd number of 16-byte units), so that the 16
+// rows read by a fragment-wise 8-B access start in 16 different 4-bank
+// groups and the row-wise 16-B accesses stay contiguous
 template <int D>
 struct Stage {
-  static constexpr int kRowBytes = 2 * D + 32;
+  static constexpr int kRowBytes = 2 * D + 16;
   static constexpr int kBytes = 16 * kRowBytes;
   static constexpr int kLanesPerRow = D / 8;             // 16 B per lane
   static constexpr int kRowsPerPass = 64 / kLanesPerRow;  // token rows per instruction
@@ -374,9 +406,9 @@ __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
   constexpr int ET = D / 16;  // 16-feature output tiles
   constexpr int NW = kApplyThreads / 64;
   extern __shared__ __align__(16) unsigned char lds[];
-  bf16x8 *s_afh = reinterpret_cast<bf16x8 *>(lds);  // ET*KS fragments x 64 lanes
-  bf16x8 *s_afl = s_afh + ET * KS * 64;
-  bf16x8 *s_zf = s_afl + ET * KS * 64;  // KS fragments x 64 lanes
+  unsigned char *s_sh = lds;             // S hi part, row-major [p][e], units permuted
+  unsigned char *s_sl = lds + D * D * 2;  // S lo part
+  bf16x8 *s_zf = reinterpret_cast<bf16x8 *>(lds + D * D * 4);  // KS fragments x 64 lanes
   using St = Stage<D>;
   unsigned char *s_stage = reinterpret_cast<unsigned char *>(s_zf + KS * 64);  // NW tiles
   float2 *s_tab = reinterpret_cast<float2 *>(s_stage + NW * St::kBytes);
@@ -391,9 +423,12 @@ __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
   const int lane = tid & 63, wave = tid >> 6;
 
   {
+    // S hi then lo, 16-byte units i = (part, row, unit), unit permuted by row
     const uint4 *src = reinterpret_cast<const uint4 *>(frags + unit * (int64_t)D * D * 2);
-    uint4 *dstf = reinterpret_cast<uint4 *>(s_afh);  // hi then lo, contiguous
-    for (int i = tid; i < D * D * 2 / 8; i += kApplyThreads) dstf[i] = src[i];
+    for (int i = tid; i < D * D * 2 / 8; i += kApplyThreads) {
+      const int u = i % (D / 8), row = (i / (D / 8)) % D, part = i / (D * D / 8);
+      *reinterpret_cast<uint4 *>(lds + part * D * D * 2 + SRow<D>::off(row, u)) = src[i];
+    }
     const float *zsrc = states + unit * (int64_t)(D * D + D) + D * D;
     for (int i = tid; i < KS * 64; i += kApplyThreads) {
       const int ks = i >> 6, l = i & 63, row = l & 15;
@@ -415,6 +450,13 @@ __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
   __syncthreads();
 
   const int nl = lane & 15, kg = lane >> 4;
+  // transposing-read offsets of the S parts: lane l (s = l%16, group
+  // g = l/16) points at row 8*g + s/4 (+ 32*ks + 4*half), column
+  // 16*et + 4*(s%4); the row's unit permutation depends only on s and g
+  int rd_s[ET];
+#pragma unroll
+  for (int et = 0; et < ET; ++et)
+    rd_s[et] = SRow<D>::off(8 * kg + (nl >> 2), 2 * et + ((nl & 3) >> 1)) + 8 * (nl & 1);
   // row-wise lane mapping of the staging tile: in pass i lane l covers token
   // i*kRowsPerPass + l/kLanesPerRow, features 8*(l%kLanesPerRow)..+7
   const int rl = lane / St::kLanesPerRow, rc = 8 * (lane % St::kLanesPerRow);
@@ -473,8 +515,14 @@ __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
         accd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s_zf[ks * 64 + lane], bden, accd, 0, 0, 0);
 #pragma unroll
         for (int et = 0; et < ET; ++et) {
-          const bf16x8 ah = s_afh[(et * KS + ks) * 64 + lane];
-          const bf16x8 al = s_afl[(et * KS + ks) * 64 + lane];
+          // A = S^T fragment (rows e = 16*et + l%16, columns p = 32*ks +
+          // 8*(l/16) + j), read transposed from the row-major S parts
+          const int o0 = rd_s[et] + (32 * ks) * (2 * D);
+          const int o1 = o0 + 4 * (2 * D);
+          const uint2 h0 = lds_read_tr16(s_sh + o0), h1 = lds_read_tr16(s_sh + o1);
+          const uint2 l0 = lds_read_tr16(s_sl + o0), l1 = lds_read_tr16(s_sl + o1);
+          const bf16x8 ah = __builtin_bit_cast(bf16x8, make_uint4(h0.x, h0.y, h1.x, h1.y));
+          const bf16x8 al = __builtin_bit_cast(bf16x8, make_uint4(l0.x, l0.y, l1.x, l1.y));
           acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc[et], 0, 0, 0);
           acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc[et], 0, 0, 0);
           acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[et], 0, 0, 0);
