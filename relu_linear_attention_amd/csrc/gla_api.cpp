@@ -14,7 +14,7 @@
 #include <mutex>
 #include <vector>
 
-#include "../../include/gla.h"
+#include "gla.h"
 #include "gla_internal.h"
 
 using gla::Plan;
@@ -162,6 +162,20 @@ gla_status make_plan(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, in
   P.Lr = Lr;
   P.R = ceil_div(P.L, Lr);
 
+  if (P.mfma) {
+    // buffer offsets of a token range are 32-bit: keep range bytes < 2^31
+    const int64_t row_bytes = H * d * 2;
+    const int64_t max_tokens = (((int64_t)1 << 31) - 2 * d) / row_bytes;
+    if (P.Lc > max_tokens) {
+      P.Lc = std::max<int64_t>(tile_s, max_tokens / tile_s * tile_s);
+      P.C = ceil_div(P.L, P.Lc);
+    }
+    if (P.Lr > max_tokens) {
+      P.Lr = std::max<int64_t>(tile_a, max_tokens / tile_a * tile_a);
+      P.R = ceil_div(P.L, P.Lr);
+    }
+    if (P.Lc > max_tokens || P.Lr > max_tokens) P.mfma = false;
+  }
   if (P.mfma) {
     // LDS of the two matrix-core kernels must fit the 160 KiB of a CU
     auto slice = [&](int64_t len) { return spatial_entries + (ceil_div(len, hw) + 1) * pt; };

@@ -40,6 +40,27 @@ struct MArgs {
   float eps;
 };
 
+// Buffer resource over the rows of one head for a token range: byte 0 is
+// feature 0 of the first token, row r starts at r * row_bytes, and the
+// range ends after the last token's d features.  Loads past the end return
+// zeros and stores past the end are dropped by the hardware, so ragged token
+// tiles need neither masks nor branches.  (Raw buffer, stride 0; the last
+// descriptor word selects 32-bit untyped data.)
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rows_rsrc(const uint16_t *first_row,
+                                                                 uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(first_row), 0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 x) {
+  const u32x4 v = {x.x, x.y, x.z, x.w};
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+}
+
 // Token index (within a batch entry, < 2^31) -> (t, h, w) of the t-major grid.
 __device__ __forceinline__ void token_pos(const MArgs &a, int64_t n, int &t, int &h, int &w) {
   const uint32_t u = (uint32_t)n;
@@ -203,7 +224,8 @@ __global__ __launch_bounds__(kBlock) void state_mfma_kernel(const uint16_t *__re
   const int64_t n_begin = blk * a.L + c * a.Lc;
   const int64_t n_end = min(n_begin + a.Lc, (blk + 1) * a.L);
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform across the wave
 
   const TabSlice<D> ts = load_tab_slice<D>(s_tab, tab, a, n_begin, n_end);
 
@@ -420,7 +442,8 @@ __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
   const int64_t n_begin = blk * a.L + r * a.Lr;
   const int64_t n_end = min(n_begin + a.Lr, (blk + 1) * a.L);
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform across the wave
 
   {
     // S hi then lo, 16-byte units i = (part, row, unit), unit permuted by row
@@ -460,32 +483,37 @@ __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
   // row-wise lane mapping of the staging tile: in pass i lane l covers token
   // i*kRowsPerPass + l/kLanesPerRow, features 8*(l%kLanesPerRow)..+7
   const int rl = lane / St::kLanesPerRow, rc = 8 * (lane % St::kLanesPerRow);
-  const int64_t row_stride = a.H * D;
-  // loads of one tile: q in the B-operand layout, g as whole rows
+  // buffer resources over this range's rows of q, g and out
+  const int64_t first = ((b * a.N + n_begin) * a.H + hd) * D;
+  const uint32_t row_bytes = (uint32_t)(a.H * D * 2);
+  const uint32_t range_bytes = (uint32_t)(n_end - n_begin - 1) * row_bytes + 2 * D;
+  const __amdgpu_buffer_rsrc_t rq = head_rows_rsrc(q + first, range_bytes);
+  const __amdgpu_buffer_rsrc_t rg = head_rows_rsrc(g + first, range_bytes);
+  const __amdgpu_buffer_rsrc_t ro = head_rows_rsrc(out + first, range_bytes);
+  // loads of one tile: q in the B-operand layout, g as whole rows (rows past
+  // the range read as zeros)
   auto fetch = [&](int64_t tile, uint4 (&qraw)[KS], uint4 (&grow)[St::kPasses]) {
-    const int64_t n = tile + nl;
-    const bool valid = n < n_end;
-    const int64_t rowoff = ((b * a.N + (valid ? n : n_end - 1)) * a.H + hd) * D;
+    const uint32_t rel = (uint32_t)(tile - n_begin);
+    const uint32_t qoff = (rel + nl) * row_bytes + 2 * 8 * kg;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qraw[ks] = valid ? *reinterpret_cast<const uint4 *>(q + rowoff + 32 * ks + 8 * kg)
-                       : make_uint4(0, 0, 0, 0);
-    const int64_t rows_base = ((b * a.N + tile) * a.H + hd) * D;
+    for (int ks = 0; ks < KS; ++ks) qraw[ks] = buf_load16(rq, qoff + 2 * 32 * ks);
 #pragma unroll
-    for (int i = 0; i < St::kPasses; ++i) {
-      const int tok = i * St::kRowsPerPass + rl;
-      grow[i] = (tile + tok < n_end)
-                    ? *reinterpret_cast<const uint4 *>(g + rows_base + tok * row_stride + rc)
-                    : make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < St::kPasses; ++i)
+      grow[i] = buf_load16(rg, (rel + i * St::kRowsPerPass + rl) * row_bytes + 2 * rc);
   };
   // everything after the loads of one tile
   auto process = [&](int64_t tile, const uint4 (&cq)[KS], const uint4 (&cg)[St::kPasses]) {
+      // An offset the compiler cannot see through (always 0) keeps the
+      // loop-invariant S-part reads inside the loop: hoisting all of them
+      // would need 256 registers per lane.  It is a register-only asm, so it
+      // does not make the compiler drain outstanding memory operations.
+      int opaque = 0;
+      asm volatile("" : "+v"(opaque));
+      const unsigned char *sh = s_sh + opaque, *sl = s_sl + opaque;
       const int64_t n = tile + nl;
       const bool valid = n < n_end;
       int t, h, w;
       token_pos(a, valid ? n : n_end - 1, t, h, w);
-      const int64_t rows_base = ((b * a.N + tile) * a.H + hd) * D;
 
       f32x4 acc[ET], accd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -513,19 +541,32 @@ __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
         const bf16x8 bh = __builtin_bit_cast(bf16x8, make_uint4(hw4[0], hw4[1], hw4[2], hw4[3]));
         const bf16x8 bl = __builtin_bit_cast(bf16x8, make_uint4(lw4[0], lw4[1], lw4[2], lw4[3]));
         accd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s_zf[ks * 64 + lane], bden, accd, 0, 0, 0);
+        // A = S^T fragments (rows e = 16*et + l%16, columns p = 32*ks +
+        // 8*(l/16) + j), read transposed from the row-major S parts, four
+        // output tiles at a time; the three products of a tile are issued
+        // round-robin over the four tiles so that consecutive matrix-core
+        // instructions do not depend on each other
 #pragma unroll
-        for (int et = 0; et < ET; ++et) {
-          // A = S^T fragment (rows e = 16*et + l%16, columns p = 32*ks +
-          // 8*(l/16) + j), read transposed from the row-major S parts
-          const int o0 = rd_s[et] + (32 * ks) * (2 * D);
-          const int o1 = o0 + 4 * (2 * D);
-          const uint2 h0 = lds_read_tr16(s_sh + o0), h1 = lds_read_tr16(s_sh + o1);
-          const uint2 l0 = lds_read_tr16(s_sl + o0), l1 = lds_read_tr16(s_sl + o1);
-          const bf16x8 ah = __builtin_bit_cast(bf16x8, make_uint4(h0.x, h0.y, h1.x, h1.y));
-          const bf16x8 al = __builtin_bit_cast(bf16x8, make_uint4(l0.x, l0.y, l1.x, l1.y));
-          acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc[et], 0, 0, 0);
-          acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc[et], 0, 0, 0);
-          acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[et], 0, 0, 0);
+        for (int eg = 0; eg < ET; eg += 4) {
+          bf16x8 ah[4], al[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int o0 = rd_s[eg + u] + (32 * ks) * (2 * D);
+            const int o1 = o0 + 4 * (2 * D);
+            const uint2 h0 = lds_read_tr16(sh + o0), h1 = lds_read_tr16(sh + o1);
+            const uint2 l0 = lds_read_tr16(sl + o0), l1 = lds_read_tr16(sl + o1);
+            ah[u] = __builtin_bit_cast(bf16x8, make_uint4(h0.x, h0.y, h1.x, h1.y));
+            al[u] = __builtin_bit_cast(bf16x8, make_uint4(l0.x, l0.y, l1.x, l1.y));
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            acc[eg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[u], bl, acc[eg + u], 0, 0, 0);
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            acc[eg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[u], bh, acc[eg + u], 0, 0, 0);
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            acc[eg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[u], bh, acc[eg + u], 0, 0, 0);
         }
       }
 
@@ -559,8 +600,7 @@ __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
       for (int i = 0; i < St::kPasses; ++i) {
         const int tok = i * St::kRowsPerPass + rl;
         const uint4 ov = *reinterpret_cast<const uint4 *>(stage + tok * St::kRowBytes + 2 * rc);
-        if (tile + tok < n_end)
-          *reinterpret_cast<uint4 *>(out + rows_base + tok * row_stride + rc) = ov;
+        buf_store16(ro, ((uint32_t)(tile - n_begin) + tok) * row_bytes + 2 * rc, ov);
       }
       // the next tile's first staging writes must not overtake these reads
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -568,38 +608,21 @@ __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  // Two tiles of loads stay in flight per wave: tile i computes while the
-  // loads of tiles i+1 and i+2 are outstanding.
+  // Two tiles of loads stay in flight per wave: buffer A holds tile i while
+  // B receives tile i+1; once tile i is done, A is refilled with tile i+2
+  // before tile i+1 (in B) is processed, and so on.
   constexpr int64_t kStep = 16 * NW;
   uint4 qa[KS], ga[St::kPasses], qb[KS], gb[St::kPasses];
   int64_t tile = n_begin + 16 * wave;
   if (tile < n_end) fetch(tile, qa, ga);
   if (tile + kStep < n_end) fetch(tile + kStep, qb, gb);
   while (tile < n_end) {
-    // keep the (loop-invariant) LDS fragment reads inside the loop: hoisting
-    // all of them would need 256 registers per lane
-    asm volatile("" ::: "memory");
-    {
-      uint4 cq[KS], cg[St::kPasses];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) cq[ks] = qa[ks];
-#pragma unroll
-      for (int i = 0; i < St::kPasses; ++i) cg[i] = ga[i];
-      if (tile + 2 * kStep < n_end) fetch(tile + 2 * kStep, qa, ga);
-      process(tile, cq, cg);
-    }
+    process(tile, qa, ga);
+    if (tile + 2 * kStep < n_end) fetch(tile + 2 * kStep, qa, ga);
     tile += kStep;
     if (tile >= n_end) break;
-    asm volatile("" ::: "memory");
-    {
-      uint4 cq[KS], cg[St::kPasses];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) cq[ks] = qb[ks];
-#pragma unroll
-      for (int i = 0; i < St::kPasses; ++i) cg[i] = gb[i];
-      if (tile + 2 * kStep < n_end) fetch(tile + 2 * kStep, qb, gb);
-      process(tile, cq, cg);
-    }
+    process(tile, qb, gb);
+    if (tile + 2 * kStep < n_end) fetch(tile + 2 * kStep, qb, gb);
     tile += kStep;
   }
 }
