@@ -22,6 +22,7 @@
 
 #include "gla_internal.h"
 
+
 namespace gla {
 namespace {
 
@@ -52,13 +53,28 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rows_rsrc(const uint16_t 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(first_row), 0, (int)bytes,
                                            0x00020000);
 }
+// Cache policy of a buffer access: kCacheNormal, or kCacheStream for data
+// touched exactly once (the non-temporal hint: the line is not kept for
+// reuse).
+constexpr int kCacheNormal = 0;
+constexpr int kCacheStream = 2;
+// Policies of the streams of the two stages.  Measured over whole
+// forward calls at 720p/81f: streaming the k and v reads of the state stage
+// saves about 3% per call; streaming the q and g reads or the out writes of
+// the apply stage only moves time between the stages (a normal write of out
+// is paid for when its dirty lines are evicted during the next state stage).
+constexpr int kStateLoadPolicy = kCacheStream;
+constexpr int kApplyLoadPolicy = kCacheNormal;
+constexpr int kApplyStorePolicy = kCacheNormal;
+template <int Policy = kCacheNormal>
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, Policy);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+template <int Policy = kCacheNormal>
 __device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 x) {
   const u32x4 v = {x.x, x.y, x.z, x.w};
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, Policy);
 }
 
 // Token index (within a batch entry, < 2^31) -> (t, h, w) of the t-major grid.
@@ -120,11 +136,26 @@ struct TabSlice {
   int sp_entries;  // (Hs + Ws) * 3D/16
   int Hs;
   int t_lo;
-  __device__ __forceinline__ int index(int axis, int pia, int t, int h, int w) const {
+  // Entry of the first of four (cos, sin) pairs for pair group pia of an
+  // axis, at grid position (t, h, w): entry = base + t*mt + h*mh + w*mw.
+  // Written as arithmetic (two of the
+  // multipliers are 0) so that the compiler cannot turn the axis choice into
+  // a divergent branch, which would make it wait for every outstanding load
+  // at the join.
+  struct Lookup {
+    int base, mt, mh, mw;
+    __device__ __forceinline__ int at(int t, int h, int w) const {
+      return base + t * mt + h * mh + w * mw;
+    }
+  };
+  __device__ __forceinline__ Lookup lookup(int axis, int pia) const {
     constexpr int ph = 3 * D / 16;
-    if (axis == 0) return sp_entries + (t - t_lo) * (D / 8) + pia;
-    if (axis == 1) return h * ph + pia;
-    return Hs * ph + w * ph + pia;
+    Lookup l;
+    l.mt = axis == 0 ? D / 8 : 0;
+    l.mh = axis == 1 ? ph : 0;
+    l.mw = axis == 2 ? ph : 0;
+    l.base = pia + (axis == 0 ? sp_entries - t_lo * (D / 8) : (axis == 2 ? Hs * ph : 0));
+    return l;
   }
 };
 
@@ -232,6 +263,7 @@ __global__ __launch_bounds__(kBlock) void state_mfma_kernel(const uint16_t *__re
   const int fc = tid % FPT, tg = tid / FPT;
   int axis, pia;
   pair_axis<D>(4 * fc, axis, pia);
+  const typename TabSlice<D>::Lookup tl = ts.lookup(axis, pia);
   // this thread's rows of a tile: tg + TPP*r, 16-byte unit fc
   const int wr_off = Cfg::off(tg, fc);
 
@@ -258,23 +290,21 @@ __global__ __launch_bounds__(kBlock) void state_mfma_kernel(const uint16_t *__re
     }
   }
 
-  // row pointers of this thread: token n_begin + tg (+ TPP*r, + 64 per step)
-  const int64_t row_elems = a.H * D;
-  const uint16_t *kp = k + ((b * a.N + n_begin + tg) * a.H + hd) * D + 8 * fc;
-  const uint16_t *vp = v + ((b * a.N + n_begin + tg) * a.H + hd) * D + 8 * fc;
+  // buffer resources over this chunk's rows of k and v (rows past the chunk
+  // read as zeros)
+  const int64_t first = ((b * a.N + n_begin) * a.H + hd) * D;
+  const uint32_t row_bytes = (uint32_t)(a.H * D * 2);
+  const uint32_t range_bytes = (uint32_t)(n_end - n_begin - 1) * row_bytes + 2 * D;
+  const __amdgpu_buffer_rsrc_t rk = head_rows_rsrc(k + first, range_bytes);
+  const __amdgpu_buffer_rsrc_t rv = head_rows_rsrc(v + first, range_bytes);
+  const uint32_t my_off = (uint32_t)tg * row_bytes + 16 * fc;
   uint4 kr[R], vr[R];
   auto load_rows = [&](int64_t n0) {
-    const int64_t step = n0 - n_begin;
+    const uint32_t base = (uint32_t)(n0 - n_begin) * row_bytes + my_off;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      if (n0 + tg + TPP * r < n_end) {
-        const int64_t off = (step + TPP * r) * row_elems;
-        kr[r] = *reinterpret_cast<const uint4 *>(kp + off);
-        vr[r] = *reinterpret_cast<const uint4 *>(vp + off);
-      } else {
-        kr[r] = make_uint4(0, 0, 0, 0);
-        vr[r] = make_uint4(0, 0, 0, 0);
-      }
+      kr[r] = buf_load16<kStateLoadPolicy>(rk, base + (uint32_t)(TPP * r) * row_bytes);
+      vr[r] = buf_load16<kStateLoadPolicy>(rv, base + (uint32_t)(TPP * r) * row_bytes);
     }
   };
 
@@ -287,13 +317,16 @@ __global__ __launch_bounds__(kBlock) void state_mfma_kernel(const uint16_t *__re
 #pragma unroll
   for (int j = 0; j < 8; ++j) zacc[j] = 0.f;
 
+  // Each 64-token step: ReLU/RoPE/split of the rows in (kr, vr) into the LDS
+  // tiles; once they are there, the same registers are refilled with the
+  // next step's rows, which stay in flight during the matrix-core phase.
   load_rows(n_begin);
   for (int64_t n0 = n_begin; n0 < n_end; n0 += kStateTile) {
     __syncthreads();  // the previous step's operand reads are done
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       int64_t n = n0 + tg + TPP * r;
-      if (n >= n_end) n = n_end - 1;  // position only; the row itself is zero
+      if (n >= n_end) n = n_end - 1;  // position only; the row itself reads as zero
       int t, h, w;
       token_pos(a, n, t, h, w);
       const uint32_t kw[4] = {kr[r].x, kr[r].y, kr[r].z, kr[r].w};
@@ -306,7 +339,7 @@ __global__ __launch_bounds__(kBlock) void state_mfma_kernel(const uint16_t *__re
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) zacc[j] += x[j];
-      const float2 *cs = s_tab + ts.index(axis, pia, t, h, w);
+      const float2 *cs = s_tab + tl.at(t, h, w);
       float2 c4[4] = {cs[0], cs[1], cs[2], cs[3]};
       rotate4(x, c4);
       uint4 hi, lo;
@@ -319,7 +352,9 @@ __global__ __launch_bounds__(kBlock) void state_mfma_kernel(const uint16_t *__re
       *reinterpret_cast<uint4 *>(s_kl + o) = lo;
       *reinterpret_cast<uint4 *>(s_v + o) = vr[r];
     }
-    if (n0 + kStateTile < n_end) load_rows(n0 + kStateTile);
+    // unconditional (rows past the chunk read as zeros): a conditional load
+    // here would make the compiler wait for it before the matrix-core phase
+    load_rows(n0 + kStateTile);
     __syncthreads();
 #pragma unroll
     for (int ks = 0; ks < (int)kStateTile / 16; ++ks) {
@@ -496,10 +531,10 @@ __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
     const uint32_t rel = (uint32_t)(tile - n_begin);
     const uint32_t qoff = (rel + nl) * row_bytes + 2 * 8 * kg;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qraw[ks] = buf_load16(rq, qoff + 2 * 32 * ks);
+    for (int ks = 0; ks < KS; ++ks) qraw[ks] = buf_load16<kApplyLoadPolicy>(rq, qoff + 2 * 32 * ks);
 #pragma unroll
     for (int i = 0; i < St::kPasses; ++i)
-      grow[i] = buf_load16(rg, (rel + i * St::kRowsPerPass + rl) * row_bytes + 2 * rc);
+      grow[i] = buf_load16<kApplyLoadPolicy>(rg, (rel + i * St::kRowsPerPass + rl) * row_bytes + 2 * rc);
   };
   // everything after the loads of one tile
   auto process = [&](int64_t tile, const uint4 (&cq)[KS], const uint4 (&cg)[St::kPasses]) {
@@ -532,7 +567,7 @@ __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
         }
         int axis, pia;
         pair_axis<D>(16 * ks + 4 * kg, axis, pia);
-        const float2 *cs = s_tab + ts.index(axis, pia, t, h, w);
+        const float2 *cs = s_tab + ts.lookup(axis, pia).at(t, h, w);
         float2 c4[4] = {cs[0], cs[1], cs[2], cs[3]};
         rotate4(x, c4);
         uint32_t hw4[4], lw4[4];
@@ -600,7 +635,7 @@ __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
       for (int i = 0; i < St::kPasses; ++i) {
         const int tok = i * St::kRowsPerPass + rl;
         const uint4 ov = *reinterpret_cast<const uint4 *>(stage + tok * St::kRowBytes + 2 * rc);
-        buf_store16(ro, ((uint32_t)(tile - n_begin) + tok) * row_bytes + 2 * rc, ov);
+        buf_store16<kApplyStorePolicy>(ro, ((uint32_t)(tile - n_begin) + tok) * row_bytes + 2 * rc, ov);
       }
       // the next tile's first staging writes must not overtake these reads
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
