@@ -131,14 +131,20 @@ __device__ __forceinline__ void pair_axis(int P0, int &axis, int &pia) {
 
 // LDS copy of the RoPE table rows a workgroup touches: the h rows and the w
 // rows (both whole), then the temporal rows t_lo..t_hi of its token range.
+// A lane always needs the (cos, sin) entries of four consecutive pairs (a
+// "group"; every axis row holds a whole number of groups).  The slice is
+// stored as two planes of 16-byte units, pairs 0-1 of every group in the
+// first and pairs 2-3 in the second, so that lanes reading neighbouring
+// groups read neighbouring 16-byte units (the direct 32-byte layout leaves
+// half the LDS banks idle and serialises on the other half).
 template <int D>
 struct TabSlice {
-  int sp_entries;  // (Hs + Ws) * 3D/16
+  int sp_groups;  // (Hs + Ws) * 3D/64 groups of the spatial rows
+  int groups;     // groups in the slice (size of one plane)
   int Hs;
   int t_lo;
-  // Entry of the first of four (cos, sin) pairs for pair group pia of an
-  // axis, at grid position (t, h, w): entry = base + t*mt + h*mh + w*mw.
-  // Written as arithmetic (two of the
+  // Group of the pair group pia/4 of an axis at grid position (t, h, w):
+  // g = base + t*mt + h*mh + w*mw.  Written as arithmetic (two of the
   // multipliers are 0) so that the compiler cannot turn the axis choice into
   // a divergent branch, which would make it wait for every outstanding load
   // at the join.
@@ -149,13 +155,22 @@ struct TabSlice {
     }
   };
   __device__ __forceinline__ Lookup lookup(int axis, int pia) const {
-    constexpr int ph = 3 * D / 16;
+    constexpr int gt = D / 32, gh = 3 * D / 64;  // groups per t row, per h or w row
     Lookup l;
-    l.mt = axis == 0 ? D / 8 : 0;
-    l.mh = axis == 1 ? ph : 0;
-    l.mw = axis == 2 ? ph : 0;
-    l.base = pia + (axis == 0 ? sp_entries - t_lo * (D / 8) : (axis == 2 ? Hs * ph : 0));
+    l.mt = axis == 0 ? gt : 0;
+    l.mh = axis == 1 ? gh : 0;
+    l.mw = axis == 2 ? gh : 0;
+    l.base = pia / 4 + (axis == 0 ? sp_groups - t_lo * gt : (axis == 2 ? Hs * gh : 0));
     return l;
+  }
+  // the four (cos, sin) entries of group g
+  __device__ __forceinline__ void read(const float2 *s_tab, int g, float2 (&c4)[4]) const {
+    const float4 a = reinterpret_cast<const float4 *>(s_tab)[g];
+    const float4 b = reinterpret_cast<const float4 *>(s_tab)[groups + g];
+    c4[0] = make_float2(a.x, a.y);
+    c4[1] = make_float2(a.z, a.w);
+    c4[2] = make_float2(b.x, b.y);
+    c4[3] = make_float2(b.z, b.w);
   }
 };
 
@@ -166,13 +181,18 @@ __device__ TabSlice<D> load_tab_slice(float2 *s_tab, const float2 *__restrict__ 
   const int64_t hw = a.Hs * a.Ws;
   TabSlice<D> ts;
   ts.Hs = (int)a.Hs;
-  ts.sp_entries = (int)((a.Hs + a.Ws) * ph);
+  const int sp_entries = (int)((a.Hs + a.Ws) * ph);
+  ts.sp_groups = sp_entries / 4;
   ts.t_lo = (int)(n_begin / hw);
   const int t_hi = (int)((n_end - 1) / hw);
-  const int nt = (t_hi - ts.t_lo + 1) * (D / 8);
-  for (int i = threadIdx.x; i < ts.sp_entries; i += blockDim.x) s_tab[i] = tab[a.tab_h_off + i];
-  for (int i = threadIdx.x; i < nt; i += blockDim.x)
-    s_tab[ts.sp_entries + i] = tab[(int64_t)ts.t_lo * (D / 8) + i];
+  const int entries = sp_entries + (t_hi - ts.t_lo + 1) * (D / 8);
+  ts.groups = entries / 4;
+  for (int i = threadIdx.x; i < entries; i += blockDim.x) {
+    const float2 cs = i < sp_entries ? tab[a.tab_h_off + i]
+                                     : tab[(int64_t)ts.t_lo * (D / 8) + (i - sp_entries)];
+    // entry i = pair i % 4 of group i / 4
+    s_tab[(i & 2) * ts.groups + 2 * (i >> 2) + (i & 1)] = cs;
+  }
   return ts;
 }
 
@@ -339,8 +359,8 @@ __global__ __launch_bounds__(kBlock) void state_mfma_kernel(const uint16_t *__re
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) zacc[j] += x[j];
-      const float2 *cs = s_tab + tl.at(t, h, w);
-      float2 c4[4] = {cs[0], cs[1], cs[2], cs[3]};
+      float2 c4[4];
+      ts.read(s_tab, tl.at(t, h, w), c4);
       rotate4(x, c4);
       uint4 hi, lo;
       split_bf16x2(x[0], x[1], hi.x, lo.x);
@@ -567,8 +587,8 @@ __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
         }
         int axis, pia;
         pair_axis<D>(16 * ks + 4 * kg, axis, pia);
-        const float2 *cs = s_tab + ts.lookup(axis, pia).at(t, h, w);
-        float2 c4[4] = {cs[0], cs[1], cs[2], cs[3]};
+        float2 c4[4];
+        ts.read(s_tab, ts.lookup(axis, pia).at(t, h, w), c4);
         rotate4(x, c4);
         uint32_t hw4[4], lw4[4];
 #pragma unroll
