@@ -100,6 +100,31 @@ gla_status check_pointers(const void *q, const void *k, const void *v, const voi
 }
 
 // ---------------------------------------------------------------- planning
+// Number of pieces to cut each of `units` token runs of `len` tokens into
+// (pieces of a multiple of `tile` tokens, at least `min_len` long), such that
+// the units * pieces workgroups fill whole rounds of `slots` workgroups that
+// are resident at once: the fewest rounds (up to four) whose last round is at
+// least 90% full, else the fullest last round.  A ragged last round leaves
+// compute units idle at the end of the stage, and fewer, longer workgroups
+// stream HBM better than many short ones.
+int64_t pick_pieces(int64_t units, int64_t len, int64_t tile, int64_t min_len, int64_t slots) {
+  const int64_t max_pieces = std::max<int64_t>(1, len / std::max(min_len, tile));
+  int64_t best = 1;
+  double best_fill = -1.0;
+  for (int64_t rounds = 1; rounds <= 4; ++rounds) {
+    int64_t n = std::min(max_pieces, std::max<int64_t>(1, rounds * slots / units));
+    n = ceil_div(len, round_up(ceil_div(len, n), tile));  // after rounding to the tile
+    const int64_t wgs = units * n;
+    const double fill = (double)wgs / (double)(ceil_div(wgs, slots) * slots);
+    if (fill >= 0.9) return n;
+    if (fill > best_fill) {
+      best_fill = fill;
+      best = n;
+    }
+  }
+  return best;
+}
+
 // aligned16: every tensor pointer is 16-byte aligned (the matrix-core
 // kernels move 16-byte vectors).
 gla_status make_plan(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, int64_t d,
@@ -136,10 +161,10 @@ gla_status make_plan(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, in
   const int64_t tile_s = P.mfma ? gla::kStateTile : 16;
   const int64_t tile_a = P.mfma ? gla::kApplyTile * 8 : 16;
 
-  // State stage: about two workgroups per compute unit in total.
-  const int64_t target_state = 2 * (int64_t)cus;
-  int64_t C = std::max<int64_t>(1, std::min(ceil_div(target_state, P.units), ceil_div(P.L, 256)));
-  int64_t Lc = round_up(ceil_div(P.L, C), tile_s);
+  // State stage: two workgroups resident per compute unit, chunks of at
+  // least 256 tokens.
+  const int64_t C0 = pick_pieces(P.units, P.L, tile_s, 256, 2 * (int64_t)cus);
+  int64_t Lc = round_up(ceil_div(P.L, C0), tile_s);
   if (P.mfma) {
     // temporal rows of a chunk: at most ceil(Lc / hw) + 1
     int64_t max_rows = (gla::kStateTabEntries - spatial_entries) / pt;
@@ -149,10 +174,16 @@ gla_status make_plan(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, in
   P.Lc = Lc;
   P.C = ceil_div(P.L, Lc);
 
-  // Apply stage: about four workgroups per compute unit, 128..4096 tokens each.
-  const int64_t target_apply = 4 * (int64_t)cus;
-  int64_t Lr = round_up(ceil_div(P.units * P.L, target_apply), tile_a);
-  Lr = std::max<int64_t>(tile_a, std::min<int64_t>(Lr, 4096));
+  // Apply stage: the matrix-core kernel holds one workgroup per compute unit
+  // (its LDS); the vector kernel takes about four per compute unit of
+  // 16..4096 tokens each.
+  int64_t Lr;
+  if (P.mfma) {
+    Lr = round_up(ceil_div(P.L, pick_pieces(P.units, P.L, tile_a, tile_a, cus)), tile_a);
+  } else {
+    Lr = round_up(ceil_div(P.units * P.L, 4 * (int64_t)cus), tile_a);
+    Lr = std::max<int64_t>(tile_a, std::min<int64_t>(Lr, 4096));
+  }
   if (P.mfma) {
     int64_t max_rows = (gla::kApplyTabEntries - spatial_entries) / pt;
     int64_t max_len = std::max<int64_t>(tile_a, ((max_rows - 1) * hw) / tile_a * tile_a);
