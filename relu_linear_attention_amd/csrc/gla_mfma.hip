@@ -224,13 +224,22 @@ __device__ __forceinline__ uint2 lds_read_tr16(const unsigned char *p) {
   return __builtin_bit_cast(uint2, r);
 }
 
+// Threads per workgroup of the state kernel: d = 128 runs eight waves (two
+// workgroups, 16 waves, per compute unit, in at most 128 registers per
+// lane: the eight waves share one RoPE table slice, and twice the waves hide
+// more of the load latency than four waves with 4 tiles each), d = 64 four.
+template <int D>
+constexpr int kStateThreads = D == 128 ? 512 : 256;
+
 template <int D>
 struct StateCfg {
+  static constexpr int NT = kStateThreads<D>;
+  static constexpr int NWV = NT / 64;                // waves
   static constexpr int FPT = D / 8;                  // threads per token row (16 B each)
-  static constexpr int TPP = kBlock / FPT;           // tokens per load pass
+  static constexpr int TPP = NT / FPT;               // tokens per load pass
   static constexpr int R = (int)kStateTile / TPP;    // passes per tile
   static constexpr int TILES = (D / 32) * (D / 32);  // 32x32 output tiles of S
-  static constexpr int TPW = TILES / 4;              // tiles per wave
+  static constexpr int TPW = TILES / NWV;            // tiles per wave
   static constexpr int ROW = 2 * D;                  // bytes per token row
   static constexpr int OP_BYTES = (int)kStateTile * ROW;
   // Operand tiles are row-major [token][feature] with the 16-byte units of a
@@ -246,7 +255,7 @@ struct StateCfg {
   }
 };
 
-// One workgroup per (unit, chunk).  Each 64-token step: 256 threads load the
+// One workgroup per (unit, chunk).  Each 64-token step: the threads load the
 // k and v rows (16 B per thread per row, whole rows per instruction), apply
 // ReLU (accumulating z) and RoPE to k in fp32, and write RoPE(phi(k)) split
 // into bf16 hi + lo parts, and v (exact in bf16), as row-major tiles into
@@ -255,7 +264,7 @@ struct StateCfg {
 // S = hi^T v + lo^T v on the matrix cores.  The rows of the next step are in
 // flight in registers meanwhile.
 template <int D>
-__global__ __launch_bounds__(kBlock) void state_mfma_kernel(const uint16_t *__restrict__ k,
+__global__ __launch_bounds__(kStateThreads<D>, kStateThreads<D> / 128) void state_mfma_kernel(const uint16_t *__restrict__ k,
                                                             const uint16_t *__restrict__ v,
                                                             const float2 *__restrict__ tab,
                                                             float *__restrict__ partials,
@@ -296,7 +305,10 @@ __global__ __launch_bounds__(kBlock) void state_mfma_kernel(const uint16_t *__re
     const int rrow = 8 * (g >> 1) + (sl >> 2);
 #pragma unroll
     for (int t = 0; t < Cfg::TPW; ++t) {
-      if (D == 128) {
+      if (D == 128 && Cfg::NWV == 8) {
+        tile_p[t] = wave >> 1;
+        tile_e[t] = 2 * (wave & 1) + t;
+      } else if (D == 128) {
         tile_p[t] = 2 * (wave >> 1) + (t >> 1);
         tile_e[t] = 2 * (wave & 1) + (t & 1);
       } else {
@@ -709,7 +721,7 @@ hipError_t state_d(const Plan &p, const void *k, const void *v, const float2 *ta
   hipError_t e = hipFuncSetAttribute((const void *)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(p.units * p.C)), dim3(kBlock), lds, stream,
+  hipLaunchKernelGGL(kern, dim3((unsigned)(p.units * p.C)), dim3(StateCfg<D>::NT), lds, stream,
                      (const uint16_t *)k, (const uint16_t *)v, tab, part, make_margs(p));
   return hipGetLastError();
 }
