@@ -60,6 +60,8 @@ def _load():
     lib.ora_apply.restype = ctypes.c_int
     lib.ora_forward.argtypes = [_ptr] * 4 + [_i64] * 7 + [_dbl, _dbl, _ptr, _ptr]
     lib.ora_forward.restype = ctypes.c_int
+    lib.ora_block_step.argtypes = [_ptr] * 6 + [_i64] * 7 + [_dbl, _dbl, _ptr, _ptr, _ptr]
+    lib.ora_block_step.restype = ctypes.c_int
     lib.ora_num_blocks.argtypes = [_i64, _i64]
     lib.ora_num_blocks.restype = _i64
     lib.ora_num_threads.argtypes = []
@@ -154,3 +156,28 @@ def forward(q, k, v, g, grid, frames_per_block: int = 0, theta: float = 10000.0,
                              float(theta), float(eps), _p(p0), _p(out))
     _check(rc, "forward")
     return out
+
+
+def block_step(q, k, v, g, S_cache, z_cache, block_grid, t_offset: int, theta: float = 10000.0,
+               eps: float = 1e-6, want_out: bool = True):
+    """One step of the streaming block-causal mode: a block of Tb x Hs x Ws
+    tokens ([B, N_b, H, d]) whose first frame is at temporal position
+    t_offset, attending to itself and to the cache (S_cache [B, H, d, d],
+    z_cache [B, H, d]).  Returns (out [B, N_b, H, d] or None, S_new, z_new),
+    all fp64; q and g may be None when want_out is False."""
+    k, v = _f32(k), _f32(v)
+    B, N, H, d = k.shape
+    Tb, Hs, Ws = block_grid
+    assert N == Tb * Hs * Ws and v.shape == k.shape
+    S_cache = np.ascontiguousarray(S_cache, dtype=np.float64).reshape(B, H, d, d)
+    z_cache = np.ascontiguousarray(z_cache, dtype=np.float64).reshape(B, H, d)
+    qq = _f32(q) if want_out else None
+    gg = _f32(g) if want_out else None
+    out = np.empty((B, N, H, d), dtype=np.float64) if want_out else None
+    S_new = np.empty((B, H, d, d), dtype=np.float64)
+    z_new = np.empty((B, H, d), dtype=np.float64)
+    rc = _load().ora_block_step(_p(qq), _p(k), _p(v), _p(gg), _p(S_cache), _p(z_cache), B, H, Tb,
+                                Hs, Ws, d, int(t_offset), float(theta), float(eps), _p(out),
+                                _p(S_new), _p(z_new))
+    _check(rc, "block_step")
+    return out, S_new, z_new

@@ -260,6 +260,46 @@ int ora_forward(const float *q, const float *k, const float *v, const float *g, 
   return rc;
 }
 
+/* One step of the streaming block-causal mode ([V1c], and Algorithm 1 on the
+ * same page: a block is generated with the cache of the earlier blocks, and
+ * the cache is then updated with the block's own sums).  The block holds Tb
+ * latent frames of a Tb x Hs x Ws grid whose first frame sits at absolute
+ * temporal position t_offset; (S_cache, z_cache) are the sums over every
+ * earlier block ([B, H, d, d] and [B, H, d] double).  The block attends to
+ * itself and to the cache, as in the causal form on that page:
+ *   S_tot = S_cache + S_blk,  z_tot = z_cache + z_blk,
+ *   out   = the apply step with (S_tot, z_tot)        (skipped if out is NULL)
+ *   S_new = S_tot, z_new = z_tot                      (if non-NULL)
+ * q and g may be NULL when out is NULL. */
+int ora_block_step(const float *q, const float *k, const float *v, const float *g,
+                   const double *S_cache, const double *z_cache, int64_t B, int64_t H,
+                   int64_t Tb, int64_t Hs, int64_t Ws, int64_t d, int64_t t_offset, double theta,
+                   double eps, double *out, double *S_new, double *z_new) {
+  if (!k || !v || !S_cache || !z_cache || t_offset < 0) return ORA_BAD_ARG;
+  if (out && (!q || !g)) return ORA_BAD_ARG;
+  int rc = check_shape(B, H, Tb, Hs, Ws, d, 0);
+  if (rc) return rc;
+  const int64_t pos0[3] = {t_offset, 0, 0};
+  double *S = (double *)malloc((size_t)(B * H * d * d) * sizeof(double));
+  double *z = (double *)malloc((size_t)(B * H * d) * sizeof(double));
+  if (!S || !z) {
+    free(S);
+    free(z);
+    return ORA_NO_MEM;
+  }
+  rc = ora_state(k, v, B, H, Tb, Hs, Ws, d, 0, theta, pos0, S, z); /* the block's own sums */
+  if (rc == ORA_OK) {
+    for (int64_t i = 0; i < B * H * d * d; ++i) S[i] += S_cache[i];
+    for (int64_t i = 0; i < B * H * d; ++i) z[i] += z_cache[i];
+    if (out) rc = ora_apply(q, g, S, z, B, H, Tb, Hs, Ws, d, 0, theta, eps, pos0, NULL, 0, out);
+    if (S_new) memcpy(S_new, S, (size_t)(B * H * d * d) * sizeof(double));
+    if (z_new) memcpy(z_new, z, (size_t)(B * H * d) * sizeof(double));
+  }
+  free(S);
+  free(z);
+  return rc;
+}
+
 /* Number of threads OpenMP will use (reported by the benchmark's CPU leg). */
 int ora_num_threads(void) {
   int n = 1;

@@ -42,6 +42,12 @@ MUTATIONS = [
      "int64_t blk = (n / tokens_per_block + 1) % nb;\n        int64_t pos[3];"),
     ("value_dropped_last_feature", "vrow[p] = (double)vn[p];",
      "vrow[p] = (p + 1 < d) ? (double)vn[p] : 0.0;"),
+    ("block_step_cache_ignored", "for (int64_t i = 0; i < B * H * d * d; ++i) S[i] += S_cache[i];",
+     "for (int64_t i = 0; i < B * H * d * d; ++i) S[i] += 0.0 * S_cache[i];"),
+    ("block_step_normaliser_cache_ignored", "for (int64_t i = 0; i < B * H * d; ++i) z[i] += z_cache[i];",
+     "for (int64_t i = 0; i < B * H * d; ++i) z[i] += 0.0 * z_cache[i];"),
+    ("block_step_offset_ignored", "const int64_t pos0[3] = {t_offset, 0, 0};",
+     "const int64_t pos0[3] = {0, 0, 0};"),
 ]
 
 

@@ -409,3 +409,99 @@ def test_host_inputs_are_seeded():
         np.testing.assert_array_equal(a[n], b[n])
         assert not np.array_equal(a[n], c[n])
         np.testing.assert_array_equal(round_to_bf16(a[n]), a[n])
+
+
+# ---------------------------------------------------------------------------
+# streaming block-causal step ([V1] Section 3.4 and its Algorithm 1: a block
+# is produced with the cache of the earlier blocks, then the cache takes the
+# block's own sums)
+# ---------------------------------------------------------------------------
+def _stream(x, grid, Tb, theta=10000.0, eps=1e-6):
+    """Run the blocks of a grid one step at a time from an empty cache."""
+    B, N, H, d = x["q"].shape
+    T, Hs, Ws = grid
+    per = Tb * Hs * Ws
+    S = np.zeros((B, H, d, d))
+    z = np.zeros((B, H, d))
+    outs = []
+    for b0 in range(0, T, Tb):
+        sl = slice(b0 * Hs * Ws, b0 * Hs * Ws + per)
+        blk = {n: a[:, sl] for n, a in x.items()}
+        out, S, z = oracle.block_step(blk["q"], blk["k"], blk["v"], blk["g"], S, z, (Tb, Hs, Ws),
+                                      b0, theta, eps)
+        outs.append(out)
+    return np.concatenate(outs, axis=1), S, z
+
+
+def test_streaming_replays_worked_example():
+    # the two-token worked example, one frame per block, fed block by block
+    fx, a = _load_fixture("worked_example_block_causal.json")
+    S0, z0 = np.zeros((1, 1, 16, 16)), np.zeros((1, 1, 16))
+    tok = lambda i: {n: arr[:, i:i + 1] for n, arr in a.items()}
+    out0, S1, z1 = oracle.block_step(tok(0)["q"], tok(0)["k"], tok(0)["v"], tok(0)["g"], S0, z0,
+                                     (1, 1, 1), 0, fx["theta"], fx["eps"])
+    # after block 0 the cache holds S[0][5] = 1 and z = e0 (the derivation's first state)
+    S_exp = np.zeros((16, 16))
+    S_exp[0, 5] = 1.0
+    np.testing.assert_array_equal(S1[0, 0], S_exp)
+    np.testing.assert_array_equal(z1[0, 0], np.eye(16)[0])
+    out1, _, _ = oracle.block_step(tok(1)["q"], tok(1)["k"], tok(1)["v"], tok(1)["g"], S1, z1,
+                                   (1, 1, 1), 1, fx["theta"], fx["eps"])
+    exp = _expected(fx["expected"], (1, 2, 1, 16))
+    np.testing.assert_allclose(out0, exp[:, 0:1], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(out1, exp[:, 1:2], rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("B,T,Hs,Ws,H,d,theta,Tb", [
+    (1, 4, 2, 3, 2, 32, 10000.0, 1),
+    (2, 4, 3, 2, 1, 16, 50.0, 2),
+    (1, 6, 2, 2, 2, 64, 7.0, 3),
+])
+def test_streaming_matches_brute_force_causal(B, T, Hs, Ws, H, d, theta, Tb):
+    x = host_inputs(B, T, Hs, Ws, H, d, "f32", seed=31)
+    got, _, _ = _stream(x, (T, Hs, Ws), Tb, theta)
+    ref = brute_force(x["q"], x["k"], x["v"], x["g"], (T, Hs, Ws), Tb, theta)
+    assert _rel_err(got, ref, floor=1e-9) < 1e-10
+
+
+def test_streaming_equals_block_causal_forward():
+    x = host_inputs(1, 6, 3, 4, 2, 32, "f32", seed=32)
+    got, S, z = _stream(x, (6, 3, 4), 2)
+    ref = oracle.forward(x["q"], x["k"], x["v"], x["g"], (6, 3, 4), 2)
+    assert _rel_err(got, ref, floor=1e-9) < 1e-11
+    # the final cache is the state of the whole grid
+    Sf, zf = oracle.state(x["k"], x["v"], (6, 3, 4))
+    np.testing.assert_allclose(S, Sf[:, :, 0], rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(z, zf[:, :, 0], rtol=1e-12, atol=1e-12)
+
+
+def test_block_at_offset_with_empty_cache_is_position_invariant():
+    # RoPE scores depend only on position differences: a lone block anywhere
+    # in time attends exactly as the same block at t = 0
+    x = host_inputs(1, 2, 3, 3, 2, 32, "f32", seed=33)
+    zero_S, zero_z = np.zeros((1, 2, 32, 32)), np.zeros((1, 2, 32))
+    ref = oracle.forward(x["q"], x["k"], x["v"], x["g"], (2, 3, 3))
+    for t0 in (0, 5, 240):
+        out, _, _ = oracle.block_step(x["q"], x["k"], x["v"], x["g"], zero_S, zero_z, (2, 3, 3), t0)
+        assert _rel_err(out, ref, floor=1e-9) < 1e-9
+
+
+def test_block_step_cache_update_is_the_block_state():
+    x = host_inputs(2, 2, 2, 3, 2, 16, "f32", seed=34)
+    rng = np.random.default_rng(5)
+    S_c = rng.standard_normal((2, 2, 16, 16))
+    z_c = np.abs(rng.standard_normal((2, 2, 16))) * 10
+    t0 = 7
+    out, S_new, z_new = oracle.block_step(x["q"], x["k"], x["v"], x["g"], S_c, z_c, (2, 2, 3), t0)
+    Sb, zb = oracle.state(x["k"], x["v"], (2, 2, 3), pos0=(t0, 0, 0))
+    np.testing.assert_allclose(S_new - S_c, Sb[:, :, 0], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(z_new - z_c, zb[:, :, 0], rtol=1e-12, atol=1e-12)
+    # the output reads the updated sums, and an update-only step gives the same cache
+    ref = oracle.apply(x["q"], x["g"], S_new[:, :, None], z_new[:, :, None], (2, 2, 3),
+                       pos0=(t0, 0, 0))
+    assert _rel_err(out, ref, floor=1e-12) < 1e-12
+    none, S2, z2 = oracle.block_step(None, x["k"], x["v"], None, S_c, z_c, (2, 2, 3), t0,
+                                     want_out=False)
+    assert none is None
+    np.testing.assert_array_equal(S2, S_new)
+    np.testing.assert_array_equal(z2, z_new)
