@@ -85,6 +85,59 @@ def cpu_baseline(w, dev_inputs):
     }
 
 
+def block_step_leg(steps: int, warmup: int, workload: str = "720p_block_causal"):
+    """The streaming block-causal step (gla_block_step): the layer's blocks of
+    frames_per_block latent frames fed one at a time through the fp32 cache,
+    each step updating it.  One pass = every block of the layer once."""
+    import torch
+
+    from relu_linear_attention_amd import gla
+    from relu_linear_attention_amd.inputs import WORKLOADS, device_inputs_for
+
+    w = WORKLOADS[workload]
+    Tb, hw = w.frames_per_block, w.Hs * w.Ws
+    x = device_inputs_for(w)
+    out = torch.empty_like(x["q"])
+    blocks = [{n: t[:, b0 * hw:(b0 + Tb) * hw] for n, t in list(x.items()) + [("out", out)]}
+              for b0 in range(0, w.T, Tb)]
+    S = torch.zeros((w.B, w.H, w.d, w.d), dtype=torch.float32, device="cuda")
+    z = torch.zeros((w.B, w.H, w.d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(gla.gla_workspace_bytes(w.B, w.H, Tb, w.Hs, w.Ws, w.d, 0, gla.GLA_BF16),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def one_pass():
+        S.zero_()
+        z.zero_()
+        for i, blk in enumerate(blocks):
+            gla.gla_block_step(blk["q"], blk["k"], blk["v"], blk["g"], blk["out"], S, z,
+                               (Tb, w.Hs, w.Ws), i * Tb, True, w.theta, w.eps, workspace=ws,
+                               stream=stream)
+
+    for _ in range(warmup):
+        one_pass()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        one_pass()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_pass = start.elapsed_time(stop) / steps
+    nblk = len(blocks)
+    tensor_bytes = 5 * w.B * w.N * w.H * w.d * w.elem_bytes
+    cache_bytes = nblk * 2 * 4 * w.B * w.H * (w.d * w.d + w.d)  # read + write per step
+    gbps = (tensor_bytes + cache_bytes) / (ms_pass * 1e-3) / 1e9
+    del x, out, blocks
+    return {
+        "workload": w.name, "blocks": nblk, "frames_per_block": Tb, "B": w.B, "H": w.H,
+        "tokens_per_block": Tb * hw, "ms_per_pass": ms_pass, "ms_per_step": ms_pass / nblk,
+        "tokens_per_s": w.B * w.N / (ms_pass * 1e-3),
+        "algorithmic_bytes_per_pass": tensor_bytes + cache_bytes, "GBps": gbps,
+        "frac_of_peak": gbps / PEAK_HBM_GBPS,
+    }
+
+
 def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
     """A plain device-to-device copy of known size, for scaling the HBM
     counters (FETCH_SIZE, WRITE_SIZE) of the kernels."""
@@ -111,6 +164,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-block-step", action="store_true",
+                    help="skip the streaming block-step measurement")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
@@ -211,6 +266,8 @@ def main() -> int:
         },
         "cpu_baseline": None,
     }
+    if not args.no_block_step:
+        result["block_step"] = block_step_leg(max(3, args.steps // 4), 2)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, x)
     print(json.dumps(result))

@@ -128,6 +128,37 @@ gla_status gla_state(const void *k, const void *v, float *S_out, float *z_out, i
                      int64_t frames_per_block, float rope_theta, gla_dtype dtype,
                      hipStream_t stream);
 
+/*
+ * One step of the streaming block-causal mode ("SANA-Video" Section 3.4
+ * and its Algorithm 1, the constant-memory cache): one temporal block of
+ * Tb latent frames (q, k, v, g, out are [B, Tb*Hs*Ws, H, d]) whose first
+ * frame sits at absolute temporal position t_offset, read against a
+ * caller-owned cache of the sums over every earlier block:
+ *   S_io [B, H, d, d] float (rows = key feature), z_io [B, H, d] float,
+ *   device memory, 4-byte aligned.
+ * With S_blk, z_blk the block's own state and normaliser, the block attends
+ * to itself and to the cache:
+ *   out = (RoPE(phi(q)) (S_io + S_blk)) / (phi(q) . (z_io + z_blk) + eps)
+ *         * sigmoid(g)
+ * and, when update != 0, the cache then takes the block's sums in place:
+ *   S_io += S_blk, z_io += z_blk.
+ * Feeding the blocks of a grid in order (t_offset = 0, Tb, 2 Tb, ...) with
+ * update = 1 from a zeroed cache reproduces gla_block_causal_forward with
+ * frames_per_block = Tb; the cache costs 4 (d*d + d) bytes per (batch,
+ * head) whatever the video length.
+ * out == NULL (q and g may then be NULL) only updates the cache, as after
+ * the last denoising step of a block; out == NULL with update == 0 is
+ * GLA_ERR_INVALID_ARG.  The cache may not overlap any tensor.
+ * workspace: NULL (taken stream-ordered on `stream`, like gla_forward) or
+ * at least gla_workspace_bytes(B, H, Tb, Hs, Ws, d, 0, dtype) bytes of
+ * device memory, 256-byte aligned (then nothing is allocated).
+ */
+gla_status gla_block_step(const void *q, const void *k, const void *v, const void *g, void *out,
+                          float *S_io, float *z_io, int64_t B, int64_t H, int64_t Tb, int64_t Hs,
+                          int64_t Ws, int64_t d, int64_t t_offset, int update, float rope_theta,
+                          float eps, gla_dtype dtype, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
 /* Static description of a status code. */
 const char *gla_status_string(gla_status status);
 

@@ -41,6 +41,15 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Streaming block step arguments of forward_impl (absent for the one-call
+// operators): the absolute position of the block's first frame and the
+// caller's cache.
+struct Step {
+  int64_t t0 = 0;
+  float *S_io = nullptr, *z_io = nullptr;
+  bool update = false;
+};
+
 // ---------------------------------------------------------------- devices
 std::mutex g_dev_mu;
 std::vector<int> g_cu_count;  // per device id, 0 = unknown
@@ -96,6 +105,35 @@ gla_status check_pointers(const void *q, const void *k, const void *v, const voi
   for (int i = 0; i < 4; ++i)
     if (ranges_overlap(out, bytes, ins[i], bytes))
       return fail(GLA_ERR_INVALID_ARG, "out overlaps input %s", names[i]);
+  return GLA_OK;
+}
+
+// gla_block_step: k and v always; q, g and out unless the call only updates
+// the cache; a cache that overlaps nothing; t_offset + Tb within int32.
+gla_status check_step(const void *q, const void *k, const void *v, const void *g, const void *out,
+                      size_t bytes, const Step &s, int64_t BH, int64_t d, int64_t Tb) {
+  if (!k || !v) return fail(GLA_ERR_INVALID_ARG, "null tensor pointer");
+  if (!s.S_io || !s.z_io) return fail(GLA_ERR_INVALID_ARG, "null cache pointer (S_io or z_io)");
+  if (out == nullptr && !s.update)
+    return fail(GLA_ERR_INVALID_ARG, "out is null and update is 0: the call would do nothing");
+  if (out != nullptr) {
+    gla_status st = check_pointers(q, k, v, g, out, bytes);
+    if (st != GLA_OK) return st;
+  }
+  if (s.t0 < 0 || s.t0 > (int64_t)INT32_MAX - Tb)
+    return fail(GLA_ERR_INVALID_ARG, "t_offset (%lld) must be in [0, 2^31 - 1 - Tb]",
+                (long long)s.t0);
+  if ((((uintptr_t)s.S_io) | ((uintptr_t)s.z_io)) & 3)
+    return fail(GLA_ERR_INVALID_ARG, "S_io and z_io must be 4-byte aligned");
+  const size_t sb = (size_t)(BH * d * d) * sizeof(float), zb = (size_t)(BH * d) * sizeof(float);
+  if (ranges_overlap(s.S_io, sb, s.z_io, zb))
+    return fail(GLA_ERR_INVALID_ARG, "S_io and z_io overlap");
+  const void *ts[5] = {q, k, v, g, out};
+  const char *names[5] = {"q", "k", "v", "g", "out"};
+  for (int i = 0; i < 5; ++i)
+    if (ts[i] != nullptr &&
+        (ranges_overlap(s.S_io, sb, ts[i], bytes) || ranges_overlap(s.z_io, zb, ts[i], bytes)))
+      return fail(GLA_ERR_INVALID_ARG, "the cache overlaps %s", names[i]);
   return GLA_OK;
 }
 
@@ -288,10 +326,20 @@ gla_status timed_launch(int stage, hipStream_t stream, const char *what, F &&lau
 }
 
 // ---------------------------------------------------------------- execution
+// The carried cache of a streaming block step: the reduce stage starts its
+// running sums from (S_in, z_in) and writes the final sums to (S_out, z_out)
+// (any of them may be null; S_out may be S_in).
+struct Cache {
+  const float *S_in = nullptr, *z_in = nullptr;
+  float *S_out = nullptr, *z_out = nullptr;
+};
+
 // Enqueues every stage of the operator on `stream`, with workspace `ws`.
-// With `apply == false` only the state is computed (gla_state).
+// With `apply == false` only the state is computed (gla_state, cache-only
+// block steps).
 gla_status run_plan(const Plan &P, const void *q, const void *k, const void *v, const void *g,
-                    void *out, void *ws, hipStream_t stream, bool apply) {
+                    void *out, void *ws, hipStream_t stream, bool apply,
+                    const Cache &cache = Cache()) {
   char *base = (char *)ws;
   float2 *tab = (float2 *)(base + P.off_tab);
   float *part = (float *)(base + P.off_part);
@@ -307,7 +355,8 @@ gla_status run_plan(const Plan &P, const void *q, const void *k, const void *v, 
   });
   if (st != GLA_OK) return st;
   st = timed_launch(2, stream, "reduce kernel", [&] {
-    return gla::launch_reduce(P, part, states, apply ? frags : nullptr, stream);
+    return gla::launch_reduce(P, part, states, apply ? frags : nullptr, cache.S_in, cache.z_in,
+                              cache.S_out, cache.z_out, stream);
   });
   if (st != GLA_OK) return st;
   if (!apply) return GLA_OK;
@@ -320,7 +369,8 @@ gla_status run_plan(const Plan &P, const void *q, const void *k, const void *v, 
 gla_status forward_impl(const void *q, const void *k, const void *v, const void *g, void *out,
                         int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, int64_t d,
                         int64_t F, float theta, float eps, gla_dtype dtype, void *ws,
-                        size_t ws_bytes, bool own_ws, hipStream_t stream) {
+                        size_t ws_bytes, bool own_ws, hipStream_t stream,
+                        const Step *step = nullptr) {
   g_last_error[0] = '\0';
   gla_status st = check_sizes(B, H, T, Hs, Ws, d, F, dtype);
   if (st != GLA_OK) return st;
@@ -328,8 +378,14 @@ gla_status forward_impl(const void *q, const void *k, const void *v, const void 
   if (!std::isfinite(eps) || eps < 0.f)
     return fail(GLA_ERR_INVALID_ARG, "eps must be finite and >= 0");
   const size_t bytes = (size_t)(B * T * Hs * Ws * H * d) * (dtype == GLA_BF16 ? 2 : 4);
-  st = check_pointers(q, k, v, g, out, bytes);
-  if (st != GLA_OK) return st;
+  const bool apply = out != nullptr || step == nullptr;
+  if (step != nullptr) {
+    st = check_step(q, k, v, g, out, bytes, *step, B * H, d, T);
+    if (st != GLA_OK) return st;
+  } else {
+    st = check_pointers(q, k, v, g, out, bytes);
+    if (st != GLA_OK) return st;
+  }
   if (!own_ws && (ws == nullptr || ((uintptr_t)ws & 255) != 0))
     return fail(GLA_ERR_INVALID_ARG, "workspace must be a non-null, 256-byte aligned pointer");
   int cus = 0;
@@ -340,11 +396,21 @@ gla_status forward_impl(const void *q, const void *k, const void *v, const void 
   Plan P;
   st = make_plan(B, H, T, Hs, Ws, d, F, dtype, theta, eps, cus, aligned16, &P);
   if (st != GLA_OK) return st;
+  Cache cache;
+  if (step != nullptr) {
+    P.t0 = step->t0;
+    cache.S_in = step->S_io;
+    cache.z_in = step->z_io;
+    if (step->update) {
+      cache.S_out = step->S_io;
+      cache.z_out = step->z_io;
+    }
+  }
   if (!own_ws) {
     if (ws_bytes < P.total_bytes)
       return fail(GLA_ERR_INVALID_ARG, "workspace too small: %zu bytes given, %zu needed", ws_bytes,
                   P.total_bytes);
-    return run_plan(P, q, k, v, g, out, ws, stream, true);
+    return run_plan(P, q, k, v, g, out, ws, stream, apply, cache);
   }
   void *mem = nullptr;
   hipError_t e = hipMallocAsync(&mem, P.total_bytes, stream);
@@ -353,7 +419,7 @@ gla_status forward_impl(const void *q, const void *k, const void *v, const void 
     return fail(GLA_ERR_ALLOC, "hipMallocAsync of %zu workspace bytes failed: %s", P.total_bytes,
                 hipGetErrorString(e));
   }
-  st = run_plan(P, q, k, v, g, out, mem, stream, true);
+  st = run_plan(P, q, k, v, g, out, mem, stream, apply, cache);
   e = hipFreeAsync(mem, stream);
   if (st == GLA_OK && e != hipSuccess) return hip_fail(e, "hipFreeAsync");
   return st;
@@ -454,6 +520,20 @@ gla_status gla_state(const void *k, const void *v, float *S_out, float *z_out, i
   e = hipFreeAsync(mem, stream);
   if (st == GLA_OK && e != hipSuccess) return hip_fail(e, "hipFreeAsync");
   return st;
+}
+
+gla_status gla_block_step(const void *q, const void *k, const void *v, const void *g, void *out,
+                          float *S_io, float *z_io, int64_t B, int64_t H, int64_t Tb, int64_t Hs,
+                          int64_t Ws, int64_t d, int64_t t_offset, int update, float rope_theta,
+                          float eps, gla_dtype dtype, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  Step s;
+  s.t0 = t_offset;
+  s.S_io = S_io;
+  s.z_io = z_io;
+  s.update = update != 0;
+  return forward_impl(q, k, v, g, out, B, H, Tb, Hs, Ws, d, 0, rope_theta, eps, dtype, workspace,
+                      workspace_bytes, workspace == nullptr, stream, &s);
 }
 
 const char *gla_status_string(gla_status status) {

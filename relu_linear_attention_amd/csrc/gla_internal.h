@@ -20,6 +20,7 @@ namespace gla {
 struct Plan {
   int64_t B, H, T, Hs, Ws, d;
   int64_t F;      // frames per block (== T when non-causal)
+  int64_t t0;     // absolute temporal position of frame 0 (streaming blocks)
   int64_t nb;     // temporal blocks per (batch, head)
   int64_t N;      // tokens per batch entry, T*Hs*Ws
   int64_t L;      // tokens per block
@@ -57,9 +58,12 @@ hipError_t launch_state_generic(const Plan &p, const void *k, const void *v, con
                                 float *partials, hipStream_t stream);
 // Fixed-order reduce of the partials plus the inclusive block prefix.
 // Writes fp32 states [units][d*d + d] and, for the matrix-core path, S as
-// row-major bf16 hi and lo parts [units][2][d][d].
+// row-major bf16 hi and lo parts [units][2][d][d].  S_in/z_in (optional,
+// [B*H][d][d] and [B*H][d]) start the running sums of each (batch, head);
+// S_out/z_out (optional, may alias S_in/z_in) receive the final sums.
 hipError_t launch_reduce(const Plan &p, const float *partials, float *states,
-                         uint16_t *frags, hipStream_t stream);
+                         uint16_t *frags, const float *S_in, const float *z_in, float *S_out,
+                         float *z_out, hipStream_t stream);
 // Output stage, vector kernels.
 hipError_t launch_apply_generic(const Plan &p, const void *q, const void *g, const float *states,
                                 const float2 *tab, void *out, hipStream_t stream);

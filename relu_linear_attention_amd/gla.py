@@ -25,7 +25,7 @@ GLA_NUM_STAGES = 4
 # every symbol include/gla.h declares
 EXPORTS = (
     "gla_forward", "gla_block_causal_forward", "gla_workspace_bytes", "gla_forward_ws",
-    "gla_state", "gla_status_string", "gla_last_error", "gla_profile_enable",
+    "gla_state", "gla_block_step", "gla_status_string", "gla_last_error", "gla_profile_enable",
     "gla_profile_read", "gla_stage_name", "gla_uses_matrix_cores",
 )
 
@@ -59,8 +59,12 @@ def load():
     lib.gla_forward_ws.argtypes = (tensors5 + sizes6 + [_i64, _f, _f, ctypes.c_int, _vp,
                                                         ctypes.c_size_t, _vp])
     lib.gla_state.argtypes = [_vp] * 4 + sizes6 + [_i64, _f, ctypes.c_int, _vp]
+    lib.gla_block_step.argtypes = (tensors5 + [_vp, _vp] + sizes6 + [_i64, ctypes.c_int, _f, _f,
+                                                                    ctypes.c_int, _vp,
+                                                                    ctypes.c_size_t, _vp])
     for name in ("gla_forward", "gla_block_causal_forward", "gla_workspace_bytes",
-                 "gla_forward_ws", "gla_state", "gla_profile_enable", "gla_profile_read"):
+                 "gla_forward_ws", "gla_state", "gla_block_step", "gla_profile_enable",
+                 "gla_profile_read"):
         getattr(lib, name).restype = ctypes.c_int
     lib.gla_status_string.argtypes = [ctypes.c_int]
     lib.gla_status_string.restype = ctypes.c_char_p
@@ -175,6 +179,23 @@ def gla_state(k, v, S_out, z_out, grid, frames_per_block=0, rope_theta=10000.0, 
     st = load().gla_state(_ptr(k), _ptr(v), _ptr(S_out), _ptr(z_out), B, H, T, Hs, Ws, d,
                           frames_per_block, rope_theta, _dtype_code(k), _stream_handle(stream))
     _check(st, "gla_state")
+
+
+def gla_block_step(q, k, v, g, out, S, z, block_grid, t_offset, update=True, rope_theta=10000.0,
+                   eps=1e-6, workspace=None, stream=None):
+    """One streaming block-causal step: the block of block_grid = (Tb, Hs, Ws)
+    latent frames at temporal position t_offset attends to itself and to
+    the cache S ([B, H, d, d] float32), z ([B, H, d] float32); with update
+    the cache then takes the block's sums in place.  out (with q and g) may
+    be None for a cache-only update."""
+    _check_tensors(*[t for t in (q, k, v, g, out, S, z, workspace) if t is not None])
+    B, H, Tb, Hs, Ws, d = _sizes(k, block_grid)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().gla_block_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(out), _ptr(S), _ptr(z),
+                               B, H, Tb, Hs, Ws, d, int(t_offset), 1 if update else 0,
+                               rope_theta, eps, _dtype_code(k), _ptr(workspace), ws_bytes,
+                               _stream_handle(stream))
+    _check(st, "gla_block_step")
 
 
 def gla_profile_enable(enable: bool = True):

@@ -102,6 +102,35 @@ def test_state_rejects_bad_arguments(lib):
                          40, 0, 1e4, 0, None) == 1
 
 
+def _step(lib, ptrs=(FAKE, FAKE * 3, FAKE * 5, FAKE * 7, FAKE * 9), S=FAKE * 11, z=FAKE * 13,
+          B=1, H=2, Tb=2, Hs=4, Ws=4, d=32, t_offset=0, update=1, ws=None, ws_bytes=0):
+    p = [ctypes.c_void_p(x) if x else None for x in ptrs]
+    c = [ctypes.c_void_p(x) if x else None for x in (S, z)]
+    w = ctypes.c_void_p(ws) if ws else None
+    return lib.gla_block_step(*p, *c, B, H, Tb, Hs, Ws, d, t_offset, update, 1e4, 1e-6,
+                              gla.GLA_BF16, w, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(S=0), "null cache"),
+    (dict(z=0), "null cache"),
+    (dict(ptrs=(FAKE, 0, FAKE * 5, FAKE * 7, FAKE * 9)), "null"),
+    (dict(ptrs=(0, FAKE * 3, FAKE * 5, FAKE * 7, FAKE * 9)), "null"),
+    (dict(ptrs=(0, FAKE * 3, FAKE * 5, 0, 0), update=0), "nothing"),
+    (dict(t_offset=-1), "t_offset"),
+    (dict(t_offset=(1 << 31) - 2), "t_offset"),
+    (dict(S=FAKE * 11 + 2), "aligned"),
+    (dict(z=FAKE * 11 + 64), "overlap"),
+    (dict(S=FAKE * 3 + 128), "overlaps k"),
+    (dict(z=FAKE * 9), "overlaps out"),
+    (dict(d=40), "d must be"),
+    (dict(ws=FAKE * 15 + 8, ws_bytes=1 << 20), "aligned"),
+])
+def test_block_step_rejects_bad_arguments(lib, kw, needle):
+    assert _step(lib, **kw) == gla.GLA_ERR_INVALID_ARG
+    assert needle in gla.gla_last_error()
+
+
 def test_workspace_query_rejects_bad_sizes(lib):
     n = ctypes.c_size_t(0)
     assert lib.gla_workspace_bytes(1, 1, 3, 2, 2, 128, 2, 0, ctypes.byref(n)) == 1
