@@ -62,6 +62,8 @@ def _load():
     lib.ora_forward.restype = ctypes.c_int
     lib.ora_block_step.argtypes = [_ptr] * 6 + [_i64] * 7 + [_dbl, _dbl, _ptr, _ptr, _ptr]
     lib.ora_block_step.restype = ctypes.c_int
+    lib.ora_gated_forward.argtypes = [_ptr] * 6 + [_i64] * 7 + [_dbl, _dbl, _dbl, _ptr]
+    lib.ora_gated_forward.restype = ctypes.c_int
     lib.ora_num_blocks.argtypes = [_i64, _i64]
     lib.ora_num_blocks.restype = _i64
     lib.ora_num_threads.argtypes = []
@@ -181,3 +183,20 @@ def block_step(q, k, v, g, S_cache, z_cache, block_grid, t_offset: int, theta: f
                                 _p(S_new), _p(z_new))
     _check(rc, "block_step")
     return out, S_new, z_new
+
+
+def gated_forward(q, k, v, g, beta, w, grid, frames_per_block: int = 0, theta: float = 10000.0,
+                  eps: float = 1e-6, rms_eps: float = 1e-6) -> np.ndarray:
+    """The gated mixer of Eq. (1) without W_o: beta [B, N, H] write gate (None:
+    1), w [d] RMSNorm weight (None: no RMSNorm).  Returns out [B, N, H, d]."""
+    q, k, v, g = _f32(q), _f32(k), _f32(v), _f32(g)
+    B, N, H, d = q.shape
+    T, Hs, Ws = grid
+    bt = None if beta is None else _f32(beta).reshape(B, N, H)
+    ww = None if w is None else _f32(w).reshape(d)
+    out = np.empty((B, N, H, d), dtype=np.float64)
+    rc = _load().ora_gated_forward(_p(q), _p(k), _p(v), _p(g), _p(bt), _p(ww), B, H, T, Hs, Ws, d,
+                                   frames_per_block, float(theta), float(eps), float(rms_eps),
+                                   _p(out))
+    _check(rc, "gated_forward")
+    return out

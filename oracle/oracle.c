@@ -109,9 +109,11 @@ int64_t ora_num_blocks(int64_t T, int64_t F) { return (F <= 0) ? 1 : T / F; }
  * k, v : [B, N, H, d] float, N = T*Hs*Ws
  * S    : [B, H, nb, d, d] double (output)   z : [B, H, nb, d] double (output)
  */
-int ora_state(const float *k, const float *v, int64_t B, int64_t H, int64_t T, int64_t Hs,
-              int64_t Ws, int64_t d, int64_t F, double theta, const int64_t *pos0, double *S,
-              double *z) {
+/* beta (optional, [B, N, H]): the write gate of [V2] Eq. (1), a factor on
+ * each token's rotated key in the state only (z keeps the plain phi(k)). */
+static int state_impl(const float *k, const float *v, const float *beta, int64_t B, int64_t H,
+                      int64_t T, int64_t Hs, int64_t Ws, int64_t d, int64_t F, double theta,
+                      const int64_t *pos0, double *S, double *z) {
   if (!k || !v || !S || !z) return ORA_BAD_ARG;
   int rc = check_shape(B, H, T, Hs, Ws, d, F);
   if (rc) return rc;
@@ -143,6 +145,10 @@ int ora_state(const float *k, const float *v, int64_t B, int64_t H, int64_t T, i
             vrow[p] = (double)vn[p];
           }
           ora_rope(phik, rotk, d, pos, theta); /* RoPE after ReLU, numerator only */
+          if (beta) { /* write gate: scales what this token writes into S */
+            const double bt = (double)beta[(b * N + n) * H + h];
+            for (int64_t p = 0; p < d; ++p) rotk[p] *= bt;
+          }
           for (int64_t p = 0; p < d; ++p) {
             zacc[p] += phik[p]; /* normaliser: un-rotated phi(k) */
             for (int64_t e = 0; e < d; ++e) Sacc[p * d + e] += rotk[p] * vrow[e];
@@ -166,6 +172,12 @@ int ora_state(const float *k, const float *v, int64_t B, int64_t H, int64_t T, i
   return failed ? ORA_NO_MEM : ORA_OK;
 }
 
+int ora_state(const float *k, const float *v, int64_t B, int64_t H, int64_t T, int64_t Hs,
+              int64_t Ws, int64_t d, int64_t F, double theta, const int64_t *pos0, double *S,
+              double *z) {
+  return state_impl(k, v, NULL, B, H, T, Hs, Ws, d, F, theta, pos0, S, z);
+}
+
 /*
  * Output for a list of tokens ([V1] Section 3.2 steps 3-5 with the gate of
  * [V2] Eq. 1):
@@ -179,10 +191,12 @@ int ora_state(const float *k, const float *v, int64_t B, int64_t H, int64_t T, i
  * tokens : ntok token indices in [0, N), or NULL for all N tokens in order
  * out    : [B, ntok, H, d] double
  */
-int ora_apply(const float *q, const float *g, const double *S, const double *z, int64_t B,
-              int64_t H, int64_t T, int64_t Hs, int64_t Ws, int64_t d, int64_t F, double theta,
-              double eps, const int64_t *pos0, const int64_t *tokens, int64_t ntok,
-              double *out) {
+/* w (optional, [d]): RMSNorm of [V2] Eq. (1) on num/den over the d features,
+ * y / sqrt(mean_e y[e]^2 + rms_eps) * w, before the sigmoid gate. */
+static int apply_impl(const float *q, const float *g, const double *S, const double *z,
+                      const float *w, double rms_eps, int64_t B, int64_t H, int64_t T, int64_t Hs,
+                      int64_t Ws, int64_t d, int64_t F, double theta, double eps,
+                      const int64_t *pos0, const int64_t *tokens, int64_t ntok, double *out) {
   if (!q || !g || !S || !z || !out) return ORA_BAD_ARG;
   int rc = check_shape(B, H, T, Hs, Ws, d, F);
   if (rc) return rc;
@@ -225,8 +239,17 @@ int ora_apply(const float *q, const float *g, const double *S, const double *z, 
           for (int64_t e = 0; e < d; ++e) {
             double num = 0.0;
             for (int64_t p = 0; p < d; ++p) num += rotq[p] * Sh[p * d + e];
+            on[e] = num / den;
+          }
+          if (w) { /* RMSNorm over the d features of y = num / den */
+            double ss = 0.0;
+            for (int64_t e = 0; e < d; ++e) ss += on[e] * on[e];
+            const double inv_rms = 1.0 / sqrt(ss / (double)d + rms_eps);
+            for (int64_t e = 0; e < d; ++e) on[e] = on[e] * inv_rms * (double)w[e];
+          }
+          for (int64_t e = 0; e < d; ++e) {
             double gate = 1.0 / (1.0 + exp(-(double)gn[e]));
-            on[e] = num / den * gate;
+            on[e] *= gate;
           }
         }
       }
@@ -235,6 +258,45 @@ int ora_apply(const float *q, const float *g, const double *S, const double *z, 
     }
   }
   return failed ? ORA_NO_MEM : ORA_OK;
+}
+
+int ora_apply(const float *q, const float *g, const double *S, const double *z, int64_t B,
+              int64_t H, int64_t T, int64_t Hs, int64_t Ws, int64_t d, int64_t F, double theta,
+              double eps, const int64_t *pos0, const int64_t *tokens, int64_t ntok,
+              double *out) {
+  return apply_impl(q, g, S, z, NULL, 0.0, B, H, T, Hs, Ws, d, F, theta, eps, pos0, tokens, ntok,
+                    out);
+}
+
+/* The full gated mixer of [V2] Eq. (1), short of the output projection W_o:
+ *   S   = sum_n beta_n RoPE_n(phi(k_n))^T v_n,   z = sum_n phi(k_n)
+ *   y_i = (RoPE_i(phi(q_i)) S) / (phi(q_i) . z + eps)
+ *   o_i = y_i / sqrt(mean_e y_i[e]^2 + rms_eps) * w  *  sigmoid(g_i)
+ * beta: [B, N, H] (NULL: every beta_n = 1); w: [d] (NULL: no RMSNorm,
+ * o_i = y_i * sigmoid(g_i)).  Block-causal like ora_forward.
+ * out: [B, N, H, d] double. */
+int ora_gated_forward(const float *q, const float *k, const float *v, const float *g,
+                      const float *beta, const float *w, int64_t B, int64_t H, int64_t T,
+                      int64_t Hs, int64_t Ws, int64_t d, int64_t F, double theta, double eps,
+                      double rms_eps, double *out) {
+  int rc = check_shape(B, H, T, Hs, Ws, d, F);
+  if (rc) return rc;
+  if (!q || !g || !out) return ORA_BAD_ARG;
+  const int64_t nb = ora_num_blocks(T, F);
+  double *S = (double *)malloc((size_t)(B * H * nb * d * d) * sizeof(double));
+  double *z = (double *)malloc((size_t)(B * H * nb * d) * sizeof(double));
+  if (!S || !z) {
+    free(S);
+    free(z);
+    return ORA_NO_MEM;
+  }
+  rc = state_impl(k, v, beta, B, H, T, Hs, Ws, d, F, theta, NULL, S, z);
+  if (rc == ORA_OK)
+    rc = apply_impl(q, g, S, z, w, rms_eps, B, H, T, Hs, Ws, d, F, theta, eps, NULL, NULL, 0,
+                    out);
+  free(S);
+  free(z);
+  return rc;
 }
 
 /* Whole operator: ora_state followed by ora_apply over every token.

@@ -46,6 +46,12 @@ MUTATIONS = [
      "for (int64_t i = 0; i < B * H * d * d; ++i) S[i] += 0.0 * S_cache[i];"),
     ("block_step_normaliser_cache_ignored", "for (int64_t i = 0; i < B * H * d; ++i) z[i] += z_cache[i];",
      "for (int64_t i = 0; i < B * H * d; ++i) z[i] += 0.0 * z_cache[i];"),
+    ("write_gate_on_normaliser", "for (int64_t p = 0; p < d; ++p) rotk[p] *= bt;",
+     "for (int64_t p = 0; p < d; ++p) { rotk[p] *= bt; phik[p] *= bt; }"),
+    ("rmsnorm_mean_over_d_minus_1", "const double inv_rms = 1.0 / sqrt(ss / (double)d + rms_eps);",
+     "const double inv_rms = 1.0 / sqrt(ss / (double)(d - 1) + rms_eps);"),
+    ("rmsnorm_weight_index", "on[e] = on[e] * inv_rms * (double)w[e];",
+     "on[e] = on[e] * inv_rms * (double)w[(e + 1) % d];"),
     ("block_step_offset_ignored", "const int64_t pos0[3] = {t_offset, 0, 0};",
      "const int64_t pos0[3] = {0, 0, 0};"),
 ]

@@ -505,3 +505,105 @@ def test_block_step_cache_update_is_the_block_state():
     assert none is None
     np.testing.assert_array_equal(S2, S_new)
     np.testing.assert_array_equal(z2, z_new)
+
+
+# ---------------------------------------------------------------------------
+# the full gated mixer of [V2] Eq. (1) short of W_o: write gate beta on the
+# state only, RMSNorm of num/den over the d features before the gate
+# ---------------------------------------------------------------------------
+def brute_force_gated(q, k, v, g, beta, w, grid, F=0, theta=10000.0, eps=1e-6, rms_eps=1e-6):
+    """O(N^2): y_i = sum_j beta_j (RoPE(phi(q_i)).RoPE(phi(k_j))) v_j /
+    (sum_j phi(q_i).phi(k_j) + eps); o_i = y_i / rms(y_i) * w * sigmoid(g_i)."""
+    B, N, H, d = q.shape
+    T, Hs, Ws = grid
+    pos = _positions(T, Hs, Ws)
+    blk = pos[:, 0] // F if F > 0 else np.zeros(N, dtype=np.int64)
+    allowed = blk[None, :] <= blk[:, None]
+    out = np.empty((B, N, H, d))
+    for b in range(B):
+        for h in range(H):
+            pq = np.maximum(q[b, :, h].astype(np.float64), 0.0)
+            pk = np.maximum(k[b, :, h].astype(np.float64), 0.0)
+            rq, rk = _rope_complex(pq, pos, theta), _rope_complex(pk, pos, theta)
+            bt = np.ones(N) if beta is None else beta[b, :, h].astype(np.float64)
+            A = (rq @ rk.T) * allowed * bt[None, :]
+            D = (pq @ pk.T) * allowed
+            y = (A @ v[b, :, h].astype(np.float64)) / (D.sum(1) + eps)[:, None]
+            if w is not None:
+                y = y / np.sqrt((y * y).mean(1, keepdims=True) + rms_eps) * w.astype(np.float64)
+            out[b, :, h] = y / (1.0 + np.exp(-g[b, :, h].astype(np.float64)))
+    return out
+
+
+def _gated_inputs(B, T, Hs, Ws, H, d, seed):
+    x = host_inputs(B, T, Hs, Ws, H, d, "f32", seed=seed)
+    rng = np.random.default_rng(seed + 1000)
+    beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((B, T * Hs * Ws, H))))).astype(np.float32)
+    w = (1.0 + 0.5 * rng.standard_normal(d)).astype(np.float32)
+    return x, beta, w
+
+
+def test_gated_without_gate_and_norm_is_the_plain_operator():
+    x = host_inputs(1, 3, 3, 4, 2, 32, "f32", seed=41)
+    for F in (0, 1):
+        a = oracle.gated_forward(x["q"], x["k"], x["v"], x["g"], None, None, (3, 3, 4), F)
+        b = oracle.forward(x["q"], x["k"], x["v"], x["g"], (3, 3, 4), F)
+        np.testing.assert_allclose(a, b, rtol=1e-14, atol=1e-300)
+
+
+@pytest.mark.parametrize("B,T,Hs,Ws,H,d,theta,F,use_beta,use_w", [
+    (1, 2, 3, 3, 2, 32, 10000.0, 0, True, True),
+    (2, 3, 2, 2, 1, 16, 50.0, 0, True, False),
+    (1, 3, 2, 3, 2, 64, 7.0, 0, False, True),
+    (1, 4, 2, 2, 2, 32, 10000.0, 2, True, True),
+])
+def test_gated_matches_brute_force(B, T, Hs, Ws, H, d, theta, F, use_beta, use_w):
+    x, beta, w = _gated_inputs(B, T, Hs, Ws, H, d, seed=42)
+    beta = beta if use_beta else None
+    w = w if use_w else None
+    got = oracle.gated_forward(x["q"], x["k"], x["v"], x["g"], beta, w, (T, Hs, Ws), F, theta)
+    ref = brute_force_gated(x["q"], x["k"], x["v"], x["g"], beta, w, (T, Hs, Ws), F, theta)
+    assert _rel_err(got, ref, floor=1e-9) < 1e-10
+
+
+def test_zero_write_gate_equals_zero_value():
+    # beta_j = 0 removes token j from the state only: the same as v_j = 0
+    x, beta, w = _gated_inputs(1, 2, 3, 4, 2, 32, seed=43)
+    drop = np.zeros(x["k"].shape[1], dtype=bool)
+    drop[[1, 5, 17]] = True
+    b0 = beta.copy()
+    b0[:, drop] = 0.0
+    v0 = x["v"].copy()
+    v0[:, drop] = 0.0
+    b1 = beta.copy()
+    a = oracle.gated_forward(x["q"], x["k"], x["v"], x["g"], b0, w, (2, 3, 4))
+    b = oracle.gated_forward(x["q"], x["k"], v0, x["g"], b1, w, (2, 3, 4))
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-15)
+
+
+def test_rmsnorm_removes_a_common_write_scale():
+    x, beta, w = _gated_inputs(1, 2, 2, 3, 2, 16, seed=44)
+    ref = oracle.gated_forward(x["q"], x["k"], x["v"], x["g"], beta, w, (2, 2, 3), rms_eps=0.0)
+    s = oracle.gated_forward(x["q"], x["k"], x["v"], x["g"], beta * 4.0, w, (2, 2, 3), rms_eps=0.0)
+    np.testing.assert_allclose(s, ref, rtol=1e-12)
+    # without the norm the output is linear in a common write scale
+    a = oracle.gated_forward(x["q"], x["k"], x["v"], x["g"], beta, None, (2, 2, 3))
+    b = oracle.gated_forward(x["q"], x["k"], x["v"], x["g"], beta * 4.0, None, (2, 2, 3))
+    np.testing.assert_allclose(b, 4.0 * a, rtol=1e-12)
+
+
+def test_gated_single_token_closed_form():
+    # N = 1: y = beta v s / (s + eps), s = phi(q).phi(k); with rms_eps = 0 the
+    # norm leaves v / rms(v) * w, whatever beta > 0
+    d = 32
+    rng = np.random.default_rng(45)
+    q = rng.standard_normal((1, 1, 1, d)).astype(np.float32)
+    k = np.abs(rng.standard_normal((1, 1, 1, d))).astype(np.float32)
+    v = rng.standard_normal((1, 1, 1, d)).astype(np.float32)
+    g = rng.standard_normal((1, 1, 1, d)).astype(np.float32)
+    w = (1.0 + rng.standard_normal(d)).astype(np.float32)
+    beta = np.full((1, 1, 1), 0.3, dtype=np.float32)
+    out = oracle.gated_forward(q, k, v, g, beta, w, (1, 1, 1), rms_eps=0.0)[0, 0, 0]
+    vv = v[0, 0, 0].astype(np.float64)
+    exp = vv / math.sqrt(float(np.mean(vv * vv))) * w / (1.0 + np.exp(-g[0, 0, 0].astype(np.float64)))
+    np.testing.assert_allclose(out, exp, rtol=1e-12, atol=1e-15)
