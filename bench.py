@@ -138,6 +138,44 @@ def block_step_leg(steps: int, warmup: int, workload: str = "720p_block_causal")
     }
 
 
+def gated_leg(w, x, ws, steps: int, warmup: int):
+    """The gated mixer (gla_gated_forward) on the same workload: the write gate
+    beta [B, N, H] and the RMSNorm weight [d], both bf16, on top of the
+    operator.  Algorithmic bytes add beta (2 bytes per token-head)."""
+    import torch
+
+    from relu_linear_attention_amd import gla
+
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed + 100)
+    beta = torch.sigmoid(torch.randn((w.B, w.N, w.H), device="cuda", generator=gen)).to(
+        torch.bfloat16)
+    rms_w = (1.0 + 0.5 * torch.randn((w.d,), device="cuda", generator=gen)).to(torch.bfloat16)
+    out = torch.empty_like(x["q"])
+    stream = torch.cuda.current_stream()
+
+    def call():
+        gla.gla_gated_forward(x["q"], x["k"], x["v"], x["g"], beta, rms_w, out, w.grid,
+                              w.frames_per_block, w.theta, w.eps, 1e-6, workspace=ws,
+                              stream=stream)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        call()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    nbytes = 5 * w.B * w.N * w.H * w.d * w.elem_bytes + w.B * w.N * w.H * 2
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": w.name, "beta": "[B, N, H] bf16", "rms_weight": "[d] bf16",
+            "ms_per_call": ms, "tokens_per_s": w.B * w.N / (ms * 1e-3),
+            "algorithmic_bytes_per_call": nbytes, "GBps": gbps, "frac_of_peak": gbps / PEAK_HBM_GBPS}
+
+
 def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
     """A plain device-to-device copy of known size, for scaling the HBM
     counters (FETCH_SIZE, WRITE_SIZE) of the kernels."""
@@ -166,6 +204,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-block-step", action="store_true",
                     help="skip the streaming block-step measurement")
+    ap.add_argument("--no-gated", action="store_true",
+                    help="skip the gated-mixer (write gate + RMSNorm) measurement")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
@@ -266,6 +306,8 @@ def main() -> int:
         },
         "cpu_baseline": None,
     }
+    if not args.no_gated and mfma:
+        result["gated"] = gated_leg(w, x, ws, max(3, args.steps // 2), 2)
     if not args.no_block_step:
         result["block_step"] = block_step_leg(max(3, args.steps // 4), 2)
     if not args.no_cpu_baseline:

@@ -129,6 +129,28 @@ gla_status gla_state(const void *k, const void *v, float *S_out, float *z_out, i
                      hipStream_t stream);
 
 /*
+ * The gated mixer of "SANA-Video 2.0" Section 2, Eq. (1), short of the
+ * output projection W_o: the operator above plus
+ *   - the write gate beta ([B, N, H], the tensors' element type; NULL: 1):
+ *       S = sum_n beta_n RoPE_n(phi(k_n))^T v_n   (z keeps the plain phi(k));
+ *   - the RMSNorm of y_i = num_i / den_i over its d features, before the
+ *     output gate (rms_weight [d], the tensors' type; NULL: no RMSNorm):
+ *       o_i = y_i / sqrt(mean_e y_i[e]^2 + rms_eps) * rms_weight * sigmoid(g_i).
+ * beta is used as given (any activation that produces it happens upstream);
+ * the RMSNorm weight is shared by the heads.  rms_eps must be finite and
+ * > 0 when rms_weight is given.  frames_per_block as gla_forward_ws (0:
+ * non-causal).  workspace: NULL (stream-ordered allocation, like
+ * gla_forward) or at least gla_workspace_bytes() bytes, 256-byte aligned.
+ * With beta and rms_weight both NULL this is gla_forward_ws.
+ */
+gla_status gla_gated_forward(const void *q, const void *k, const void *v, const void *g,
+                             const void *beta, const void *rms_weight, void *out, int64_t B,
+                             int64_t H, int64_t T, int64_t Hs, int64_t Ws, int64_t d,
+                             int64_t frames_per_block, float rope_theta, float eps, float rms_eps,
+                             gla_dtype dtype, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/*
  * One step of the streaming block-causal mode ("SANA-Video" Section 3.4
  * and its Algorithm 1, the constant-memory cache): one temporal block of
  * Tb latent frames (q, k, v, g, out are [B, Tb*Hs*Ws, H, d]) whose first

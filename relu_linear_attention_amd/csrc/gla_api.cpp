@@ -137,6 +137,13 @@ gla_status check_step(const void *q, const void *k, const void *v, const void *g
   return GLA_OK;
 }
 
+// gla_gated_forward: beta [B, N, H] and rms_w [d] of the tensors' type, each
+// optional, aligned to their element size, not overlapping out;
+// rms_eps finite and > 0 when the RMSNorm is on.
+struct Gates;
+gla_status check_gates(const Gates &gt, const void *out, size_t bytes, int64_t BNH, int64_t d,
+                       gla_dtype dtype, float rms_eps);
+
 // ---------------------------------------------------------------- planning
 // Number of pieces to cut each of `units` token runs of `len` tokens into
 // (pieces of a multiple of `tile` tokens, at least `min_len` long), such that
@@ -250,7 +257,8 @@ gla_status make_plan(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, in
     // LDS of the two matrix-core kernels must fit the 160 KiB of a CU
     auto slice = [&](int64_t len) { return spatial_entries + (ceil_div(len, hw) + 1) * pt; };
     const int64_t lds_state = 3 * d * 128 + slice(P.Lc) * 8;
-    const int64_t lds_apply = d * d * 4 + (d / 32) * 64 * 16 + 8 * 16 * (2 * d + 16) + slice(P.Lr) * 8;
+    const int64_t lds_apply =
+        d * d * 4 + (d / 32) * 64 * 16 + d * 4 + 8 * 16 * (2 * d + 16) + slice(P.Lr) * 8;
     if (std::max(lds_state, lds_apply) > 160 * 1024) return fail(GLA_ERR_UNSUPPORTED,
         "internal: LDS plan of %lld bytes exceeds the CU", (long long)std::max(lds_state, lds_apply));
   }
@@ -334,12 +342,36 @@ struct Cache {
   float *S_out = nullptr, *z_out = nullptr;
 };
 
+// The gates of the full mixer (gla_gated_forward): the write gate beta
+// [B, N, H] and the RMSNorm weight rms_w [d] (either may be null).
+struct Gates {
+  const void *beta = nullptr, *rms_w = nullptr;
+};
+
+gla_status check_gates(const Gates &gt, const void *out, size_t bytes, int64_t BNH, int64_t d,
+                       gla_dtype dtype, float rms_eps) {
+  const size_t es = dtype == GLA_BF16 ? 2 : 4;
+  if (gt.beta != nullptr) {
+    if ((uintptr_t)gt.beta % es) return fail(GLA_ERR_INVALID_ARG, "beta is misaligned");
+    if (ranges_overlap(out, bytes, gt.beta, (size_t)BNH * es))
+      return fail(GLA_ERR_INVALID_ARG, "out overlaps beta");
+  }
+  if (gt.rms_w != nullptr) {
+    if ((uintptr_t)gt.rms_w % es) return fail(GLA_ERR_INVALID_ARG, "rms_weight is misaligned");
+    if (ranges_overlap(out, bytes, gt.rms_w, (size_t)d * es))
+      return fail(GLA_ERR_INVALID_ARG, "out overlaps rms_weight");
+    if (!std::isfinite(rms_eps) || !(rms_eps > 0.f))
+      return fail(GLA_ERR_INVALID_ARG, "rms_eps must be finite and > 0");
+  }
+  return GLA_OK;
+}
+
 // Enqueues every stage of the operator on `stream`, with workspace `ws`.
 // With `apply == false` only the state is computed (gla_state, cache-only
 // block steps).
 gla_status run_plan(const Plan &P, const void *q, const void *k, const void *v, const void *g,
                     void *out, void *ws, hipStream_t stream, bool apply,
-                    const Cache &cache = Cache()) {
+                    const Cache &cache = Cache(), const Gates &gates = Gates()) {
   char *base = (char *)ws;
   float2 *tab = (float2 *)(base + P.off_tab);
   float *part = (float *)(base + P.off_part);
@@ -350,8 +382,8 @@ gla_status run_plan(const Plan &P, const void *q, const void *k, const void *v, 
                                [&] { return gla::launch_rope_table(P, tab, stream); });
   if (st != GLA_OK) return st;
   st = timed_launch(1, stream, "state kernel", [&] {
-    return P.mfma ? gla::launch_state_mfma(P, k, v, tab, part, stream)
-                  : gla::launch_state_generic(P, k, v, tab, part, stream);
+    return P.mfma ? gla::launch_state_mfma(P, k, v, gates.beta, tab, part, stream)
+                  : gla::launch_state_generic(P, k, v, gates.beta, tab, part, stream);
   });
   if (st != GLA_OK) return st;
   st = timed_launch(2, stream, "reduce kernel", [&] {
@@ -361,8 +393,8 @@ gla_status run_plan(const Plan &P, const void *q, const void *k, const void *v, 
   if (st != GLA_OK) return st;
   if (!apply) return GLA_OK;
   return timed_launch(3, stream, "apply kernel", [&] {
-    return P.mfma ? gla::launch_apply_mfma(P, q, g, states, frags, tab, out, stream)
-                  : gla::launch_apply_generic(P, q, g, states, tab, out, stream);
+    return P.mfma ? gla::launch_apply_mfma(P, q, g, states, frags, tab, gates.rms_w, out, stream)
+                  : gla::launch_apply_generic(P, q, g, states, tab, gates.rms_w, out, stream);
   });
 }
 
@@ -370,7 +402,8 @@ gla_status forward_impl(const void *q, const void *k, const void *v, const void 
                         int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, int64_t d,
                         int64_t F, float theta, float eps, gla_dtype dtype, void *ws,
                         size_t ws_bytes, bool own_ws, hipStream_t stream,
-                        const Step *step = nullptr) {
+                        const Step *step = nullptr, const Gates *gates = nullptr,
+                        float rms_eps = 0.f) {
   g_last_error[0] = '\0';
   gla_status st = check_sizes(B, H, T, Hs, Ws, d, F, dtype);
   if (st != GLA_OK) return st;
@@ -386,6 +419,10 @@ gla_status forward_impl(const void *q, const void *k, const void *v, const void 
     st = check_pointers(q, k, v, g, out, bytes);
     if (st != GLA_OK) return st;
   }
+  if (gates != nullptr) {
+    st = check_gates(*gates, out, bytes, B * T * Hs * Ws * H, d, dtype, rms_eps);
+    if (st != GLA_OK) return st;
+  }
   if (!own_ws && (ws == nullptr || ((uintptr_t)ws & 255) != 0))
     return fail(GLA_ERR_INVALID_ARG, "workspace must be a non-null, 256-byte aligned pointer");
   int cus = 0;
@@ -396,6 +433,9 @@ gla_status forward_impl(const void *q, const void *k, const void *v, const void 
   Plan P;
   st = make_plan(B, H, T, Hs, Ws, d, F, dtype, theta, eps, cus, aligned16, &P);
   if (st != GLA_OK) return st;
+  P.rms_eps = rms_eps;
+  const Gates no_gates;
+  const Gates &gt = gates != nullptr ? *gates : no_gates;
   Cache cache;
   if (step != nullptr) {
     P.t0 = step->t0;
@@ -410,7 +450,7 @@ gla_status forward_impl(const void *q, const void *k, const void *v, const void 
     if (ws_bytes < P.total_bytes)
       return fail(GLA_ERR_INVALID_ARG, "workspace too small: %zu bytes given, %zu needed", ws_bytes,
                   P.total_bytes);
-    return run_plan(P, q, k, v, g, out, ws, stream, apply, cache);
+    return run_plan(P, q, k, v, g, out, ws, stream, apply, cache, gt);
   }
   void *mem = nullptr;
   hipError_t e = hipMallocAsync(&mem, P.total_bytes, stream);
@@ -419,7 +459,7 @@ gla_status forward_impl(const void *q, const void *k, const void *v, const void 
     return fail(GLA_ERR_ALLOC, "hipMallocAsync of %zu workspace bytes failed: %s", P.total_bytes,
                 hipGetErrorString(e));
   }
-  st = run_plan(P, q, k, v, g, out, mem, stream, apply, cache);
+  st = run_plan(P, q, k, v, g, out, mem, stream, apply, cache, gt);
   e = hipFreeAsync(mem, stream);
   if (st == GLA_OK && e != hipSuccess) return hip_fail(e, "hipFreeAsync");
   return st;
@@ -534,6 +574,20 @@ gla_status gla_block_step(const void *q, const void *k, const void *v, const voi
   s.update = update != 0;
   return forward_impl(q, k, v, g, out, B, H, Tb, Hs, Ws, d, 0, rope_theta, eps, dtype, workspace,
                       workspace_bytes, workspace == nullptr, stream, &s);
+}
+
+gla_status gla_gated_forward(const void *q, const void *k, const void *v, const void *g,
+                             const void *beta, const void *rms_weight, void *out, int64_t B,
+                             int64_t H, int64_t T, int64_t Hs, int64_t Ws, int64_t d,
+                             int64_t frames_per_block, float rope_theta, float eps, float rms_eps,
+                             gla_dtype dtype, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  Gates gt;
+  gt.beta = beta;
+  gt.rms_w = rms_weight;
+  return forward_impl(q, k, v, g, out, B, H, T, Hs, Ws, d, frames_per_block, rope_theta, eps,
+                      dtype, workspace, workspace_bytes, workspace == nullptr, stream, nullptr, &gt,
+                      rms_eps);
 }
 
 const char *gla_status_string(gla_status status) {

@@ -30,6 +30,7 @@ struct Plan {
   bool bf16;      // element type of q, k, v, g, out
   bool mfma;      // matrix-core kernels (bf16, d = 64 or 128)
   float theta, eps;
+  float rms_eps;  // RMSNorm epsilon (gated mixer only)
   int64_t tab_entries;  // RoPE table entries (cos, sin pairs)
   int64_t tab_t_off, tab_h_off, tab_w_off;  // entry offsets of the axis tables
   // workspace layout, byte offsets
@@ -53,9 +54,11 @@ constexpr int64_t kApplyTabEntries = 5120;  // 40 KiB
 // stored as float2.
 hipError_t launch_rope_table(const Plan &p, float2 *tab, hipStream_t stream);
 
-// State partials, vector kernels (any supported d, bf16 or f32).
-hipError_t launch_state_generic(const Plan &p, const void *k, const void *v, const float2 *tab,
-                                float *partials, hipStream_t stream);
+// State partials, vector kernels (any supported d, bf16 or f32).  beta
+// (optional, [B, N, H] of the tensors' type): the write gate, a factor on
+// each token's rotated key in S only.
+hipError_t launch_state_generic(const Plan &p, const void *k, const void *v, const void *beta,
+                                const float2 *tab, float *partials, hipStream_t stream);
 // Fixed-order reduce of the partials plus the inclusive block prefix.
 // Writes fp32 states [units][d*d + d] and, for the matrix-core path, S as
 // row-major bf16 hi and lo parts [units][2][d][d].  S_in/z_in (optional,
@@ -64,16 +67,18 @@ hipError_t launch_state_generic(const Plan &p, const void *k, const void *v, con
 hipError_t launch_reduce(const Plan &p, const float *partials, float *states,
                          uint16_t *frags, const float *S_in, const float *z_in, float *S_out,
                          float *z_out, hipStream_t stream);
-// Output stage, vector kernels.
+// Output stage, vector kernels.  rms_w (optional, [d] of the tensors' type):
+// RMSNorm of num/den with that weight (epsilon p.rms_eps) before the gate.
 hipError_t launch_apply_generic(const Plan &p, const void *q, const void *g, const float *states,
-                                const float2 *tab, void *out, hipStream_t stream);
+                                const float2 *tab, const void *rms_w, void *out,
+                                hipStream_t stream);
 
 // Matrix-core kernels (bf16, d = 64 or 128).
-hipError_t launch_state_mfma(const Plan &p, const void *k, const void *v, const float2 *tab,
-                             float *partials, hipStream_t stream);
+hipError_t launch_state_mfma(const Plan &p, const void *k, const void *v, const void *beta,
+                             const float2 *tab, float *partials, hipStream_t stream);
 hipError_t launch_apply_mfma(const Plan &p, const void *q, const void *g, const float *states,
-                             const uint16_t *frags, const float2 *tab, void *out,
-                             hipStream_t stream);
+                             const uint16_t *frags, const float2 *tab, const void *rms_w,
+                             void *out, hipStream_t stream);
 
 // Division by a fixed divisor d >= 1 for dividends 0 <= n < 2^31, by a
 // multiply-high and a shift: with s = ceil(log2 d) and

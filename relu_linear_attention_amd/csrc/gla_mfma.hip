@@ -39,6 +39,7 @@ struct MArgs {
   int64_t tab_h_off;  // global entry offset of the h rows (the w rows follow)
   FastDiv div_hw, div_w;  // by Hs*Ws and by Ws (token indices < 2^31)
   float eps;
+  float rms_eps;  // epsilon of the optional RMSNorm of num/den
 };
 
 // Buffer resource over the rows of one head for a token range: byte 0 is
@@ -263,9 +264,13 @@ struct StateCfg {
 // feature per lane and read) and accumulates its share of the 32x32 tiles of
 // S = hi^T v + lo^T v on the matrix cores.  The rows of the next step are in
 // flight in registers meanwhile.
-template <int D>
+//
+// kBeta: the write gate ("SANA-Video 2.0" Eq. (1)): beta [B, N, H] scales each
+// token's rotated key before it enters S (z keeps the plain phi(k)).
+template <int D, bool kBeta>
 __global__ __launch_bounds__(kStateThreads<D>, kStateThreads<D> / 128) void state_mfma_kernel(const uint16_t *__restrict__ k,
                                                             const uint16_t *__restrict__ v,
+                                                            const uint16_t *__restrict__ beta,
                                                             const float2 *__restrict__ tab,
                                                             float *__restrict__ partials,
                                                             MArgs a) {
@@ -330,13 +335,21 @@ __global__ __launch_bounds__(kStateThreads<D>, kStateThreads<D> / 128) void stat
   const __amdgpu_buffer_rsrc_t rk = head_rows_rsrc(k + first, range_bytes);
   const __amdgpu_buffer_rsrc_t rv = head_rows_rsrc(v + first, range_bytes);
   const uint32_t my_off = (uint32_t)tg * row_bytes + 16 * fc;
+  // the write gates of this chunk's tokens (a 2-byte column of [B, N, H])
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(kBeta ? beta + (b * a.N + n_begin) * a.H + hd : k), 0,
+      kBeta ? (int)((n_end - n_begin - 1) * a.H * 2 + 2) : 0, 0x00020000);
   uint4 kr[R], vr[R];
+  uint32_t br[R];
   auto load_rows = [&](int64_t n0) {
     const uint32_t base = (uint32_t)(n0 - n_begin) * row_bytes + my_off;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       kr[r] = buf_load16<kStateLoadPolicy>(rk, base + (uint32_t)(TPP * r) * row_bytes);
       vr[r] = buf_load16<kStateLoadPolicy>(rv, base + (uint32_t)(TPP * r) * row_bytes);
+      if (kBeta)
+        br[r] = __builtin_amdgcn_raw_buffer_load_b16(
+            rb, (int)(((uint32_t)(n0 - n_begin) + tg + TPP * r) * (uint32_t)a.H * 2), 0, 0);
     }
   };
 
@@ -374,6 +387,11 @@ __global__ __launch_bounds__(kStateThreads<D>, kStateThreads<D> / 128) void stat
       float2 c4[4];
       ts.read(s_tab, tl.at(t, h, w), c4);
       rotate4(x, c4);
+      if (kBeta) {
+        const float bt = bf16_bits_to_float(br[r]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] *= bt;
+      }
       uint4 hi, lo;
       split_bf16x2(x[0], x[1], hi.x, lo.x);
       split_bf16x2(x[2], x[3], hi.y, lo.y);
@@ -486,11 +504,17 @@ struct Stage {
   static constexpr int kPasses = 16 / kRowsPerPass;
 };
 
-template <int D>
+//
+// kNorm: the RMSNorm of "SANA-Video 2.0" Eq. (1) between num/den and the
+// gate: y = num/den is scaled by 1/sqrt(mean over the D features of y^2 +
+// rms_eps) and by the weight w [D].  A token's D values are spread over the
+// four lanes l % 16 == token (32 each), summed with two lane exchanges.
+template <int D, bool kNorm>
 __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ g,
     const float *__restrict__ states, const uint16_t *__restrict__ frags,
-    const float2 *__restrict__ tab, uint16_t *__restrict__ out, MArgs a) {
+    const float2 *__restrict__ tab, const uint16_t *__restrict__ rms_w,
+    uint16_t *__restrict__ out, MArgs a) {
   constexpr int KS = D / 32;  // 32-feature contraction steps
   constexpr int ET = D / 16;  // 16-feature output tiles
   constexpr int NW = kApplyThreads / 64;
@@ -498,8 +522,9 @@ __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
   unsigned char *s_sh = lds;             // S hi part, row-major [p][e], units permuted
   unsigned char *s_sl = lds + D * D * 2;  // S lo part
   bf16x8 *s_zf = reinterpret_cast<bf16x8 *>(lds + D * D * 4);  // KS fragments x 64 lanes
+  float *s_w = reinterpret_cast<float *>(s_zf + KS * 64);        // RMSNorm weight (D)
   using St = Stage<D>;
-  unsigned char *s_stage = reinterpret_cast<unsigned char *>(s_zf + KS * 64);  // NW tiles
+  unsigned char *s_stage = reinterpret_cast<unsigned char *>(s_w + D);  // NW tiles
   float2 *s_tab = reinterpret_cast<float2 *>(s_stage + NW * St::kBytes);
 
   const int64_t wg = blockIdx.x;
@@ -536,6 +561,8 @@ __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
       s_zf[i] = f;
     }
   }
+  if (kNorm)
+    for (int i = tid; i < D; i += kApplyThreads) s_w[i] = bf16_bits_to_float(rms_w[i]);
   const TabSlice<D> ts = load_tab_slice<D>(s_tab, tab, a, n_begin, n_end);
   __syncthreads();
 
@@ -646,17 +673,49 @@ __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      float scale = 0.f;  // (kNorm) 1 / (den * rms(num / den))
+      if (kNorm) {
+        // sum of num^2 over the token's D features: 32 in this lane, the rest
+        // in lanes l ^ 16, l ^ 32 and l ^ 48, added by two in-register lane
+        // swaps (gfx950 permlane16/32 swap: each returns the pair of values
+        // exchanged between rows, whose sum is this lane's plus its partner's)
+        float ss = 0.f;
+#pragma unroll
+        for (int et = 0; et < ET; ++et)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ss = __builtin_fmaf(acc[et][i], acc[et][i], ss);
+        const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(ss), __float_as_uint(ss),
+                                                          false, false);
+        ss = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+        const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss), __float_as_uint(ss),
+                                                          false, false);
+        ss = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+        // rms(num / den) = sqrt(sum num^2 / (D den^2) + rms_eps)
+        const float inv_den = __builtin_amdgcn_rcpf(den);
+        scale = inv_den * rsqrtf(ss * inv_den * inv_den * (1.f / D) + a.rms_eps);
+      }
 #pragma unroll
       for (int et = 0; et < ET; ++et) {
         uint2 *slot = reinterpret_cast<uint2 *>(stage + nl * St::kRowBytes + 2 * (16 * et + 4 * kg));
         const uint2 gw = *slot;
         const float gv[4] = {lo_bf16(gw.x), hi_bf16(gw.x), lo_bf16(gw.y), hi_bf16(gw.y)};
         float o[4];
+        if (kNorm) {
+          const float4 w4 = *reinterpret_cast<const float4 *>(s_w + 16 * et + 4 * kg);
+          const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // num / den * sigmoid(g) = num / (den * (1 + exp(-g)))
-          const float e = __expf(-gv[i]);
-          o[i] = acc[et][i] * __builtin_amdgcn_rcpf(__builtin_fmaf(den, e, den));
+          for (int i = 0; i < 4; ++i) {
+            // num / den / rms * w * sigmoid(g)
+            const float e = __expf(-gv[i]);
+            o[i] = acc[et][i] * scale * wv[i] * __builtin_amdgcn_rcpf(1.f + e);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            // num / den * sigmoid(g) = num / (den * (1 + exp(-g)))
+            const float e = __expf(-gv[i]);
+            o[i] = acc[et][i] * __builtin_amdgcn_rcpf(__builtin_fmaf(den, e, den));
+          }
         }
         *slot = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
       }
@@ -702,6 +761,7 @@ MArgs make_margs(const Plan &p) {
   a.div_hw = FastDiv::make((uint32_t)(p.Hs * p.Ws));
   a.div_w = FastDiv::make((uint32_t)p.Ws);
   a.eps = p.eps;
+  a.rms_eps = p.rms_eps;
   return a;
 }
 
@@ -713,49 +773,60 @@ int64_t tab_slice_entries(const Plan &p, int64_t len) {
   return (p.Hs + p.Ws) * (3 * p.d / 16) + rows * (p.d / 8);
 }
 
-template <int D>
-hipError_t state_d(const Plan &p, const void *k, const void *v, const float2 *tab, float *part,
-                   hipStream_t stream) {
+template <int D, bool kBeta>
+hipError_t state_d(const Plan &p, const void *k, const void *v, const void *beta,
+                   const float2 *tab, float *part, hipStream_t stream) {
   const size_t lds = 3 * StateCfg<D>::OP_BYTES + tab_slice_entries(p, p.Lc) * sizeof(float2);
-  auto kern = state_mfma_kernel<D>;
+  auto kern = state_mfma_kernel<D, kBeta>;
   hipError_t e = hipFuncSetAttribute((const void *)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)(p.units * p.C)), dim3(StateCfg<D>::NT), lds, stream,
-                     (const uint16_t *)k, (const uint16_t *)v, tab, part, make_margs(p));
+                     (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)beta, tab, part,
+                     make_margs(p));
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool kNorm>
 hipError_t apply_d(const Plan &p, const void *q, const void *g, const float *states,
-                   const uint16_t *frags, const float2 *tab, void *out, hipStream_t stream) {
-  const size_t lds = (size_t)D * D * 2 * 2 + (size_t)(D / 32) * 64 * 16 +
+                   const uint16_t *frags, const float2 *tab, const void *rms_w, void *out,
+                   hipStream_t stream) {
+  const size_t lds = (size_t)D * D * 2 * 2 + (size_t)(D / 32) * 64 * 16 + (size_t)D * 4 +
                      (size_t)(kApplyThreads / 64) * Stage<D>::kBytes +
                      tab_slice_entries(p, p.Lr) * sizeof(float2);
-  auto kern = apply_mfma_kernel<D>;
+  auto kern = apply_mfma_kernel<D, kNorm>;
   hipError_t e = hipFuncSetAttribute((const void *)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)(p.units * p.R)), dim3(kApplyThreads), lds, stream,
-                     (const uint16_t *)q, (const uint16_t *)g, states, frags, tab, (uint16_t *)out,
+                     (const uint16_t *)q, (const uint16_t *)g, states, frags, tab,
+                     (const uint16_t *)rms_w, (uint16_t *)out,
                      make_margs(p));
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_state_mfma(const Plan &p, const void *k, const void *v, const float2 *tab,
-                             float *partials, hipStream_t stream) {
-  if (p.d == 128) return state_d<128>(p, k, v, tab, partials, stream);
-  if (p.d == 64) return state_d<64>(p, k, v, tab, partials, stream);
+hipError_t launch_state_mfma(const Plan &p, const void *k, const void *v, const void *beta,
+                             const float2 *tab, float *partials, hipStream_t stream) {
+  if (p.d == 128)
+    return beta ? state_d<128, true>(p, k, v, beta, tab, partials, stream)
+                : state_d<128, false>(p, k, v, beta, tab, partials, stream);
+  if (p.d == 64)
+    return beta ? state_d<64, true>(p, k, v, beta, tab, partials, stream)
+                : state_d<64, false>(p, k, v, beta, tab, partials, stream);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_apply_mfma(const Plan &p, const void *q, const void *g, const float *states,
-                             const uint16_t *frags, const float2 *tab, void *out,
-                             hipStream_t stream) {
-  if (p.d == 128) return apply_d<128>(p, q, g, states, frags, tab, out, stream);
-  if (p.d == 64) return apply_d<64>(p, q, g, states, frags, tab, out, stream);
+                             const uint16_t *frags, const float2 *tab, const void *rms_w,
+                             void *out, hipStream_t stream) {
+  if (p.d == 128)
+    return rms_w ? apply_d<128, true>(p, q, g, states, frags, tab, rms_w, out, stream)
+                 : apply_d<128, false>(p, q, g, states, frags, tab, rms_w, out, stream);
+  if (p.d == 64)
+    return rms_w ? apply_d<64, true>(p, q, g, states, frags, tab, rms_w, out, stream)
+                 : apply_d<64, false>(p, q, g, states, frags, tab, rms_w, out, stream);
   return hipErrorInvalidValue;
 }
 

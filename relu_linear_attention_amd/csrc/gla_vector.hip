@@ -19,6 +19,7 @@ struct VecArgs {
   int64_t nb, L, C, Lc, R, Lr;
   int64_t tab_h_off, tab_w_off;  // entry offsets of the h and w tables (t starts at 0)
   float eps;
+  float rms_eps;
 };
 
 template <typename TIn>
@@ -59,9 +60,11 @@ constexpr int kTok = 16;  // tokens staged in LDS per step
 // One workgroup per (unit, chunk): S_c = sum RoPE(phi(k))^T v and
 // z_c = sum phi(k) over the chunk's tokens, written row-major to the partial
 // slot unit*C + c.  Thread t owns the (D/16)^2 state entries t + 256*m.
+// beta (optional): the write gate, scaling a token's rotated key in S only.
 template <typename TIn, int D>
 __global__ __launch_bounds__(kBlock) void state_vector_kernel(const TIn *__restrict__ k,
                                                               const TIn *__restrict__ v,
+                                                              const TIn *__restrict__ beta,
                                                               const float2 *__restrict__ tab,
                                                               float *__restrict__ partials,
                                                               VecArgs a) {
@@ -99,6 +102,11 @@ __global__ __launch_bounds__(kBlock) void state_vector_kernel(const TIn *__restr
         const float2 cs = rope_cs<D>(tab, a, P, t, h, w);
         r0 = k0 * cs.x - k1 * cs.y;
         r1 = k0 * cs.y + k1 * cs.x;
+        if (beta != nullptr) {
+          const float bt = load_elem(beta, (b * a.N + n) * a.H + hd);
+          r0 *= bt;
+          r1 *= bt;
+        }
       }
       s_phi[s][2 * P] = k0;
       s_phi[s][2 * P + 1] = k1;
@@ -132,18 +140,21 @@ __global__ __launch_bounds__(kBlock) void state_vector_kernel(const TIn *__restr
 // One workgroup per (unit, token range): out = num / den * sigmoid(g) with
 // num = RoPE(phi(q)) S and den = phi(q) . z + eps, S and z of the unit read
 // from the reduced fp32 states.  S sits in dynamic LDS (64 KiB at D = 128).
+// rms_w (optional): y = num / den passes an RMSNorm over its D features
+// with weight rms_w before the gate.
 template <typename TIn, int D>
 __global__ __launch_bounds__(kBlock) void apply_vector_kernel(const TIn *__restrict__ q,
                                                               const TIn *__restrict__ g,
                                                               const float *__restrict__ states,
                                                               const float2 *__restrict__ tab,
+                                                              const TIn *__restrict__ rms_w,
                                                               TIn *__restrict__ out, VecArgs a) {
   extern __shared__ float lds[];
   float *s_S = lds;                   // D*D
   float *s_z = s_S + D * D;           // D
-  float *s_phi = s_z + D;             // kTok*D
+  float *s_phi = s_z + D;             // kTok*D (y = num / den when normalising)
   float *s_rot = s_phi + kTok * D;    // kTok*D
-  float *s_den = s_rot + kTok * D;    // kTok
+  float *s_den = s_rot + kTok * D;    // kTok (1 / rms when normalising)
 
   const int64_t wg = blockIdx.x;
   const int64_t unit = wg / a.R, r = wg % a.R;
@@ -184,16 +195,49 @@ __global__ __launch_bounds__(kBlock) void apply_vector_kernel(const TIn *__restr
       s_den[tid] = den + a.eps;
     }
     __syncthreads();
-    for (int o = tid; o < kTok * D; o += kBlock) {
-      const int s = o / D, e = o % D;
-      const int64_t n = n0 + s;
-      if (n < n_end) {
+    if (rms_w == nullptr) {
+      for (int o = tid; o < kTok * D; o += kBlock) {
+        const int s = o / D, e = o % D;
+        const int64_t n = n0 + s;
+        if (n < n_end) {
+          float num = 0.f;
+#pragma unroll 8
+          for (int p = 0; p < D; ++p) num += s_rot[s * D + p] * s_S[p * D + e];
+          const int64_t idx = ((b * a.N + n) * a.H + hd) * D + e;
+          const float gate = 1.f / (1.f + expf(-load_elem(g, idx)));
+          store_elem(out, idx, num / s_den[s] * gate);
+        }
+      }
+    } else {
+      // y = num / den into s_phi (phi(q) is no longer needed), 1 / rms into
+      // s_den, then the normalised and gated output
+      for (int o = tid; o < kTok * D; o += kBlock) {
+        const int s = o / D, e = o % D;
         float num = 0.f;
 #pragma unroll 8
         for (int p = 0; p < D; ++p) num += s_rot[s * D + p] * s_S[p * D + e];
-        const int64_t idx = ((b * a.N + n) * a.H + hd) * D + e;
-        const float gate = 1.f / (1.f + expf(-load_elem(g, idx)));
-        store_elem(out, idx, num / s_den[s] * gate);
+        s_phi[s * D + e] = num;  // (every thread has read s_phi before the last barrier)
+      }
+      __syncthreads();
+      if (tid < kTok) {
+        const float inv_den = 1.f / s_den[tid];
+        float ss = 0.f;
+        for (int e = 0; e < D; ++e) {
+          const float y = s_phi[tid * D + e] * inv_den;
+          s_phi[tid * D + e] = y;
+          ss += y * y;
+        }
+        s_den[tid] = 1.f / sqrtf(ss / D + a.rms_eps);
+      }
+      __syncthreads();
+      for (int o = tid; o < kTok * D; o += kBlock) {
+        const int s = o / D, e = o % D;
+        const int64_t n = n0 + s;
+        if (n < n_end) {
+          const int64_t idx = ((b * a.N + n) * a.H + hd) * D + e;
+          const float gate = 1.f / (1.f + expf(-load_elem(g, idx)));
+          store_elem(out, idx, s_phi[s * D + e] * s_den[s] * load_elem(rms_w, e) * gate);
+        }
       }
     }
     __syncthreads();
@@ -206,74 +250,78 @@ VecArgs make_args(const Plan &p) {
   a.nb = p.nb; a.L = p.L; a.C = p.C; a.Lc = p.Lc; a.R = p.R; a.Lr = p.Lr;
   a.tab_h_off = p.tab_h_off; a.tab_w_off = p.tab_w_off;
   a.eps = p.eps;
+  a.rms_eps = p.rms_eps;
   return a;
 }
 
 template <typename TIn, int D>
-hipError_t state_d(const Plan &p, const void *k, const void *v, const float2 *tab, float *part,
-                   hipStream_t stream) {
+hipError_t state_d(const Plan &p, const void *k, const void *v, const void *beta,
+                   const float2 *tab, float *part, hipStream_t stream) {
   hipLaunchKernelGGL((state_vector_kernel<TIn, D>), dim3((unsigned)(p.units * p.C)), dim3(kBlock),
-                     0, stream, (const TIn *)k, (const TIn *)v, tab, part, make_args(p));
+                     0, stream, (const TIn *)k, (const TIn *)v, (const TIn *)beta, tab, part,
+                     make_args(p));
   return hipGetLastError();
 }
 
 template <typename TIn, int D>
 hipError_t apply_d(const Plan &p, const void *q, const void *g, const float *states,
-                   const float2 *tab, void *out, hipStream_t stream) {
+                   const float2 *tab, const void *rms_w, void *out, hipStream_t stream) {
   const size_t lds = sizeof(float) * (D * D + D + 2 * kTok * D + kTok);
   auto kern = apply_vector_kernel<TIn, D>;
   hipError_t e = hipFuncSetAttribute((const void *)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)(p.units * p.R)), dim3(kBlock), lds, stream,
-                     (const TIn *)q, (const TIn *)g, states, tab, (TIn *)out, make_args(p));
+                     (const TIn *)q, (const TIn *)g, states, tab, (const TIn *)rms_w, (TIn *)out,
+                     make_args(p));
   return hipGetLastError();
 }
 
 template <typename TIn>
-hipError_t state_t(const Plan &p, const void *k, const void *v, const float2 *tab, float *part,
-                   hipStream_t s) {
+hipError_t state_t(const Plan &p, const void *k, const void *v, const void *beta,
+                   const float2 *tab, float *part, hipStream_t s) {
   switch (p.d) {
-    case 16: return state_d<TIn, 16>(p, k, v, tab, part, s);
-    case 32: return state_d<TIn, 32>(p, k, v, tab, part, s);
-    case 48: return state_d<TIn, 48>(p, k, v, tab, part, s);
-    case 64: return state_d<TIn, 64>(p, k, v, tab, part, s);
-    case 80: return state_d<TIn, 80>(p, k, v, tab, part, s);
-    case 96: return state_d<TIn, 96>(p, k, v, tab, part, s);
-    case 112: return state_d<TIn, 112>(p, k, v, tab, part, s);
-    case 128: return state_d<TIn, 128>(p, k, v, tab, part, s);
+    case 16: return state_d<TIn, 16>(p, k, v, beta, tab, part, s);
+    case 32: return state_d<TIn, 32>(p, k, v, beta, tab, part, s);
+    case 48: return state_d<TIn, 48>(p, k, v, beta, tab, part, s);
+    case 64: return state_d<TIn, 64>(p, k, v, beta, tab, part, s);
+    case 80: return state_d<TIn, 80>(p, k, v, beta, tab, part, s);
+    case 96: return state_d<TIn, 96>(p, k, v, beta, tab, part, s);
+    case 112: return state_d<TIn, 112>(p, k, v, beta, tab, part, s);
+    case 128: return state_d<TIn, 128>(p, k, v, beta, tab, part, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename TIn>
 hipError_t apply_t(const Plan &p, const void *q, const void *g, const float *st,
-                   const float2 *tab, void *out, hipStream_t s) {
+                   const float2 *tab, const void *w, void *out, hipStream_t s) {
   switch (p.d) {
-    case 16: return apply_d<TIn, 16>(p, q, g, st, tab, out, s);
-    case 32: return apply_d<TIn, 32>(p, q, g, st, tab, out, s);
-    case 48: return apply_d<TIn, 48>(p, q, g, st, tab, out, s);
-    case 64: return apply_d<TIn, 64>(p, q, g, st, tab, out, s);
-    case 80: return apply_d<TIn, 80>(p, q, g, st, tab, out, s);
-    case 96: return apply_d<TIn, 96>(p, q, g, st, tab, out, s);
-    case 112: return apply_d<TIn, 112>(p, q, g, st, tab, out, s);
-    case 128: return apply_d<TIn, 128>(p, q, g, st, tab, out, s);
+    case 16: return apply_d<TIn, 16>(p, q, g, st, tab, w, out, s);
+    case 32: return apply_d<TIn, 32>(p, q, g, st, tab, w, out, s);
+    case 48: return apply_d<TIn, 48>(p, q, g, st, tab, w, out, s);
+    case 64: return apply_d<TIn, 64>(p, q, g, st, tab, w, out, s);
+    case 80: return apply_d<TIn, 80>(p, q, g, st, tab, w, out, s);
+    case 96: return apply_d<TIn, 96>(p, q, g, st, tab, w, out, s);
+    case 112: return apply_d<TIn, 112>(p, q, g, st, tab, w, out, s);
+    case 128: return apply_d<TIn, 128>(p, q, g, st, tab, w, out, s);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_state_generic(const Plan &p, const void *k, const void *v, const float2 *tab,
-                                float *partials, hipStream_t stream) {
-  return p.bf16 ? state_t<uint16_t>(p, k, v, tab, partials, stream)
-                : state_t<float>(p, k, v, tab, partials, stream);
+hipError_t launch_state_generic(const Plan &p, const void *k, const void *v, const void *beta,
+                                const float2 *tab, float *partials, hipStream_t stream) {
+  return p.bf16 ? state_t<uint16_t>(p, k, v, beta, tab, partials, stream)
+                : state_t<float>(p, k, v, beta, tab, partials, stream);
 }
 
 hipError_t launch_apply_generic(const Plan &p, const void *q, const void *g, const float *states,
-                                const float2 *tab, void *out, hipStream_t stream) {
-  return p.bf16 ? apply_t<uint16_t>(p, q, g, states, tab, out, stream)
-                : apply_t<float>(p, q, g, states, tab, out, stream);
+                                const float2 *tab, const void *rms_w, void *out,
+                                hipStream_t stream) {
+  return p.bf16 ? apply_t<uint16_t>(p, q, g, states, tab, rms_w, out, stream)
+                : apply_t<float>(p, q, g, states, tab, rms_w, out, stream);
 }
 
 }  // namespace gla

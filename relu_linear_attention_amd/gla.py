@@ -25,7 +25,7 @@ GLA_NUM_STAGES = 4
 # every symbol include/gla.h declares
 EXPORTS = (
     "gla_forward", "gla_block_causal_forward", "gla_workspace_bytes", "gla_forward_ws",
-    "gla_state", "gla_block_step", "gla_status_string", "gla_last_error", "gla_profile_enable",
+    "gla_state", "gla_block_step", "gla_gated_forward", "gla_status_string", "gla_last_error", "gla_profile_enable",
     "gla_profile_read", "gla_stage_name", "gla_uses_matrix_cores",
 )
 
@@ -62,9 +62,11 @@ def load():
     lib.gla_block_step.argtypes = (tensors5 + [_vp, _vp] + sizes6 + [_i64, ctypes.c_int, _f, _f,
                                                                     ctypes.c_int, _vp,
                                                                     ctypes.c_size_t, _vp])
+    lib.gla_gated_forward.argtypes = ([_vp] * 7 + sizes6 + [_i64, _f, _f, _f, ctypes.c_int, _vp,
+                                                            ctypes.c_size_t, _vp])
     for name in ("gla_forward", "gla_block_causal_forward", "gla_workspace_bytes",
-                 "gla_forward_ws", "gla_state", "gla_block_step", "gla_profile_enable",
-                 "gla_profile_read"):
+                 "gla_forward_ws", "gla_state", "gla_block_step", "gla_gated_forward",
+                 "gla_profile_enable", "gla_profile_read"):
         getattr(lib, name).restype = ctypes.c_int
     lib.gla_status_string.argtypes = [ctypes.c_int]
     lib.gla_status_string.restype = ctypes.c_char_p
@@ -196,6 +198,20 @@ def gla_block_step(q, k, v, g, out, S, z, block_grid, t_offset, update=True, rop
                                rope_theta, eps, _dtype_code(k), _ptr(workspace), ws_bytes,
                                _stream_handle(stream))
     _check(st, "gla_block_step")
+
+
+def gla_gated_forward(q, k, v, g, beta, rms_weight, out, grid, frames_per_block=0,
+                      rope_theta=10000.0, eps=1e-6, rms_eps=1e-6, workspace=None, stream=None):
+    """The gated mixer of Eq. (1) without W_o: beta [B, N, H] (None: no write
+    gate) and rms_weight [d] (None: no RMSNorm), both of q's dtype."""
+    _check_tensors(*[t for t in (q, k, v, g, beta, rms_weight, out, workspace) if t is not None])
+    B, H, T, Hs, Ws, d = _sizes(q, grid)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().gla_gated_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(rms_weight),
+                                  _ptr(out), B, H, T, Hs, Ws, d, frames_per_block, rope_theta, eps,
+                                  rms_eps, _dtype_code(q), _ptr(workspace), ws_bytes,
+                                  _stream_handle(stream))
+    _check(st, "gla_gated_forward")
 
 
 def gla_profile_enable(enable: bool = True):

@@ -131,6 +131,28 @@ def test_block_step_rejects_bad_arguments(lib, kw, needle):
     assert needle in gla.gla_last_error()
 
 
+def _gated(lib, beta=FAKE * 11, w=FAKE * 13, rms_eps=1e-6, out=FAKE * 9, F=0):
+    p = [ctypes.c_void_p(x) if x else None for x in (FAKE, FAKE * 3, FAKE * 5, FAKE * 7)]
+    gb = [ctypes.c_void_p(x) if x else None for x in (beta, w, out)]
+    return lib.gla_gated_forward(*p, *gb, 1, 2, 2, 4, 4, 32, F, 1e4, 1e-6, rms_eps, gla.GLA_BF16,
+                                 None, 0, None)
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(beta=FAKE * 11 + 1), "beta is misaligned"),
+    (dict(w=FAKE * 13 + 1), "rms_weight is misaligned"),
+    (dict(rms_eps=0.0), "rms_eps"),
+    (dict(rms_eps=float("nan")), "rms_eps"),
+    (dict(beta=FAKE * 9 + 64), "overlaps beta"),
+    (dict(w=FAKE * 9 + 64), "overlaps rms_weight"),
+    (dict(out=0), "null"),
+    (dict(F=3), "divide"),
+])
+def test_gated_forward_rejects_bad_arguments(lib, kw, needle):
+    assert _gated(lib, **kw) == gla.GLA_ERR_INVALID_ARG
+    assert needle in gla.gla_last_error()
+
+
 def test_workspace_query_rejects_bad_sizes(lib):
     n = ctypes.c_size_t(0)
     assert lib.gla_workspace_bytes(1, 1, 3, 2, 2, 128, 2, 0, ctypes.byref(n)) == 1
