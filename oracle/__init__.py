@@ -64,6 +64,8 @@ def _load():
     lib.ora_block_step.restype = ctypes.c_int
     lib.ora_gated_forward.argtypes = [_ptr] * 6 + [_i64] * 7 + [_dbl, _dbl, _dbl, _ptr]
     lib.ora_gated_forward.restype = ctypes.c_int
+    lib.ora_backward.argtypes = [_ptr] * 5 + [_i64] * 7 + [_dbl, _dbl] + [_ptr] * 4
+    lib.ora_backward.restype = ctypes.c_int
     lib.ora_num_blocks.argtypes = [_i64, _i64]
     lib.ora_num_blocks.restype = _i64
     lib.ora_num_threads.argtypes = []
@@ -200,3 +202,17 @@ def gated_forward(q, k, v, g, beta, w, grid, frames_per_block: int = 0, theta: f
                                    _p(out))
     _check(rc, "gated_forward")
     return out
+
+
+def backward(q, k, v, g, dout, grid, frames_per_block: int = 0, theta: float = 10000.0,
+             eps: float = 1e-6):
+    """Gradients of sum(dout * forward(...)) with respect to q, k, v, g, each
+    [B, N, H, d] fp64."""
+    q, k, v, g, dout = _f32(q), _f32(k), _f32(v), _f32(g), _f32(dout)
+    B, N, H, d = q.shape
+    T, Hs, Ws = grid
+    outs = [np.empty((B, N, H, d), dtype=np.float64) for _ in range(4)]
+    rc = _load().ora_backward(_p(q), _p(k), _p(v), _p(g), _p(dout), B, H, T, Hs, Ws, d,
+                              frames_per_block, float(theta), float(eps), *[_p(o) for o in outs])
+    _check(rc, "backward")
+    return tuple(outs)

@@ -299,6 +299,139 @@ int ora_gated_forward(const float *q, const float *k, const float *v, const floa
   return rc;
 }
 
+/* Gradients of the operator (the loss L = sum dout . out), derived from the
+ * forward definition above by the chain rule; [V2] Section 3 trains the
+ * model from scratch, so the mixer needs them.  Per (batch, head), with the
+ * state S^b and normaliser z^b each token of block b reads (ora_state):
+ *   y_i    = num_i / den_i,   num_i = RoPE_i(phi(q_i)) S^b,   den_i = phi(q_i) . z^b + eps
+ *   dg_i   = dout_i * y_i * s_i (1 - s_i),   s_i = sigmoid(g_i)
+ *   dnum_i = dout_i * s_i / den_i,   dden_i = - (dout_i * s_i) . y_i / den_i
+ *   dq_i   = [ RoPE_i^T(S^b dnum_i) + dden_i z^b ] * 1[q_i > 0]
+ *   dS^b  += RoPE_i(phi(q_i))^T dnum_i,   dz^b += dden_i phi(q_i)
+ * S^b sums the per-block states of blocks 0..b, so the gradient of block c's
+ * own state is the suffix sum G^c = sum over b >= c of dS^b (likewise for z):
+ *   dv_n   = RoPE_n(phi(k_n)) G^c
+ *   dk_n   = [ RoPE_n^T(G^c v_n) + Gz^c ] * 1[k_n > 0]         (n in block c)
+ * RoPE^T, the transpose of a rotation, is the rotation by minus the angle.
+ * All inputs [B, N, H, d] float; outputs dq, dk, dv, dg [B, N, H, d] double. */
+int ora_backward(const float *q, const float *k, const float *v, const float *g,
+                 const float *dout, int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws,
+                 int64_t d, int64_t F, double theta, double eps, double *dq, double *dk,
+                 double *dv, double *dg) {
+  if (!q || !k || !v || !g || !dout || !dq || !dk || !dv || !dg) return ORA_BAD_ARG;
+  int rc = check_shape(B, H, T, Hs, Ws, d, F);
+  if (rc) return rc;
+  const int64_t N = T * Hs * Ws;
+  const int64_t nb = ora_num_blocks(T, F);
+  const int64_t tpb = N / nb;
+  const int64_t dd = d * d;
+  double *S = (double *)malloc((size_t)(B * H * nb * dd) * sizeof(double));
+  double *z = (double *)malloc((size_t)(B * H * nb * d) * sizeof(double));
+  if (!S || !z) {
+    free(S);
+    free(z);
+    return ORA_NO_MEM;
+  }
+  rc = ora_state(k, v, B, H, T, Hs, Ws, d, F, theta, NULL, S, z);
+  int failed = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  for (int64_t b = 0; b < B; ++b) {
+    for (int64_t h = 0; h < H; ++h) {
+      if (rc != ORA_OK) continue;
+      double *dS = (double *)calloc((size_t)(nb * dd), sizeof(double));
+      double *dz = (double *)calloc((size_t)(nb * d), sizeof(double));
+      double *w = (double *)malloc((size_t)(8 * d) * sizeof(double));
+      if (!dS || !dz || !w) {
+#pragma omp atomic write
+        failed = 1;
+      } else {
+        double *phi = w, *rot = w + d, *dy = w + 2 * d, *dnum = w + 3 * d, *t1 = w + 4 * d,
+               *t2 = w + 5 * d, *vrow = w + 6 * d, *y = w + 7 * d;
+        /* the q side: dq, dg and the per-block dS, dz */
+        for (int64_t n = 0; n < N; ++n) {
+          const int64_t row = ((b * N + n) * H + h) * d, blk = n / tpb;
+          const double *Sb = S + ((b * H + h) * nb + blk) * dd;
+          const double *zb = z + ((b * H + h) * nb + blk) * d;
+          int64_t pos[3], neg[3];
+          grid_position(n, Hs, Ws, NULL, pos);
+          for (int a = 0; a < 3; ++a) neg[a] = -pos[a];
+          for (int64_t p = 0; p < d; ++p) {
+            const double x = (double)q[row + p];
+            phi[p] = x > 0.0 ? x : 0.0;
+          }
+          ora_rope(phi, rot, d, pos, theta);
+          double den = eps;
+          for (int64_t p = 0; p < d; ++p) den += phi[p] * zb[p];
+          double dyy = 0.0;
+          for (int64_t e = 0; e < d; ++e) {
+            double num = 0.0;
+            for (int64_t p = 0; p < d; ++p) num += rot[p] * Sb[p * d + e];
+            y[e] = num / den;
+            const double s = 1.0 / (1.0 + exp(-(double)g[row + e]));
+            dg[row + e] = (double)dout[row + e] * y[e] * s * (1.0 - s);
+            dy[e] = (double)dout[row + e] * s;
+            dyy += dy[e] * y[e];
+          }
+          const double dden = -dyy / den;
+          for (int64_t e = 0; e < d; ++e) dnum[e] = dy[e] / den;
+          for (int64_t p = 0; p < d; ++p) {
+            double acc = 0.0;
+            for (int64_t e = 0; e < d; ++e) acc += Sb[p * d + e] * dnum[e];
+            t1[p] = acc; /* gradient of the rotated phi(q) */
+          }
+          ora_rope(t1, t2, d, neg, theta); /* back through the rotation */
+          for (int64_t p = 0; p < d; ++p)
+            dq[row + p] = (double)q[row + p] > 0.0 ? t2[p] + dden * zb[p] : 0.0;
+          double *dSb = dS + blk * dd, *dzb = dz + blk * d;
+          for (int64_t p = 0; p < d; ++p) {
+            dzb[p] += dden * phi[p];
+            for (int64_t e = 0; e < d; ++e) dSb[p * d + e] += rot[p] * dnum[e];
+          }
+        }
+        /* suffix sums over blocks: the gradients of each block's own sums */
+        for (int64_t blk = nb - 2; blk >= 0; --blk) {
+          for (int64_t i = 0; i < dd; ++i) dS[blk * dd + i] += dS[(blk + 1) * dd + i];
+          for (int64_t i = 0; i < d; ++i) dz[blk * d + i] += dz[(blk + 1) * d + i];
+        }
+        /* the k, v side */
+        for (int64_t n = 0; n < N; ++n) {
+          const int64_t row = ((b * N + n) * H + h) * d, blk = n / tpb;
+          const double *G = dS + blk * dd, *Gz = dz + blk * d;
+          int64_t pos[3], neg[3];
+          grid_position(n, Hs, Ws, NULL, pos);
+          for (int a = 0; a < 3; ++a) neg[a] = -pos[a];
+          for (int64_t p = 0; p < d; ++p) {
+            const double x = (double)k[row + p];
+            phi[p] = x > 0.0 ? x : 0.0;
+            vrow[p] = (double)v[row + p];
+          }
+          ora_rope(phi, rot, d, pos, theta);
+          for (int64_t e = 0; e < d; ++e) {
+            double acc = 0.0;
+            for (int64_t p = 0; p < d; ++p) acc += rot[p] * G[p * d + e];
+            dv[row + e] = acc;
+          }
+          for (int64_t p = 0; p < d; ++p) {
+            double acc = 0.0;
+            for (int64_t e = 0; e < d; ++e) acc += G[p * d + e] * vrow[e];
+            t1[p] = acc;
+          }
+          ora_rope(t1, t2, d, neg, theta);
+          for (int64_t p = 0; p < d; ++p)
+            dk[row + p] = (double)k[row + p] > 0.0 ? t2[p] + Gz[p] : 0.0;
+        }
+      }
+      free(dS);
+      free(dz);
+      free(w);
+    }
+  }
+  free(S);
+  free(z);
+  if (rc != ORA_OK) return rc;
+  return failed ? ORA_NO_MEM : ORA_OK;
+}
+
 /* Whole operator: ora_state followed by ora_apply over every token.
  * out : [B, N, H, d] double. */
 int ora_forward(const float *q, const float *k, const float *v, const float *g, int64_t B,

@@ -52,6 +52,13 @@ MUTATIONS = [
      "const double inv_rms = 1.0 / sqrt(ss / (double)(d - 1) + rms_eps);"),
     ("rmsnorm_weight_index", "on[e] = on[e] * inv_rms * (double)w[e];",
      "on[e] = on[e] * inv_rms * (double)w[(e + 1) % d];"),
+    ("backward_prefix_not_suffix", "for (int64_t blk = nb - 2; blk >= 0; --blk) {\n          for (int64_t i = 0; i < dd; ++i) dS[blk * dd + i] += dS[(blk + 1) * dd + i];",
+     "for (int64_t blk = nb - 2; blk >= 0; --blk) {\n          for (int64_t i = 0; i < dd; ++i) dS[(blk + 1) * dd + i] += dS[blk * dd + i];"),
+    ("backward_dden_sign", "const double dden = -dyy / den;", "const double dden = dyy / den;"),
+    ("backward_forward_rotation", "ora_rope(t1, t2, d, neg, theta); /* back through the rotation */",
+     "ora_rope(t1, t2, d, pos, theta); /* back through the rotation */"),
+    ("backward_relu_mask_dropped_on_k", "dk[row + p] = (double)k[row + p] > 0.0 ? t2[p] + Gz[p] : 0.0;",
+     "dk[row + p] = t2[p] + Gz[p];"),
     ("block_step_offset_ignored", "const int64_t pos0[3] = {t_offset, 0, 0};",
      "const int64_t pos0[3] = {0, 0, 0};"),
 ]

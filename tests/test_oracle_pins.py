@@ -607,3 +607,55 @@ def test_gated_single_token_closed_form():
     vv = v[0, 0, 0].astype(np.float64)
     exp = vv / math.sqrt(float(np.mean(vv * vv))) * w / (1.0 + np.exp(-g[0, 0, 0].astype(np.float64)))
     np.testing.assert_allclose(out, exp, rtol=1e-12, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# gradients (the loss L = sum dout * out): central finite differences of the
+# forward oracle, one element at a time (a step of 2^-10 is exact in fp32 for
+# these magnitudes), and Euler's identities for homogeneous functions
+# ---------------------------------------------------------------------------
+def _loss(x, dout, grid, F, theta, eps):
+    return float(np.sum(dout * oracle.forward(x["q"], x["k"], x["v"], x["g"], grid, F, theta, eps)))
+
+
+@pytest.mark.parametrize("B,T,Hs,Ws,H,d,theta,F", [
+    (1, 2, 2, 3, 2, 16, 10000.0, 0),
+    (1, 3, 2, 2, 1, 32, 50.0, 1),
+    (2, 2, 2, 2, 1, 16, 7.0, 0),
+])
+def test_backward_matches_finite_differences(B, T, Hs, Ws, H, d, theta, F):
+    grid = (T, Hs, Ws)
+    x = host_inputs(B, T, Hs, Ws, H, d, "f32", seed=51)
+    rng = np.random.default_rng(52)
+    dout = rng.standard_normal(x["q"].shape).astype(np.float32)
+    eps = 1e-6
+    grads = dict(zip("qkvg", oracle.backward(x["q"], x["k"], x["v"], x["g"], dout, grid, F, theta,
+                                             eps)))
+    h = 2.0 ** -10
+    for name in "qkvg":
+        flat = x[name].reshape(-1)
+        cand = np.arange(flat.size)
+        if name in "qk":  # stay clear of the ReLU kink
+            cand = cand[np.abs(flat) > 8 * h]
+        for idx in rng.choice(cand, size=10, replace=False):
+            xp = {n: a.copy() for n, a in x.items()}
+            xm = {n: a.copy() for n, a in x.items()}
+            xp[name].reshape(-1)[idx] += h
+            xm[name].reshape(-1)[idx] -= h
+            fd = (_loss(xp, dout, grid, F, theta, eps) - _loss(xm, dout, grid, F, theta, eps)) / (2 * h)
+            an = grads[name].reshape(-1)[idx]
+            scale = np.max(np.abs(grads[name]))
+            assert abs(fd - an) <= 1e-5 * abs(an) + 1e-6 * scale, (name, idx, fd, an)
+
+
+def test_backward_euler_identities():
+    # L is linear in v: sum dv * v = L.  With eps = 0 the output does not
+    # change when q or k is scaled by c > 0, so sum dq * q = sum dk * k = 0.
+    x = host_inputs(1, 3, 2, 3, 2, 32, "f32", seed=53)
+    dout = np.random.default_rng(54).standard_normal(x["q"].shape).astype(np.float32)
+    for F in (0, 1):
+        dq, dk, dv, dg = oracle.backward(x["q"], x["k"], x["v"], x["g"], dout, (3, 2, 3), F, eps=0.0)
+        L = _loss(x, dout, (3, 2, 3), F, 10000.0, 0.0)
+        assert abs(np.sum(dv * x["v"]) - L) <= 1e-10 * np.sum(np.abs(dv * x["v"]))
+        assert abs(np.sum(dq * x["q"])) <= 1e-10 * np.sum(np.abs(dq * x["q"]))
+        assert abs(np.sum(dk * x["k"])) <= 1e-10 * np.sum(np.abs(dk * x["k"]))
