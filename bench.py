@@ -176,6 +176,50 @@ def gated_leg(w, x, ws, steps: int, warmup: int):
             "algorithmic_bytes_per_call": nbytes, "GBps": gbps, "frac_of_peak": gbps / PEAK_HBM_GBPS}
 
 
+def backward_leg(w, x, steps: int, warmup: int):
+    """Gradients (gla_backward) of sum(dout * out) on the same workload: the
+    state stage re-run, then the gradient kernels.  Algorithmic bytes: q, k,
+    v, g, dout read once and dq, dk, dv, dg written once."""
+    import torch
+
+    from relu_linear_attention_amd import gla
+
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed + 200)
+    dout = torch.randn(x["q"].shape, device="cuda", generator=gen).to(x["q"].dtype)
+    grads = [torch.empty_like(x["q"]) for _ in range(4)]
+    ws = torch.empty(gla.gla_backward_workspace_bytes(w.B, w.H, w.T, w.Hs, w.Ws, w.d,
+                                                      w.frames_per_block,
+                                                      gla.GLA_BF16 if w.dtype == "bf16"
+                                                      else gla.GLA_F32),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call():
+        gla.gla_backward(x["q"], x["k"], x["v"], x["g"], dout, *grads, w.grid, w.frames_per_block,
+                         w.theta, w.eps, workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    gla.gla_profile_enable(True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        call()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    stages = gla.gla_profile_read()
+    gla.gla_profile_enable(False)
+    ms = start.elapsed_time(stop) / steps
+    nbytes = 9 * w.B * w.N * w.H * w.d * w.elem_bytes
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": w.name, "ms_per_call": ms, "tokens_per_s": w.B * w.N / (ms * 1e-3),
+            "stages_ms": {k: (v / n if n else None) for k, (n, v) in stages.items()},
+            "algorithmic_bytes_per_call": nbytes, "GBps": gbps, "frac_of_peak": gbps / PEAK_HBM_GBPS,
+            "kernels": "vector (fp32 VALU) gradient kernels; matrix-core state stage"}
+
+
 def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
     """A plain device-to-device copy of known size, for scaling the HBM
     counters (FETCH_SIZE, WRITE_SIZE) of the kernels."""
@@ -208,6 +252,8 @@ def main() -> int:
                     help="skip the streaming block-step measurement")
     ap.add_argument("--no-gated", action="store_true",
                     help="skip the gated-mixer (write gate + RMSNorm) measurement")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the gradient measurement")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
@@ -310,6 +356,8 @@ def main() -> int:
     }
     if not args.no_gated and mfma:
         result["gated"] = gated_leg(w, x, ws, max(3, args.steps // 2), 10)
+    if not args.no_backward:
+        result["backward"] = backward_leg(w, x, max(3, args.steps // 10), 3)
     if not args.no_block_step:
         result["block_step"] = block_step_leg(max(3, args.steps // 4), 5)
     if not args.no_cpu_baseline:

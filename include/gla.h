@@ -181,6 +181,31 @@ gla_status gla_block_step(const void *q, const void *k, const void *v, const voi
                           float eps, gla_dtype dtype, void *workspace, size_t workspace_bytes,
                           hipStream_t stream);
 
+/*
+ * Gradients of the non-causal or block-causal operator (frames_per_block = 0
+ * or its block size): with the loss L = sum over every element of
+ * dout * out, writes dq = dL/dq, dk, dv and dg ([B, N, H, d], the tensors'
+ * element type, device memory; none may overlap another or an input).
+ * By the chain rule through the definition above ("SANA-Video 2.0" Eq. (1),
+ * "SANA-Video" Sections 3.2 and 3.4); the derivative of ReLU at 0 is taken
+ * as 0, and in block-causal mode a block's keys and values receive the
+ * gradients of every later block that reads them.  The call re-runs the
+ * state stage, then the gradient kernels (fp32 arithmetic on the vector
+ * units for every supported d).
+ * workspace: NULL (taken stream-ordered on `stream`) or at least
+ * gla_backward_workspace_bytes() bytes of device memory, 256-byte aligned.
+ */
+gla_status gla_backward(const void *q, const void *k, const void *v, const void *g,
+                        const void *dout, void *dq, void *dk, void *dv, void *dg, int64_t B,
+                        int64_t H, int64_t T, int64_t Hs, int64_t Ws, int64_t d,
+                        int64_t frames_per_block, float rope_theta, float eps, gla_dtype dtype,
+                        void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace of gla_backward with these sizes on the current device. */
+gla_status gla_backward_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws,
+                                        int64_t d, int64_t frames_per_block, gla_dtype dtype,
+                                        size_t *bytes);
+
 /* Static description of a status code. */
 const char *gla_status_string(gla_status status);
 
@@ -192,10 +217,10 @@ const char *gla_last_error(void);
  * by HIP events recorded on the launch stream.  gla_profile_read() waits for
  * the recorded events and returns, per stage, the number of launches and
  * their summed duration in milliseconds.  Stages: 0 rope table, 1 state
- * partials, 2 reduce/prefix, 3 apply.  Enabling (or disabling) clears the
+ * partials, 2 reduce/prefix, 3 apply, 4 gradient kernels (gla_backward).  Enabling (or disabling) clears the
  * record.  Meant for one thread at a time.
  */
-#define GLA_NUM_STAGES 4
+#define GLA_NUM_STAGES 5
 gla_status gla_profile_enable(int enable);
 gla_status gla_profile_read(int64_t launches[GLA_NUM_STAGES], double total_ms[GLA_NUM_STAGES]);
 const char *gla_stage_name(int stage);

@@ -262,8 +262,16 @@ gla_status make_plan(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, in
     if (std::max(lds_state, lds_apply) > 160 * 1024) return fail(GLA_ERR_UNSUPPORTED,
         "internal: LDS plan of %lld bytes exceeds the CU", (long long)std::max(lds_state, lds_apply));
   }
+  // Backward: vector kernels, about four workgroups per compute unit of
+  // 16..4096 tokens each.
+  P.Lb = round_up(ceil_div(P.units * P.L, 4 * (int64_t)cus), 16);
+  P.Lb = std::max<int64_t>(16, std::min<int64_t>(P.Lb, 4096));
+  P.Lb = std::min(P.Lb, round_up(P.L, 16));
+  P.Rb = ceil_div(P.L, P.Lb);
+
   const int64_t max_grid = 0x7fffffff;
-  if (P.units * P.C > max_grid || P.units * P.R > max_grid || B * H > max_grid)
+  if (P.units * P.C > max_grid || P.units * P.R > max_grid || P.units * P.Rb > max_grid ||
+      B * H > max_grid)
     return fail(GLA_ERR_UNSUPPORTED, "too many (batch, head, block) units for one launch");
 
   // Workspace layout.
@@ -277,6 +285,11 @@ gla_status make_plan(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, in
   P.off_frag = off;
   if (P.mfma) off = align256(off + (size_t)P.units * 2 * d * d * sizeof(uint16_t));
   P.total_bytes = off;
+  P.off_bpart = off;
+  off = align256(off + (size_t)P.units * P.Rb * gla::kPartialStride(d) * sizeof(float));
+  P.off_grad = off;
+  off = align256(off + (size_t)P.units * gla::kPartialStride(d) * sizeof(float));
+  P.bwd_total_bytes = off;
   *p = P;
   return GLA_OK;
 }
@@ -291,7 +304,7 @@ bool g_prof_on = false;
 std::vector<StageRecord> g_prof;
 
 const char *kStageNames[GLA_NUM_STAGES] = {"rope_table", "state_partials", "reduce_prefix",
-                                           "apply"};
+                                           "apply", "backward"};
 
 void prof_clear_locked() {
   for (auto &r : g_prof) {
@@ -588,6 +601,92 @@ gla_status gla_gated_forward(const void *q, const void *k, const void *v, const 
   return forward_impl(q, k, v, g, out, B, H, T, Hs, Ws, d, frames_per_block, rope_theta, eps,
                       dtype, workspace, workspace_bytes, workspace == nullptr, stream, nullptr, &gt,
                       rms_eps);
+}
+
+gla_status gla_backward(const void *q, const void *k, const void *v, const void *g,
+                        const void *dout, void *dq, void *dk, void *dv, void *dg, int64_t B,
+                        int64_t H, int64_t T, int64_t Hs, int64_t Ws, int64_t d,
+                        int64_t frames_per_block, float rope_theta, float eps, gla_dtype dtype,
+                        void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  const int64_t F = frames_per_block;
+  gla_status st = check_sizes(B, H, T, Hs, Ws, d, F, dtype);
+  if (st != GLA_OK) return st;
+  if (!std::isfinite(rope_theta)) return fail(GLA_ERR_INVALID_ARG, "rope_theta must be finite");
+  if (!std::isfinite(eps) || eps < 0.f)
+    return fail(GLA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  const void *ins[5] = {q, k, v, g, dout};
+  const void *outs[4] = {dq, dk, dv, dg};
+  const char *in_names[5] = {"q", "k", "v", "g", "dout"};
+  const char *out_names[4] = {"dq", "dk", "dv", "dg"};
+  for (int i = 0; i < 5; ++i)
+    if (!ins[i]) return fail(GLA_ERR_INVALID_ARG, "null tensor pointer (%s)", in_names[i]);
+  for (int i = 0; i < 4; ++i)
+    if (!outs[i]) return fail(GLA_ERR_INVALID_ARG, "null tensor pointer (%s)", out_names[i]);
+  const size_t bytes = (size_t)(B * T * Hs * Ws * H * d) * (dtype == GLA_BF16 ? 2 : 4);
+  for (int o = 0; o < 4; ++o) {
+    for (int i = 0; i < 5; ++i)
+      if (ranges_overlap(outs[o], bytes, ins[i], bytes))
+        return fail(GLA_ERR_INVALID_ARG, "%s overlaps input %s", out_names[o], in_names[i]);
+    for (int o2 = o + 1; o2 < 4; ++o2)
+      if (ranges_overlap(outs[o], bytes, outs[o2], bytes))
+        return fail(GLA_ERR_INVALID_ARG, "%s overlaps %s", out_names[o], out_names[o2]);
+  }
+  if (workspace != nullptr && ((uintptr_t)workspace & 255) != 0)
+    return fail(GLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  int cus = 0;
+  st = device_cus(&cus);
+  if (st != GLA_OK) return st;
+  const bool aligned16 = (((uintptr_t)k | (uintptr_t)v) & 15) == 0;
+  Plan P;
+  st = make_plan(B, H, T, Hs, Ws, d, F, dtype, rope_theta, eps, cus, aligned16, &P);
+  if (st != GLA_OK) return st;
+  if (workspace != nullptr && workspace_bytes < P.bwd_total_bytes)
+    return fail(GLA_ERR_INVALID_ARG, "workspace too small: %zu bytes given, %zu needed",
+                workspace_bytes, P.bwd_total_bytes);
+  void *mem = workspace;
+  if (mem == nullptr) {
+    hipError_t e = hipMallocAsync(&mem, P.bwd_total_bytes, stream);
+    if (e != hipSuccess || mem == nullptr) {
+      (void)hipGetLastError();
+      return fail(GLA_ERR_ALLOC, "hipMallocAsync of %zu workspace bytes failed", P.bwd_total_bytes);
+    }
+  }
+  // the forward state of the call, then the gradient kernels
+  st = run_plan(P, nullptr, k, v, nullptr, nullptr, mem, stream, false);
+  if (st == GLA_OK) {
+    char *base = (char *)mem;
+    st = timed_launch(4, stream, "gradient kernels", [&] {
+      return gla::launch_backward(P, q, k, v, g, dout, (const float *)(base + P.off_state),
+                                  (const float2 *)(base + P.off_tab),
+                                  (float *)(base + P.off_bpart), (float *)(base + P.off_grad),
+                                  dq, dk, dv, dg, stream);
+    });
+  }
+  if (workspace == nullptr) {
+    hipError_t e = hipFreeAsync(mem, stream);
+    if (st == GLA_OK && e != hipSuccess) return hip_fail(e, "hipFreeAsync");
+  }
+  return st;
+}
+
+gla_status gla_backward_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws,
+                                        int64_t d, int64_t frames_per_block, gla_dtype dtype,
+                                        size_t *bytes) {
+  g_last_error[0] = '\0';
+  if (!bytes) return fail(GLA_ERR_INVALID_ARG, "bytes must not be null");
+  gla_status st = check_sizes(B, H, T, Hs, Ws, d, frames_per_block, dtype);
+  if (st != GLA_OK) return st;
+  int cus = 0;
+  st = device_cus(&cus);
+  if (st != GLA_OK) return st;
+  Plan P, Pv;
+  st = make_plan(B, H, T, Hs, Ws, d, frames_per_block, dtype, 10000.f, 0.f, cus, true, &P);
+  if (st != GLA_OK) return st;
+  st = make_plan(B, H, T, Hs, Ws, d, frames_per_block, dtype, 10000.f, 0.f, cus, false, &Pv);
+  if (st != GLA_OK) return st;
+  *bytes = std::max(P.bwd_total_bytes, Pv.bwd_total_bytes);
+  return GLA_OK;
 }
 
 const char *gla_status_string(gla_status status) {

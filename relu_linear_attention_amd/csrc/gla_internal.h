@@ -27,6 +27,7 @@ struct Plan {
   int64_t units;  // B*H*nb
   int64_t C, Lc;  // state chunks per unit, tokens per chunk
   int64_t R, Lr;  // apply ranges per unit, tokens per range
+  int64_t Rb, Lb; // backward ranges per unit, tokens per range
   bool bf16;      // element type of q, k, v, g, out
   bool mfma;      // matrix-core kernels (bf16, d = 64 or 128)
   float theta, eps;
@@ -35,6 +36,9 @@ struct Plan {
   int64_t tab_t_off, tab_h_off, tab_w_off;  // entry offsets of the axis tables
   // workspace layout, byte offsets
   size_t off_tab, off_part, off_state, off_frag, total_bytes;
+  // the backward call's extra sections (after total_bytes): the per-range
+  // dS, dz partials and the suffix-summed gradients of the block states
+  size_t off_bpart, off_grad, bwd_total_bytes;
 };
 
 constexpr int kBlock = 256;          // threads per workgroup for every kernel
@@ -79,6 +83,14 @@ hipError_t launch_state_mfma(const Plan &p, const void *k, const void *v, const 
 hipError_t launch_apply_mfma(const Plan &p, const void *q, const void *g, const float *states,
                              const uint16_t *frags, const float2 *tab, const void *rms_w,
                              void *out, hipStream_t stream);
+
+// Gradients (vector kernels): with the forward states of the call in
+// `states`, writes dq, dk, dv, dg; `partials` holds units*Rb and `grads`
+// units state vectors of d*d + d floats.
+hipError_t launch_backward(const Plan &p, const void *q, const void *k, const void *v,
+                           const void *g, const void *dout, const float *states,
+                           const float2 *tab, float *partials, float *grads, void *dq, void *dk,
+                           void *dv, void *dg, hipStream_t stream);
 
 // Division by a fixed divisor d >= 1 for dividends 0 <= n < 2^31, by a
 // multiply-high and a shift: with s = ceil(log2 d) and

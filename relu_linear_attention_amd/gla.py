@@ -20,12 +20,13 @@ LIB_PATH = os.path.join(_HERE, "libgla.so")
 
 GLA_OK, GLA_ERR_INVALID_ARG, GLA_ERR_UNSUPPORTED, GLA_ERR_ALLOC, GLA_ERR_HIP = range(5)
 GLA_BF16, GLA_F32 = 0, 1
-GLA_NUM_STAGES = 4
+GLA_NUM_STAGES = 5
 
 # every symbol include/gla.h declares
 EXPORTS = (
     "gla_forward", "gla_block_causal_forward", "gla_workspace_bytes", "gla_forward_ws",
-    "gla_state", "gla_block_step", "gla_gated_forward", "gla_status_string", "gla_last_error", "gla_profile_enable",
+    "gla_state", "gla_block_step", "gla_gated_forward", "gla_backward",
+    "gla_backward_workspace_bytes", "gla_status_string", "gla_last_error", "gla_profile_enable",
     "gla_profile_read", "gla_stage_name", "gla_uses_matrix_cores",
 )
 
@@ -64,9 +65,14 @@ def load():
                                                                     ctypes.c_size_t, _vp])
     lib.gla_gated_forward.argtypes = ([_vp] * 7 + sizes6 + [_i64, _f, _f, _f, ctypes.c_int, _vp,
                                                             ctypes.c_size_t, _vp])
+    lib.gla_backward.argtypes = ([_vp] * 9 + sizes6 + [_i64, _f, _f, ctypes.c_int, _vp,
+                                                        ctypes.c_size_t, _vp])
+    lib.gla_backward_workspace_bytes.argtypes = sizes6 + [_i64, ctypes.c_int,
+                                                          ctypes.POINTER(ctypes.c_size_t)]
     for name in ("gla_forward", "gla_block_causal_forward", "gla_workspace_bytes",
                  "gla_forward_ws", "gla_state", "gla_block_step", "gla_gated_forward",
-                 "gla_profile_enable", "gla_profile_read"):
+                 "gla_backward", "gla_backward_workspace_bytes", "gla_profile_enable",
+                 "gla_profile_read"):
         getattr(lib, name).restype = ctypes.c_int
     lib.gla_status_string.argtypes = [ctypes.c_int]
     lib.gla_status_string.restype = ctypes.c_char_p
@@ -212,6 +218,26 @@ def gla_gated_forward(q, k, v, g, beta, rms_weight, out, grid, frames_per_block=
                                   rms_eps, _dtype_code(q), _ptr(workspace), ws_bytes,
                                   _stream_handle(stream))
     _check(st, "gla_gated_forward")
+
+
+def gla_backward(q, k, v, g, dout, dq, dk, dv, dg, grid, frames_per_block=0, rope_theta=10000.0,
+                 eps=1e-6, workspace=None, stream=None):
+    """Gradients dq, dk, dv, dg (written in place) of sum(dout * out)."""
+    _check_tensors(*[t for t in (q, k, v, g, dout, dq, dk, dv, dg, workspace) if t is not None])
+    B, H, T, Hs, Ws, d = _sizes(q, grid)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().gla_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(dout), _ptr(dq), _ptr(dk),
+                             _ptr(dv), _ptr(dg), B, H, T, Hs, Ws, d, frames_per_block, rope_theta,
+                             eps, _dtype_code(q), _ptr(workspace), ws_bytes,
+                             _stream_handle(stream))
+    _check(st, "gla_backward")
+
+
+def gla_backward_workspace_bytes(B, H, T, Hs, Ws, d, frames_per_block=0, dtype=GLA_BF16) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().gla_backward_workspace_bytes(B, H, T, Hs, Ws, d, frames_per_block, dtype,
+                                               ctypes.byref(n)), "gla_backward_workspace_bytes")
+    return n.value
 
 
 def gla_profile_enable(enable: bool = True):

@@ -153,6 +153,27 @@ def test_gated_forward_rejects_bad_arguments(lib, kw, needle):
     assert needle in gla.gla_last_error()
 
 
+def _bwd(lib, ins=(FAKE, FAKE * 3, FAKE * 5, FAKE * 7, FAKE * 9),
+         outs=(FAKE * 11, FAKE * 13, FAKE * 15, FAKE * 17), F=0, eps=1e-6, ws=None):
+    p = [ctypes.c_void_p(x) if x else None for x in ins + outs]
+    w = ctypes.c_void_p(ws) if ws else None
+    return lib.gla_backward(*p, 1, 2, 2, 4, 4, 32, F, 1e4, eps, gla.GLA_BF16, w, 1 << 20, None)
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(ins=(FAKE, FAKE * 3, FAKE * 5, FAKE * 7, 0)), "null tensor pointer (dout)"),
+    (dict(outs=(FAKE * 11, 0, FAKE * 15, FAKE * 17)), "null tensor pointer (dk)"),
+    (dict(outs=(FAKE * 11, FAKE * 13, FAKE * 15, FAKE * 9 + 64)), "dg overlaps input dout"),
+    (dict(outs=(FAKE * 11, FAKE * 11 + 64, FAKE * 15, FAKE * 17)), "dq overlaps dk"),
+    (dict(F=3), "divide"),
+    (dict(eps=-1.0), "eps"),
+    (dict(ws=FAKE * 19 + 8), "aligned"),
+])
+def test_backward_rejects_bad_arguments(lib, kw, needle):
+    assert _bwd(lib, **kw) == gla.GLA_ERR_INVALID_ARG
+    assert needle in gla.gla_last_error()
+
+
 def test_workspace_query_rejects_bad_sizes(lib):
     n = ctypes.c_size_t(0)
     assert lib.gla_workspace_bytes(1, 1, 3, 2, 2, 128, 2, 0, ctypes.byref(n)) == 1
@@ -174,6 +195,6 @@ def test_kernel_family_selection(lib):
 def test_profile_read_without_records(lib):
     gla.gla_profile_enable(True)
     rec = gla.gla_profile_read()
-    assert set(rec) == {"rope_table", "state_partials", "reduce_prefix", "apply"}
+    assert set(rec) == {"rope_table", "state_partials", "reduce_prefix", "apply", "backward"}
     assert all(v == (0, 0.0) for v in rec.values())
     gla.gla_profile_enable(False)

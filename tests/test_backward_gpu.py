@@ -1,0 +1,106 @@
+"""Parity of the gradients (gla_backward) with the fp64 oracle's, through the
+C ABI.  Gradients of the loss sum(dout * out); dout ~ N(0, 1), seeded.
+
+Bar: max |gpu - oracle| / (|oracle| + 1e-3 * max |oracle|) <= 1e-4 for fp32
+tensors and <= 1e-2 for bf16 tensors, per gradient tensor.  The floor is
+relative to the tensor's own scale because the four gradients differ in
+magnitude by orders (the forward's absolute floor of 1e-3 would hide all
+of dg at large N); bf16 gradients are rounded once to bf16 (2^-9)."""
+import numpy as np
+import pytest
+
+import oracle
+from relu_linear_attention_amd import gla
+from relu_linear_attention_amd.inputs import WORKLOADS, device_inputs_for, host_inputs
+from tests.gpu_util import TOL, have_gpu, to_device, to_host_f32
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
+
+
+def grad_err(got, ref) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    floor = 1e-3 * float(np.max(np.abs(ref)))
+    return float(np.max(np.abs(got - ref) / (np.abs(ref) + floor)))
+
+
+def _run(dev, dout, grid, F, workspace=None):
+    import torch
+
+    outs = [torch.empty_like(dev["q"]) for _ in range(4)]
+    gla.gla_backward(dev["q"], dev["k"], dev["v"], dev["g"], dout, *outs, grid, F,
+                     workspace=workspace)
+    torch.cuda.synchronize()
+    return outs
+
+
+def _dout(shape, dtype, seed):
+    from relu_linear_attention_amd.inputs import round_to_bf16
+
+    x = np.random.default_rng(seed).standard_normal(shape).astype(np.float32)
+    return round_to_bf16(x) if dtype == "bf16" else x
+
+
+# name, B, T, Hs, Ws, H, d, dtype, F
+CASES = [
+    ("f32_d32", 1, 2, 4, 5, 2, 32, "f32", 0),
+    ("f32_d64_blocks", 1, 4, 3, 5, 2, 64, "f32", 1),
+    ("bf16_d128", 1, 3, 5, 7, 2, 128, "bf16", 0),
+    ("bf16_d128_blocks_batch2", 2, 4, 4, 5, 2, 128, "bf16", 2),
+    ("bf16_d64", 1, 4, 6, 5, 3, 64, "bf16", 0),
+    ("bf16_d112", 1, 2, 5, 5, 2, 112, "bf16", 1),
+    ("f32_d16_ragged", 1, 3, 7, 5, 1, 16, "f32", 0),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_backward_matches_oracle(case):
+    name, B, T, Hs, Ws, H, d, dtype, F = case
+    print(f"case {name}: B={B} grid={T}x{Hs}x{Ws} H={H} d={d} {dtype} F={F}", flush=True)
+    x = host_inputs(B, T, Hs, Ws, H, d, dtype, seed=400 + len(name))
+    dout = _dout(x["q"].shape, dtype, seed=401)
+    dev = to_device(x, dtype)
+    ddev = to_device({"o": dout}, dtype)["o"]
+    got = _run(dev, ddev, (T, Hs, Ws), F)
+    ref = oracle.backward(x["q"], x["k"], x["v"], x["g"], dout, (T, Hs, Ws), F)
+    for gname, a, r in zip(("dq", "dk", "dv", "dg"), got, ref):
+        err = grad_err(to_host_f32(a), r)
+        print(f"  {gname}: err {err:.3e}", flush=True)
+        assert err <= TOL[dtype], gname
+
+
+def test_backward_is_deterministic_and_workspace_matches():
+    import torch
+
+    B, T, Hs, Ws, H, d, F = 1, 4, 5, 6, 2, 128, 2
+    x = host_inputs(B, T, Hs, Ws, H, d, "bf16", seed=41)
+    dev = to_device(x, "bf16")
+    ddev = to_device({"o": _dout(x["q"].shape, "bf16", 42)}, "bf16")["o"]
+    a = _run(dev, ddev, (T, Hs, Ws), F)
+    b = _run(dev, ddev, (T, Hs, Ws), F)
+    nbytes = gla.gla_backward_workspace_bytes(B, H, T, Hs, Ws, d, F, gla.GLA_BF16)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    c = _run(dev, ddev, (T, Hs, Ws), F, workspace=ws)
+    for u, v_, w in zip(a, b, c):
+        assert torch.equal(u.view(torch.int16), v_.view(torch.int16))
+        assert torch.equal(u.view(torch.int16), w.view(torch.int16))
+
+
+@pytest.mark.slow
+def test_full_size_backward_480p():
+    import torch
+
+    w = WORKLOADS["480p_81f"]
+    print(f"workload {w.name} backward: grid {w.T}x{w.Hs}x{w.Ws} H={w.H}", flush=True)
+    dev = device_inputs_for(w)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed + 7)
+    dout = torch.randn(dev["q"].shape, generator=gen, device="cuda").to(torch.bfloat16)
+    got = _run(dev, dout, w.grid, 0)
+    host = {n: t.float().cpu().numpy() for n, t in dev.items()}
+    ref = oracle.backward(host["q"], host["k"], host["v"], host["g"], dout.float().cpu().numpy(),
+                          w.grid, 0)
+    for gname, a, r in zip(("dq", "dk", "dv", "dg"), got, ref):
+        err = grad_err(a.float().cpu().numpy(), r)
+        print(f"  {gname}: err {err:.3e}", flush=True)
+        assert err <= TOL["bf16"], gname
