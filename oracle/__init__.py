@@ -5,13 +5,16 @@ CPU-baseline leg of ``bench.py`` are the only callers.  The product path (the
 HIP library and its binding) never imports this package.
 
 This module compiles ``oracle.c`` with gcc into ``liboracle.so`` and wraps its
-four entry points with numpy marshalling:
+entry points with numpy marshalling:
 
 * :func:`rope`    - 3D rotary embedding of one vector at a (t, h, w) position
 * :func:`state`   - S = sum_n RoPE(phi(k_n))^T v_n and z = sum_n phi(k_n),
                     per (batch, head), inclusive per temporal block
 * :func:`apply`   - out_i = (RoPE(phi(q_i)) S) / (phi(q_i).z + eps) * sigmoid(g_i)
 * :func:`forward` - state followed by apply over every token
+* :func:`block_step`, :func:`gated_forward`, :func:`backward`,
+  :func:`token_causal` - the streaming step, the gated mixer, the gradients
+  and the token-causal form
 
 The formulas follow "SANA-Video 2.0" (arXiv 2607.21553) Section 2, Eq. (1)
 (gate, +eps) and the SANA-Video notes page, Section 3.2 (ReLU feature map,
@@ -66,6 +69,8 @@ def _load():
     lib.ora_gated_forward.restype = ctypes.c_int
     lib.ora_backward.argtypes = [_ptr] * 5 + [_i64] * 7 + [_dbl, _dbl] + [_ptr] * 4
     lib.ora_backward.restype = ctypes.c_int
+    lib.ora_token_causal.argtypes = [_ptr] * 4 + [_i64] * 6 + [_dbl, _dbl, _ptr]
+    lib.ora_token_causal.restype = ctypes.c_int
     lib.ora_num_blocks.argtypes = [_i64, _i64]
     lib.ora_num_blocks.restype = _i64
     lib.ora_num_threads.argtypes = []
@@ -216,3 +221,16 @@ def backward(q, k, v, g, dout, grid, frames_per_block: int = 0, theta: float = 1
                               frames_per_block, float(theta), float(eps), *[_p(o) for o in outs])
     _check(rc, "backward")
     return tuple(outs)
+
+
+def token_causal(q, k, v, g, grid, theta: float = 10000.0, eps: float = 1e-6) -> np.ndarray:
+    """Token-causal form: token i attends to tokens 0..i through running sums.
+    q, k, v, g: [B, N, H, d].  Returns out [B, N, H, d] (fp64)."""
+    q, k, v, g = _f32(q), _f32(k), _f32(v), _f32(g)
+    B, N, H, d = q.shape
+    T, Hs, Ws = grid
+    out = np.empty((B, N, H, d), dtype=np.float64)
+    rc = _load().ora_token_causal(_p(q), _p(k), _p(v), _p(g), B, H, T, Hs, Ws, d, float(theta),
+                                  float(eps), _p(out))
+    _check(rc, "token_causal")
+    return out

@@ -495,6 +495,84 @@ int ora_block_step(const float *q, const float *k, const float *v, const float *
   return rc;
 }
 
+/* Token-causal form ([V1c], the causal linear-attention output of token i
+ * derived there for the KV cache): token i attends to tokens 0..i, itself
+ * included, through the running sums of the states and of phi(k):
+ *   S_i = sum_{j<=i} RoPE_j(phi(k_j))^T v_j,   z_i = sum_{j<=i} phi(k_j)
+ *   out_i = RoPE_i(phi(q_i)) S_i / (phi(q_i).z_i + eps) * sigma(g_i)
+ * with the same RoPE, eps and gate readings as the other forms.  One pass per
+ * (batch, head) in increasing token order: token n is added to the sums,
+ * then read them.  out : [B, N, H, d] double. */
+
+/* S += RoPE_n(phi(k_n))^T v_n and z += phi(k_n) for the row at k + row, v + row. */
+static void causal_add(const float *k, const float *v, int64_t row, int64_t d,
+                       const int64_t pos[3], double theta, double *phik, double *rotk, double *S,
+                       double *z) {
+  for (int64_t p = 0; p < d; ++p) {
+    double x = (double)k[row + p];
+    phik[p] = x > 0.0 ? x : 0.0;
+  }
+  ora_rope(phik, rotk, d, pos, theta);
+  for (int64_t p = 0; p < d; ++p) {
+    z[p] += phik[p];
+    for (int64_t e = 0; e < d; ++e) S[p * d + e] += rotk[p] * (double)v[row + e];
+  }
+}
+
+/* out_n from the current sums. */
+static void causal_read(const float *q, const float *g, int64_t row, int64_t d,
+                        const int64_t pos[3], double theta, double eps, double *phiq,
+                        double *rotq, const double *S, const double *z, double *out) {
+  for (int64_t p = 0; p < d; ++p) {
+    double x = (double)q[row + p];
+    phiq[p] = x > 0.0 ? x : 0.0;
+  }
+  ora_rope(phiq, rotq, d, pos, theta);
+  double den = 0.0;
+  for (int64_t p = 0; p < d; ++p) den += phiq[p] * z[p];
+  den += eps;
+  for (int64_t e = 0; e < d; ++e) {
+    double num = 0.0;
+    for (int64_t p = 0; p < d; ++p) num += rotq[p] * S[p * d + e];
+    out[row + e] = num / den / (1.0 + exp(-(double)g[row + e]));
+  }
+}
+
+int ora_token_causal(const float *q, const float *k, const float *v, const float *g, int64_t B,
+                     int64_t H, int64_t T, int64_t Hs, int64_t Ws, int64_t d, double theta,
+                     double eps, double *out) {
+  if (!q || !k || !v || !g || !out) return ORA_BAD_ARG;
+  int rc = check_shape(B, H, T, Hs, Ws, d, 0);
+  if (rc) return rc;
+  const int64_t N = T * Hs * Ws;
+  int failed = 0;
+
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  for (int64_t b = 0; b < B; ++b) {
+    for (int64_t h = 0; h < H; ++h) {
+      double *S = (double *)calloc((size_t)(d * d), sizeof(double));
+      double *z = (double *)calloc((size_t)d, sizeof(double));
+      double *tmp = (double *)malloc((size_t)(4 * d) * sizeof(double));
+      if (!S || !z || !tmp) {
+#pragma omp atomic write
+        failed = 1;
+      } else {
+        for (int64_t n = 0; n < N; ++n) {
+          const int64_t row = ((b * N + n) * H + h) * d;
+          int64_t pos[3];
+          grid_position(n, Hs, Ws, NULL, pos);
+          causal_add(k, v, row, d, pos, theta, tmp, tmp + d, S, z);
+          causal_read(q, g, row, d, pos, theta, eps, tmp + 2 * d, tmp + 3 * d, S, z, out);
+        }
+      }
+      free(S);
+      free(z);
+      free(tmp);
+    }
+  }
+  return failed ? ORA_NO_MEM : ORA_OK;
+}
+
 /* Number of threads OpenMP will use (reported by the benchmark's CPU leg). */
 int ora_num_threads(void) {
   int n = 1;

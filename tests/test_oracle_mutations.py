@@ -59,6 +59,19 @@ MUTATIONS = [
      "ora_rope(t1, t2, d, pos, theta); /* back through the rotation */"),
     ("backward_relu_mask_dropped_on_k", "dk[row + p] = (double)k[row + p] > 0.0 ? t2[p] + Gz[p] : 0.0;",
      "dk[row + p] = t2[p] + Gz[p];"),
+    ("token_causal_normaliser_rotated", "z[p] += phik[p];", "z[p] += rotk[p];"),
+    ("token_causal_state_transposed", "num += rotq[p] * S[p * d + e];",
+     "num += rotq[p] * S[e * d + p];"),
+    ("token_causal_relu_dropped_on_k",
+     "phik[p] = x > 0.0 ? x : 0.0;\n  }\n  ora_rope(phik, rotk, d, pos, theta);",
+     "phik[p] = x;\n  }\n  ora_rope(phik, rotk, d, pos, theta);"),
+    ("token_causal_gate_sign", "out[row + e] = num / den / (1.0 + exp(-(double)g[row + e]));",
+     "out[row + e] = num / den / (1.0 + exp((double)g[row + e]));"),
+    ("token_causal_strict_no_diagonal",
+     "causal_add(k, v, row, d, pos, theta, tmp, tmp + d, S, z);\n"
+     "          causal_read(q, g, row, d, pos, theta, eps, tmp + 2 * d, tmp + 3 * d, S, z, out);",
+     "causal_read(q, g, row, d, pos, theta, eps, tmp + 2 * d, tmp + 3 * d, S, z, out);\n"
+     "          causal_add(k, v, row, d, pos, theta, tmp, tmp + d, S, z);"),
     ("block_step_offset_ignored", "const int64_t pos0[3] = {t_offset, 0, 0};",
      "const int64_t pos0[3] = {0, 0, 0};"),
 ]

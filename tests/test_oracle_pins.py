@@ -659,3 +659,85 @@ def test_backward_euler_identities():
         assert abs(np.sum(dv * x["v"]) - L) <= 1e-10 * np.sum(np.abs(dv * x["v"]))
         assert abs(np.sum(dq * x["q"])) <= 1e-10 * np.sum(np.abs(dq * x["q"]))
         assert abs(np.sum(dk * x["k"])) <= 1e-10 * np.sum(np.abs(dk * x["k"]))
+
+
+# ---------------------------------------------------------------------------
+# token-causal form ("SANA-Video" notes page, Section 3.4, the causal output
+# of token i): token i attends to tokens 0..i
+# ---------------------------------------------------------------------------
+def brute_force_token_causal(q, k, v, g, grid, theta=10000.0, eps=1e-6):
+    """The pairwise form restricted to j <= i (a lower-triangular mask)."""
+    B, N, H, d = q.shape
+    pos = _positions(*grid)
+    allowed = np.tril(np.ones((N, N), dtype=bool))
+    out = np.empty((B, N, H, d))
+    for b in range(B):
+        for h in range(H):
+            pq = np.maximum(q[b, :, h].astype(np.float64), 0.0)
+            pk = np.maximum(k[b, :, h].astype(np.float64), 0.0)
+            rq, rk = _rope_complex(pq, pos, theta), _rope_complex(pk, pos, theta)
+            num = ((rq @ rk.T) * allowed) @ v[b, :, h].astype(np.float64)
+            den = ((pq @ pk.T) * allowed).sum(1) + eps
+            out[b, :, h] = num / den[:, None] / (1.0 + np.exp(-g[b, :, h].astype(np.float64)))
+    return out
+
+
+@pytest.mark.parametrize("B,T,Hs,Ws,H,d,theta", [
+    (1, 2, 3, 4, 2, 16, 10000.0),
+    (2, 3, 2, 3, 1, 32, 50.0),
+    (1, 1, 5, 7, 2, 64, 3.0),
+    (1, 4, 2, 2, 1, 16, 0.0),
+])
+def test_token_causal_matches_brute_force(B, T, Hs, Ws, H, d, theta):
+    x = host_inputs(B, T, Hs, Ws, H, d, "bf16", seed=61 + d)
+    got = oracle.token_causal(x["q"], x["k"], x["v"], x["g"], (T, Hs, Ws), theta)
+    ref = brute_force_token_causal(x["q"], x["k"], x["v"], x["g"], (T, Hs, Ws), theta)
+    assert _rel_err(got, ref, floor=1e-12) <= 1e-10
+
+
+def test_token_causal_one_token_frames_is_block_causal():
+    # with one token per latent frame (Hs = Ws = 1) and blocks of one frame,
+    # the block-causal form is the token-causal one
+    x = host_inputs(1, 9, 1, 1, 2, 32, "bf16", seed=62)
+    got = oracle.token_causal(x["q"], x["k"], x["v"], x["g"], (9, 1, 1))
+    ref = oracle.forward(x["q"], x["k"], x["v"], x["g"], (9, 1, 1), 1)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_token_causal_last_token_is_noncausal():
+    x = host_inputs(1, 3, 3, 4, 2, 32, "bf16", seed=63)
+    got = oracle.token_causal(x["q"], x["k"], x["v"], x["g"], (3, 3, 4))
+    ref = oracle.forward(x["q"], x["k"], x["v"], x["g"], (3, 3, 4))
+    np.testing.assert_allclose(got[:, -1], ref[:, -1], rtol=1e-12, atol=1e-14)
+    assert not np.allclose(got[:, 0], ref[:, 0])
+
+
+def test_token_causal_first_token_closed_form():
+    # token 0 sees only itself: RoPE cancels, out = v sigma(g) s / (s + eps)
+    x = host_inputs(1, 2, 2, 2, 1, 16, "f32", seed=64)
+    x["q"][0, 0, 0, :4] = np.abs(x["q"][0, 0, 0, :4]) + 0.5  # s > 0
+    x["k"][0, 0, 0, :4] = np.abs(x["k"][0, 0, 0, :4]) + 0.5
+    out = oracle.token_causal(x["q"], x["k"], x["v"], x["g"], (2, 2, 2), eps=0.25)[0, 0, 0]
+    pq = np.maximum(x["q"][0, 0, 0].astype(np.float64), 0)
+    pk = np.maximum(x["k"][0, 0, 0].astype(np.float64), 0)
+    s = float(pq @ pk)
+    gate = 1.0 / (1.0 + np.exp(-x["g"][0, 0, 0].astype(np.float64)))
+    np.testing.assert_allclose(out, x["v"][0, 0, 0] * gate * s / (s + 0.25), rtol=1e-13)
+
+
+def test_token_causal_ignores_the_future():
+    grid = (2, 3, 3)
+    x = host_inputs(1, *grid, 2, 32, "bf16", seed=65)
+    base = oracle.token_causal(x["q"], x["k"], x["v"], x["g"], grid)
+    m = 7
+    for name in "kv":
+        y = {n: a.copy() for n, a in x.items()}
+        y[name][:, m + 1:] = np.random.default_rng(66).standard_normal(y[name][:, m + 1:].shape)
+        got = oracle.token_causal(y["q"], y["k"], y["v"], y["g"], grid)
+        assert np.array_equal(got[:, :m + 1], base[:, :m + 1])
+        assert not np.allclose(got[:, m + 1:], base[:, m + 1:])
+    # and token m's own key enters its output
+    y = {n: a.copy() for n, a in x.items()}
+    y["v"][:, m] += 1.0
+    got = oracle.token_causal(y["q"], y["k"], y["v"], y["g"], grid)
+    assert np.array_equal(got[:, :m], base[:, :m]) and not np.allclose(got[:, m], base[:, m])
