@@ -206,6 +206,34 @@ gla_status gla_backward_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t
                                         int64_t d, int64_t frames_per_block, gla_dtype dtype,
                                         size_t *bytes);
 
+/*
+ * Token-causal form ("SANA-Video" notes page, Section 3.4: the causal
+ * linear-attention output of token i, the form behind the constant-memory
+ * cache): token i of a (batch, head) attends to tokens 0..i of the t-major
+ * flattened grid, itself included:
+ *   S_i = sum_{j<=i} RoPE_j(phi(k_j))^T v_j,   z_i = sum_{j<=i} phi(k_j)
+ *   out_i = (RoPE_i(phi(q_i)) S_i) / (phi(q_i) . z_i + eps) * sigmoid(g_i)
+ * with the RoPE, eps and gate of gla_forward.  Tensors, layout, dtype,
+ * alignment, ownership and errors as gla_forward.  Computed chunkwise: a
+ * state stage over chunks of tokens, an exclusive prefix over the chunks,
+ * then per range of tokens a tile kernel that adds each tile's own
+ * (lower-triangular) part to the carried sums; the result does not depend on
+ * the decomposition beyond rounding.
+ * workspace: NULL (taken stream-ordered on `stream`) or at least
+ * gla_token_causal_workspace_bytes() bytes of device memory, 256-byte
+ * aligned (then nothing is allocated).
+ */
+gla_status gla_token_causal_forward(const void *q, const void *k, const void *v, const void *g,
+                                    void *out, int64_t B, int64_t H, int64_t T, int64_t Hs,
+                                    int64_t Ws, int64_t d, float rope_theta, float eps,
+                                    gla_dtype dtype, void *workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
+/* Workspace of gla_token_causal_forward with these sizes on the current device. */
+gla_status gla_token_causal_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t Hs,
+                                            int64_t Ws, int64_t d, gla_dtype dtype,
+                                            size_t *bytes);
+
 /* Static description of a status code. */
 const char *gla_status_string(gla_status status);
 
@@ -217,10 +245,11 @@ const char *gla_last_error(void);
  * by HIP events recorded on the launch stream.  gla_profile_read() waits for
  * the recorded events and returns, per stage, the number of launches and
  * their summed duration in milliseconds.  Stages: 0 rope table, 1 state
- * partials, 2 reduce/prefix, 3 apply, 4 gradient kernels (gla_backward).  Enabling (or disabling) clears the
- * record.  Meant for one thread at a time.
+ * partials, 2 reduce/prefix, 3 apply, 4 gradient kernels (gla_backward),
+ * 5 token-causal tile kernel (gla_token_causal_forward).  Enabling (or
+ * disabling) clears the record.  Meant for one thread at a time.
  */
-#define GLA_NUM_STAGES 5
+#define GLA_NUM_STAGES 6
 gla_status gla_profile_enable(int enable);
 gla_status gla_profile_read(int64_t launches[GLA_NUM_STAGES], double total_ms[GLA_NUM_STAGES]);
 const char *gla_stage_name(int stage);

@@ -294,6 +294,41 @@ gla_status make_plan(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, in
   return GLA_OK;
 }
 
+// Token-causal plan: one unit per (batch, head) over all N tokens.  The
+// tile kernel holds one workgroup per compute unit and walks a range of Lr
+// tokens; ranges are whole multiples of the state chunks (Lr = m * Lc), so
+// the prefix at a range start is a sum of whole chunk partials.  Workspace:
+// the table, the chunk partials, and the range prefixes [units][R][d*d + d].
+gla_status make_causal_plan(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, int64_t d,
+                            gla_dtype dtype, float theta, float eps, int cus, bool aligned16,
+                            Plan *p) {
+  Plan P;
+  gla_status st = make_plan(B, H, T, Hs, Ws, d, 0, dtype, theta, eps, cus, aligned16, &P);
+  if (st != GLA_OK) return st;
+  P.mfma = false;  // vector tile kernel
+  const int64_t tile = 16;
+  int64_t Lr = round_up(ceil_div(P.N, pick_pieces(P.units, P.N, tile, 256, cus)), tile);
+  Lr = std::min(Lr, round_up(P.N, tile));
+  P.Lr = Lr;
+  P.R = ceil_div(P.N, Lr);
+  P.Lc = Lr;  // m = 1
+  P.C = P.R;
+  if (P.units * P.C > 0x7fffffff)
+    return fail(GLA_ERR_UNSUPPORTED, "too many (batch, head, range) units for one launch");
+  size_t off = 0;
+  P.off_tab = off;
+  off = align256(off + (size_t)P.tab_entries * sizeof(float2));
+  P.off_part = off;
+  off = align256(off + (size_t)P.units * P.C * gla::kPartialStride(d) * sizeof(float));
+  P.off_state = off;
+  off = align256(off + (size_t)P.units * P.R * gla::kPartialStride(d) * sizeof(float));
+  P.off_frag = off;
+  P.total_bytes = off;
+  P.off_bpart = P.off_grad = P.bwd_total_bytes = off;
+  *p = P;
+  return GLA_OK;
+}
+
 // ---------------------------------------------------------------- profiling
 struct StageRecord {
   int stage;
@@ -304,7 +339,7 @@ bool g_prof_on = false;
 std::vector<StageRecord> g_prof;
 
 const char *kStageNames[GLA_NUM_STAGES] = {"rope_table", "state_partials", "reduce_prefix",
-                                           "apply", "backward"};
+                                           "apply", "backward", "causal_apply"};
 
 void prof_clear_locked() {
   for (auto &r : g_prof) {
@@ -408,6 +443,29 @@ gla_status run_plan(const Plan &P, const void *q, const void *k, const void *v, 
   return timed_launch(3, stream, "apply kernel", [&] {
     return P.mfma ? gla::launch_apply_mfma(P, q, g, states, frags, tab, gates.rms_w, out, stream)
                   : gla::launch_apply_generic(P, q, g, states, tab, gates.rms_w, out, stream);
+  });
+}
+
+// Token-causal call: table, chunk partials, range prefixes, tile kernel.
+gla_status run_causal(const Plan &P, const void *q, const void *k, const void *v, const void *g,
+                      void *out, void *ws, hipStream_t stream) {
+  char *base = (char *)ws;
+  float2 *tab = (float2 *)(base + P.off_tab);
+  float *part = (float *)(base + P.off_part);
+  float *states = (float *)(base + P.off_state);
+  gla_status st = timed_launch(0, stream, "rope table kernel",
+                               [&] { return gla::launch_rope_table(P, tab, stream); });
+  if (st != GLA_OK) return st;
+  st = timed_launch(1, stream, "state kernel", [&] {
+    return P.mfma ? gla::launch_state_mfma(P, k, v, nullptr, tab, part, stream)
+                  : gla::launch_state_generic(P, k, v, nullptr, tab, part, stream);
+  });
+  if (st != GLA_OK) return st;
+  st = timed_launch(2, stream, "range prefix kernel",
+                    [&] { return gla::launch_range_prefix(P, part, states, stream); });
+  if (st != GLA_OK) return st;
+  return timed_launch(5, stream, "causal tile kernel", [&] {
+    return gla::launch_causal_generic(P, q, k, v, g, states, tab, out, stream);
   });
 }
 
@@ -668,6 +726,67 @@ gla_status gla_backward(const void *q, const void *k, const void *v, const void 
     if (st == GLA_OK && e != hipSuccess) return hip_fail(e, "hipFreeAsync");
   }
   return st;
+}
+
+gla_status gla_token_causal_forward(const void *q, const void *k, const void *v, const void *g,
+                                    void *out, int64_t B, int64_t H, int64_t T, int64_t Hs,
+                                    int64_t Ws, int64_t d, float rope_theta, float eps,
+                                    gla_dtype dtype, void *workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  g_last_error[0] = '\0';
+  gla_status st = check_sizes(B, H, T, Hs, Ws, d, 0, dtype);
+  if (st != GLA_OK) return st;
+  if (!std::isfinite(rope_theta)) return fail(GLA_ERR_INVALID_ARG, "rope_theta must be finite");
+  if (!std::isfinite(eps) || eps < 0.f)
+    return fail(GLA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  const size_t bytes = (size_t)(B * T * Hs * Ws * H * d) * (dtype == GLA_BF16 ? 2 : 4);
+  st = check_pointers(q, k, v, g, out, bytes);
+  if (st != GLA_OK) return st;
+  if (workspace != nullptr && ((uintptr_t)workspace & 255) != 0)
+    return fail(GLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  int cus = 0;
+  st = device_cus(&cus);
+  if (st != GLA_OK) return st;
+  const bool aligned16 = (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)g |
+                          (uintptr_t)out) & 15) == 0;
+  Plan P;
+  st = make_causal_plan(B, H, T, Hs, Ws, d, dtype, rope_theta, eps, cus, aligned16, &P);
+  if (st != GLA_OK) return st;
+  if (workspace != nullptr) {
+    if (workspace_bytes < P.total_bytes)
+      return fail(GLA_ERR_INVALID_ARG, "workspace too small: %zu bytes given, %zu needed",
+                  workspace_bytes, P.total_bytes);
+    return run_causal(P, q, k, v, g, out, workspace, stream);
+  }
+  void *mem = nullptr;
+  hipError_t e = hipMallocAsync(&mem, P.total_bytes, stream);
+  if (e != hipSuccess || mem == nullptr) {
+    (void)hipGetLastError();
+    return fail(GLA_ERR_ALLOC, "hipMallocAsync of %zu workspace bytes failed", P.total_bytes);
+  }
+  st = run_causal(P, q, k, v, g, out, mem, stream);
+  e = hipFreeAsync(mem, stream);
+  if (st == GLA_OK && e != hipSuccess) return hip_fail(e, "hipFreeAsync");
+  return st;
+}
+
+gla_status gla_token_causal_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t Hs,
+                                            int64_t Ws, int64_t d, gla_dtype dtype,
+                                            size_t *bytes) {
+  g_last_error[0] = '\0';
+  if (!bytes) return fail(GLA_ERR_INVALID_ARG, "bytes must not be null");
+  gla_status st = check_sizes(B, H, T, Hs, Ws, d, 0, dtype);
+  if (st != GLA_OK) return st;
+  int cus = 0;
+  st = device_cus(&cus);
+  if (st != GLA_OK) return st;
+  Plan P, Pv;
+  st = make_causal_plan(B, H, T, Hs, Ws, d, dtype, 10000.f, 0.f, cus, true, &P);
+  if (st != GLA_OK) return st;
+  st = make_causal_plan(B, H, T, Hs, Ws, d, dtype, 10000.f, 0.f, cus, false, &Pv);
+  if (st != GLA_OK) return st;
+  *bytes = std::max(P.total_bytes, Pv.total_bytes);
+  return GLA_OK;
 }
 
 gla_status gla_backward_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws,

@@ -84,6 +84,16 @@ hipError_t launch_apply_mfma(const Plan &p, const void *q, const void *g, const 
                              const uint16_t *frags, const float2 *tab, const void *rms_w,
                              void *out, hipStream_t stream);
 
+// Token-causal form.  The state stage writes one partial per chunk of Lc
+// tokens (units = B*H, one block each); the prefix kernel writes, for every
+// range of Lr = m*Lc tokens, the exclusive sum of the partials before it
+// ([units][R][d*d + d]); the tile kernels walk each range from that sum.
+hipError_t launch_range_prefix(const Plan &p, const float *partials, float *states,
+                               hipStream_t stream);
+hipError_t launch_causal_generic(const Plan &p, const void *q, const void *k, const void *v,
+                                 const void *g, const float *states, const float2 *tab, void *out,
+                                 hipStream_t stream);
+
 // Gradients (vector kernels): with the forward states of the call in
 // `states`, writes dq, dk, dv, dg; `partials` holds units*Rb and `grads`
 // units state vectors of d*d + d floats.

@@ -20,13 +20,14 @@ LIB_PATH = os.path.join(_HERE, "libgla.so")
 
 GLA_OK, GLA_ERR_INVALID_ARG, GLA_ERR_UNSUPPORTED, GLA_ERR_ALLOC, GLA_ERR_HIP = range(5)
 GLA_BF16, GLA_F32 = 0, 1
-GLA_NUM_STAGES = 5
+GLA_NUM_STAGES = 6
 
 # every symbol include/gla.h declares
 EXPORTS = (
     "gla_forward", "gla_block_causal_forward", "gla_workspace_bytes", "gla_forward_ws",
     "gla_state", "gla_block_step", "gla_gated_forward", "gla_backward",
-    "gla_backward_workspace_bytes", "gla_status_string", "gla_last_error", "gla_profile_enable",
+    "gla_backward_workspace_bytes", "gla_token_causal_forward", "gla_token_causal_workspace_bytes",
+    "gla_status_string", "gla_last_error", "gla_profile_enable",
     "gla_profile_read", "gla_stage_name", "gla_uses_matrix_cores",
 )
 
@@ -69,9 +70,14 @@ def load():
                                                         ctypes.c_size_t, _vp])
     lib.gla_backward_workspace_bytes.argtypes = sizes6 + [_i64, ctypes.c_int,
                                                           ctypes.POINTER(ctypes.c_size_t)]
+    lib.gla_token_causal_forward.argtypes = (tensors5 + sizes6 + [_f, _f, ctypes.c_int, _vp,
+                                                                  ctypes.c_size_t, _vp])
+    lib.gla_token_causal_workspace_bytes.argtypes = sizes6 + [ctypes.c_int,
+                                                              ctypes.POINTER(ctypes.c_size_t)]
     for name in ("gla_forward", "gla_block_causal_forward", "gla_workspace_bytes",
                  "gla_forward_ws", "gla_state", "gla_block_step", "gla_gated_forward",
-                 "gla_backward", "gla_backward_workspace_bytes", "gla_profile_enable",
+                 "gla_backward", "gla_backward_workspace_bytes", "gla_token_causal_forward",
+                 "gla_token_causal_workspace_bytes", "gla_profile_enable",
                  "gla_profile_read"):
         getattr(lib, name).restype = ctypes.c_int
     lib.gla_status_string.argtypes = [ctypes.c_int]
@@ -237,6 +243,25 @@ def gla_backward_workspace_bytes(B, H, T, Hs, Ws, d, frames_per_block=0, dtype=G
     n = ctypes.c_size_t(0)
     _check(load().gla_backward_workspace_bytes(B, H, T, Hs, Ws, d, frames_per_block, dtype,
                                                ctypes.byref(n)), "gla_backward_workspace_bytes")
+    return n.value
+
+
+def gla_token_causal_forward(q, k, v, g, out, grid, rope_theta=10000.0, eps=1e-6, workspace=None,
+                             stream=None):
+    """Token-causal form: token i attends to tokens 0..i (out written in place)."""
+    _check_tensors(*[t for t in (q, k, v, g, out, workspace) if t is not None])
+    B, H, T, Hs, Ws, d = _sizes(q, grid)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().gla_token_causal_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(out), B, H, T,
+                                         Hs, Ws, d, rope_theta, eps, _dtype_code(q),
+                                         _ptr(workspace), ws_bytes, _stream_handle(stream))
+    _check(st, "gla_token_causal_forward")
+
+
+def gla_token_causal_workspace_bytes(B, H, T, Hs, Ws, d, dtype=GLA_BF16) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().gla_token_causal_workspace_bytes(B, H, T, Hs, Ws, d, dtype, ctypes.byref(n)),
+           "gla_token_causal_workspace_bytes")
     return n.value
 
 

@@ -174,6 +174,27 @@ def test_backward_rejects_bad_arguments(lib, kw, needle):
     assert needle in gla.gla_last_error()
 
 
+def _causal(lib, ts=(FAKE, FAKE * 3, FAKE * 5, FAKE * 7, FAKE * 9), d=32, eps=1e-6, theta=1e4,
+            ws=None):
+    p = [ctypes.c_void_p(x) if x else None for x in ts]
+    w = ctypes.c_void_p(ws) if ws else None
+    return lib.gla_token_causal_forward(*p, 1, 2, 2, 4, 4, d, theta, eps, gla.GLA_BF16, w, 1 << 20,
+                                        None)
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(ts=(FAKE, 0, FAKE * 5, FAKE * 7, FAKE * 9)), "null tensor pointer"),
+    (dict(ts=(FAKE, FAKE * 3, FAKE * 5, FAKE * 7, FAKE * 5 + 32)), "out overlaps input v"),
+    (dict(d=40), "multiple of 16"),
+    (dict(eps=float("nan")), "eps"),
+    (dict(theta=float("inf")), "rope_theta"),
+    (dict(ws=FAKE * 19 + 8), "aligned"),
+])
+def test_token_causal_rejects_bad_arguments(lib, kw, needle):
+    assert _causal(lib, **kw) == gla.GLA_ERR_INVALID_ARG
+    assert needle in gla.gla_last_error()
+
+
 def test_workspace_query_rejects_bad_sizes(lib):
     n = ctypes.c_size_t(0)
     assert lib.gla_workspace_bytes(1, 1, 3, 2, 2, 128, 2, 0, ctypes.byref(n)) == 1
@@ -195,6 +216,7 @@ def test_kernel_family_selection(lib):
 def test_profile_read_without_records(lib):
     gla.gla_profile_enable(True)
     rec = gla.gla_profile_read()
-    assert set(rec) == {"rope_table", "state_partials", "reduce_prefix", "apply", "backward"}
+    assert set(rec) == {"rope_table", "state_partials", "reduce_prefix", "apply", "backward",
+                        "causal_apply"}
     assert all(v == (0, 0.0) for v in rec.values())
     gla.gla_profile_enable(False)

@@ -196,4 +196,4 @@ def test_stage_timing_records_every_launch():
     # one launch per forward stage and call; a forward call runs no gradient kernels
     assert all(rec[s][0] == 3 and rec[s][1] > 0
                for s in ("rope_table", "state_partials", "reduce_prefix", "apply")), rec
-    assert rec["backward"][0] == 0, rec
+    assert rec["backward"][0] == 0 and rec["causal_apply"][0] == 0, rec
