@@ -27,6 +27,7 @@ if ROOT not in sys.path:
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
 DEFAULT_WORKLOAD = "720p_81f"
 MFMA_SOURCES = ("relu_linear_attention_amd/csrc/gla_mfma.hip",
+                "relu_linear_attention_amd/csrc/gla_mfma_common.h",
                 "relu_linear_attention_amd/csrc/gla_common.hip")
 
 

@@ -25,7 +25,7 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 SOURCES = ["gla_common.hip", "gla_vector.hip", "gla_mfma.hip", "gla_backward.hip", "gla_causal.hip",
-           "gla_api.cpp"]
+           "gla_causal_mfma.hip",            "gla_api.cpp"]
 
 
 def _compile(src: str) -> str:

@@ -295,24 +295,54 @@ gla_status make_plan(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, in
 }
 
 // Token-causal plan: one unit per (batch, head) over all N tokens.  The
-// tile kernel holds one workgroup per compute unit and walks a range of Lr
-// tokens; ranges are whole multiples of the state chunks (Lr = m * Lc), so
-// the prefix at a range start is a sum of whole chunk partials.  Workspace:
-// the table, the chunk partials, and the range prefixes [units][R][d*d + d].
+// tile kernel walks a range of Lr tokens per workgroup (about one workgroup
+// per compute unit); ranges are whole multiples of the state chunks
+// (Lr = m * Lc), so the prefix at a range start is a sum of whole chunk
+// partials.  The matrix-core path takes two chunks per range (two state
+// workgroups per compute unit).  Workspace: the table, the chunk partials,
+// and the range prefixes [units][R][d*d + d].
 gla_status make_causal_plan(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, int64_t d,
                             gla_dtype dtype, float theta, float eps, int cus, bool aligned16,
                             Plan *p) {
   Plan P;
   gla_status st = make_plan(B, H, T, Hs, Ws, d, 0, dtype, theta, eps, cus, aligned16, &P);
   if (st != GLA_OK) return st;
-  P.mfma = false;  // vector tile kernel
-  const int64_t tile = 16;
-  int64_t Lr = round_up(ceil_div(P.N, pick_pieces(P.units, P.N, tile, 256, cus)), tile);
-  Lr = std::min(Lr, round_up(P.N, tile));
-  P.Lr = Lr;
-  P.R = ceil_div(P.N, Lr);
-  P.Lc = Lr;  // m = 1
-  P.C = P.R;
+  if (P.mfma) {
+    const int64_t tile = 2 * gla::kStateTile;
+    int64_t Lr = round_up(ceil_div(P.N, pick_pieces(P.units, P.N, tile, 256, cus)), tile);
+    Lr = std::min(Lr, round_up(P.N, tile));
+    // the table slice of a range must fit beside the tile kernel's other
+    // LDS, and the state kernel's slice of a chunk in its own budget
+    const int64_t hw = Hs * Ws, pt = d / 8, spatial = Hs * (3 * d / 16) + Ws * (3 * d / 16);
+    const int64_t state_rows = (gla::kStateTabEntries - spatial) / pt;
+    const int64_t state_max = ((state_rows - 1) * hw) / gla::kStateTile * gla::kStateTile;
+    Lr = std::min(Lr, 2 * state_max / tile * tile);
+    // buffer offsets are 32-bit: the range plus one step of prefetch
+    const int64_t row_bytes = H * d * 2;
+    const int64_t max_tokens = (((int64_t)1 << 31) - 2 * d) / row_bytes - 2 * gla::kStateTile;
+    Lr = std::min(Lr, max_tokens / tile * tile);
+    auto set_ranges = [&](int64_t len) {
+      P.Lr = len;
+      P.R = ceil_div(P.N, len);
+      P.Lc = len / 2;
+      P.C = ceil_div(P.N, P.Lc);
+    };
+    set_ranges(std::max(Lr, tile));
+    // fewer temporal table rows per range until the tile kernel's LDS fits
+    while (gla::causal_mfma_lds_bytes(P) > 160 * 1024 && P.Lr > tile)
+      set_ranges(std::max(tile, (P.Lr - hw) / tile * tile));
+    if (Lr < tile || state_max < gla::kStateTile || gla::causal_mfma_lds_bytes(P) > 160 * 1024)
+      P.mfma = false;
+  }
+  if (!P.mfma) {  // vector tile kernel
+    const int64_t tile = 16;
+    int64_t Lr = round_up(ceil_div(P.N, pick_pieces(P.units, P.N, tile, 256, cus)), tile);
+    Lr = std::min(Lr, round_up(P.N, tile));
+    P.Lr = Lr;
+    P.R = ceil_div(P.N, Lr);
+    P.Lc = Lr;  // m = 1
+    P.C = P.R;
+  }
   if (P.units * P.C > 0x7fffffff)
     return fail(GLA_ERR_UNSUPPORTED, "too many (batch, head, range) units for one launch");
   size_t off = 0;
@@ -465,7 +495,8 @@ gla_status run_causal(const Plan &P, const void *q, const void *k, const void *v
                     [&] { return gla::launch_range_prefix(P, part, states, stream); });
   if (st != GLA_OK) return st;
   return timed_launch(5, stream, "causal tile kernel", [&] {
-    return gla::launch_causal_generic(P, q, k, v, g, states, tab, out, stream);
+    return P.mfma ? gla::launch_causal_mfma(P, q, k, v, g, states, tab, out, stream)
+                  : gla::launch_causal_generic(P, q, k, v, g, states, tab, out, stream);
   });
 }
 

@@ -90,6 +90,12 @@ hipError_t launch_apply_mfma(const Plan &p, const void *q, const void *g, const 
 // ([units][R][d*d + d]); the tile kernels walk each range from that sum.
 hipError_t launch_range_prefix(const Plan &p, const float *partials, float *states,
                                hipStream_t stream);
+// Matrix-core tile kernel (bf16, d = 64 or 128, Lr a multiple of 64) and its
+// LDS bytes for the plan's ranges.
+hipError_t launch_causal_mfma(const Plan &p, const void *q, const void *k, const void *v,
+                              const void *g, const float *states, const float2 *tab, void *out,
+                              hipStream_t stream);
+size_t causal_mfma_lds_bytes(const Plan &p);
 hipError_t launch_causal_generic(const Plan &p, const void *q, const void *k, const void *v,
                                  const void *g, const float *states, const float2 *tab, void *out,
                                  hipStream_t stream);

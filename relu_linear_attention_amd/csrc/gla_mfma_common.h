@@ -1,0 +1,244 @@
+// Helpers of the matrix-core kernels (gfx950): vector types, buffer
+// resources over a head's rows, bf16 packing and hi/lo splitting, the RoPE
+// table slice kept in LDS, the transposing LDS read, and the LDS layout of
+// the bf16 parts of S.  Included by the matrix-core translation units only;
+// everything here has internal linkage.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "gla_internal.h"
+
+namespace gla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+struct MArgs {
+  int64_t N, H, Hs, Ws;
+  int64_t nb, L, C, Lc, R, Lr;
+  int64_t tab_h_off;  // global entry offset of the h rows (the w rows follow)
+  FastDiv div_hw, div_w;  // by Hs*Ws and by Ws (token indices < 2^31)
+  float eps;
+  float rms_eps;  // epsilon of the optional RMSNorm of num/den
+};
+
+// Buffer resource over the rows of one head for a token range: byte 0 is
+// feature 0 of the first token, row r starts at r * row_bytes, and the
+// range ends after the last token's d features.  Loads past the end return
+// zeros and stores past the end are dropped by the hardware, so ragged token
+// tiles need neither masks nor branches.  (Raw buffer, stride 0; the last
+// descriptor word selects 32-bit untyped data.)
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rows_rsrc(const uint16_t *first_row,
+                                                                 uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(first_row), 0, (int)bytes,
+                                           0x00020000);
+}
+// Cache policy of a buffer access: kCacheNormal, or kCacheStream for data
+// touched exactly once (the non-temporal hint: the line is not kept for
+// reuse).
+constexpr int kCacheNormal = 0;
+constexpr int kCacheStream = 2;
+template <int Policy = kCacheNormal>
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, Policy);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+template <int Policy = kCacheNormal>
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 x) {
+  const u32x4 v = {x.x, x.y, x.z, x.w};
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, Policy);
+}
+
+// Token index (within a batch entry, < 2^31) -> (t, h, w) of the t-major grid.
+__device__ __forceinline__ void token_pos(const MArgs &a, int64_t n, int &t, int &h, int &w) {
+  const uint32_t u = (uint32_t)n;
+  const uint32_t tt = a.div_hw.div(u);
+  const uint32_t r = u - tt * a.div_hw.d;
+  const uint32_t hh = a.div_w.div(r);
+  t = (int)tt;
+  h = (int)hh;
+  w = (int)(r - hh * a.div_w.d);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 f = {lo, hi};
+  bf16x2 h = __builtin_convertvector(f, bf16x2);  // round to nearest even
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// ReLU of two packed bf16 values: a bf16 is negative exactly when its sign
+// bit is set, so a signed 16-bit max with 0 keeps x >= 0 and maps x < 0
+// (and -0) to +0.
+__device__ __forceinline__ uint32_t relu_bf16x2(uint32_t x) {
+  s16x2 v = __builtin_bit_cast(s16x2, x);
+  s16x2 zero = {0, 0};
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(v, zero));
+}
+
+__device__ __forceinline__ float lo_bf16(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+// Split two floats into packed bf16 hi parts (round to nearest even) and
+// packed bf16 lo parts, the rounded remainders: x ~ hi + lo to about 16
+// significant bits.
+__device__ __forceinline__ void split_bf16x2(float x0, float x1, uint32_t &hi, uint32_t &lo) {
+  hi = pack_bf16x2(x0, x1);
+  lo = pack_bf16x2(x0 - lo_bf16(hi), x1 - hi_bf16(hi));
+}
+
+// Feature pair P0 (a multiple of 4) -> axis (0 t, 1 h, 2 w) and the pair's
+// index within that axis.  For d = 64 and 128 a group of four pairs never
+// straddles two axes.
+template <int D>
+__device__ __forceinline__ void pair_axis(int P0, int &axis, int &pia) {
+  constexpr int pt = D / 8, ph = 3 * D / 16;
+  if (P0 < pt) {
+    axis = 0; pia = P0;
+  } else if (P0 < pt + ph) {
+    axis = 1; pia = P0 - pt;
+  } else {
+    axis = 2; pia = P0 - pt - ph;
+  }
+}
+
+// LDS copy of the RoPE table rows a workgroup touches: the h rows and the w
+// rows (both whole), then the temporal rows t_lo..t_hi of its token range.
+// A lane always needs the (cos, sin) entries of four consecutive pairs (a
+// "group"; every axis row holds a whole number of groups).  The slice is
+// stored as two planes of 16-byte units, pairs 0-1 of every group in the
+// first and pairs 2-3 in the second, so that lanes reading neighbouring
+// groups read neighbouring 16-byte units (the direct 32-byte layout leaves
+// half the LDS banks idle and serialises on the other half).
+template <int D>
+struct TabSlice {
+  int sp_groups;  // (Hs + Ws) * 3D/64 groups of the spatial rows
+  int groups;     // groups in the slice (size of one plane)
+  int Hs;
+  int t_lo;
+  // Group of the pair group pia/4 of an axis at grid position (t, h, w):
+  // g = base + t*mt + h*mh + w*mw.  Written as arithmetic (two of the
+  // multipliers are 0) so that the compiler cannot turn the axis choice into
+  // a divergent branch, which would make it wait for every outstanding load
+  // at the join.
+  struct Lookup {
+    int base, mt, mh, mw;
+    __device__ __forceinline__ int at(int t, int h, int w) const {
+      return base + t * mt + h * mh + w * mw;
+    }
+  };
+  __device__ __forceinline__ Lookup lookup(int axis, int pia) const {
+    constexpr int gt = D / 32, gh = 3 * D / 64;  // groups per t row, per h or w row
+    Lookup l;
+    l.mt = axis == 0 ? gt : 0;
+    l.mh = axis == 1 ? gh : 0;
+    l.mw = axis == 2 ? gh : 0;
+    l.base = pia / 4 + (axis == 0 ? sp_groups - t_lo * gt : (axis == 2 ? Hs * gh : 0));
+    return l;
+  }
+  // the four (cos, sin) entries of group g
+  __device__ __forceinline__ void read(const float2 *s_tab, int g, float2 (&c4)[4]) const {
+    const float4 a = reinterpret_cast<const float4 *>(s_tab)[g];
+    const float4 b = reinterpret_cast<const float4 *>(s_tab)[groups + g];
+    c4[0] = make_float2(a.x, a.y);
+    c4[1] = make_float2(a.z, a.w);
+    c4[2] = make_float2(b.x, b.y);
+    c4[3] = make_float2(b.z, b.w);
+  }
+};
+
+template <int D>
+__device__ TabSlice<D> load_tab_slice(float2 *s_tab, const float2 *__restrict__ tab,
+                                      const MArgs &a, int64_t n_begin, int64_t n_end) {
+  constexpr int ph = 3 * D / 16;
+  const int64_t hw = a.Hs * a.Ws;
+  TabSlice<D> ts;
+  ts.Hs = (int)a.Hs;
+  const int sp_entries = (int)((a.Hs + a.Ws) * ph);
+  ts.sp_groups = sp_entries / 4;
+  ts.t_lo = (int)(n_begin / hw);
+  const int t_hi = (int)((n_end - 1) / hw);
+  const int entries = sp_entries + (t_hi - ts.t_lo + 1) * (D / 8);
+  ts.groups = entries / 4;
+  for (int i = threadIdx.x; i < entries; i += blockDim.x) {
+    const float2 cs = i < sp_entries ? tab[a.tab_h_off + i]
+                                     : tab[(int64_t)ts.t_lo * (D / 8) + (i - sp_entries)];
+    // entry i = pair i % 4 of group i / 4
+    s_tab[(i & 2) * ts.groups + 2 * (i >> 2) + (i & 1)] = cs;
+  }
+  return ts;
+}
+
+// Rotate four adjacent pairs x[0..7] by the (cos, sin) entries cs[0..3].
+__device__ __forceinline__ void rotate4(float *x, const float2 *cs) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float2 c = cs[i];
+    const float x0 = x[2 * i], x1 = x[2 * i + 1];
+    x[2 * i] = x0 * c.x - x1 * c.y;
+    x[2 * i + 1] = x0 * c.y + x1 * c.x;
+  }
+}
+
+// Transposing LDS read of gfx950 (ds_read_b64_tr_b16).  Within each group of
+// 16 lanes, lane s supplies the address of a row of four 16-bit values
+// M[s][0..3], and lane i receives M[i/4 + 4k][i%4] for k = 0..3.  With lane
+// s pointing at row tok0 + s/4, column c0 + 4*(s%4) of a row-major
+// [token][feature] tile, lane i receives X[tok0 + k][c0 + i], k = 0..3: four
+// consecutive tokens of one feature, half of the eight a lane contributes to
+// a matrix-core operand whose contraction runs over tokens.  This read moves
+// 512 B in two LDS cycles, twice the rate of plain 16-B reads.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const unsigned char *p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4 *)(p));
+  return __builtin_bit_cast(uint2, r);
+}
+
+// LDS layout of the S parts in the apply stage: row-major [p][e] bf16 with
+// the 16-byte units of row p XOR-permuted by f(p).  The A operand of the
+// 16x16x32 instruction (S^T: rows e, columns p) is read with the transposing
+// LDS read: lane s of a 16-lane group points at row p0 + s/4, column
+// e0 + 4*(s%4), and lane i receives S[p0 + k][e0 + i], k = 0..3.  A read
+// touches rows p0..p0+3 and p0+8..p0+11 per 32 lanes, 32 B each; f gives
+// those eight rows distinct unit pairs, so a read covers all banks once.
+// f depends only on row bits that the k-step and half offsets (multiples of
+// 4 rows, bit 3 untouched) leave alone.
+template <int D>
+struct SRow {
+  static __device__ __forceinline__ int f(int row) {
+    return D == 128 ? 2 * ((row & 3) + 4 * ((row >> 3) & 1))
+                    : 2 * (((row >> 1) & 1) + 2 * ((row >> 3) & 1));
+  }
+  static __device__ __forceinline__ int off(int row, int unit) {
+    return row * (2 * D) + ((unit ^ f(row)) << 4);
+  }
+};
+inline MArgs make_margs(const Plan &p) {
+  MArgs a;
+  a.N = p.N; a.H = p.H; a.Hs = p.Hs; a.Ws = p.Ws;
+  a.nb = p.nb; a.L = p.L; a.C = p.C; a.Lc = p.Lc; a.R = p.R; a.Lr = p.Lr;
+  a.tab_h_off = p.tab_h_off;
+  a.div_hw = FastDiv::make((uint32_t)(p.Hs * p.Ws));
+  a.div_w = FastDiv::make((uint32_t)p.Ws);
+  a.eps = p.eps;
+  a.rms_eps = p.rms_eps;
+  return a;
+}
+
+// LDS entries of the RoPE table slice for a token range of at most `len`
+// tokens: the spatial rows plus the temporal rows it can span.
+inline int64_t tab_slice_entries(const Plan &p, int64_t len) {
+  const int64_t hw = p.Hs * p.Ws;
+  const int64_t rows = (len + hw - 1) / hw + 1;
+  return (p.Hs + p.Ws) * (3 * p.d / 16) + rows * (p.d / 8);
+}
+
+}  // namespace
+}  // namespace gla
