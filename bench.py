@@ -25,16 +25,17 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
+PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector, published
 DEFAULT_WORKLOAD = "720p_81f"
-MFMA_SOURCES = ("relu_linear_attention_amd/csrc/gla_mfma.hip",
-                "relu_linear_attention_amd/csrc/gla_mfma_common.h",
-                "relu_linear_attention_amd/csrc/gla_common.hip")
+CSRC = os.path.join(ROOT, "relu_linear_attention_amd", "csrc")
 
 
 def source_digest() -> str:
+    """sha256[:16] over every kernel and launcher source (a change to any of
+    them invalidates the recorded counters)."""
     h = hashlib.sha256()
-    for rel in MFMA_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -215,10 +216,91 @@ def backward_leg(w, x, steps: int, warmup: int):
     ms = start.elapsed_time(stop) / steps
     nbytes = 9 * w.B * w.N * w.H * w.d * w.elem_bytes
     gbps = nbytes / (ms * 1e-3) / 1e9
+    stage_ms = {k: (v / n if n else None) for k, (n, v) in stages.items()}
+    # the gradient kernels are fp32 FMA work on the vector units: per
+    # token-head, five d x d products (num, S dnum and the dS outer product on
+    # the q side; G v and RoPE(phi(k)) G on the k/v side; the recomputed
+    # forward state is not counted)
+    flops = 2 * 5 * w.d * w.d * w.B * w.N * w.H
+    grad_ms = stage_ms["backward"]
+    tflops = flops / (grad_ms * 1e-3) / 1e12
     return {"workload": w.name, "ms_per_call": ms, "tokens_per_s": w.B * w.N / (ms * 1e-3),
-            "stages_ms": {k: (v / n if n else None) for k, (n, v) in stages.items()},
-            "algorithmic_bytes_per_call": nbytes, "GBps": gbps, "frac_of_peak": gbps / PEAK_HBM_GBPS,
+            "stages_ms": stage_ms, "algorithmic_bytes_per_call": nbytes, "GBps": gbps,
+            "frac_of_peak": gbps / PEAK_HBM_GBPS,
+            "roofline": {"bound": "alu", "kernel": "bwd_q_kernel + bwd_reduce_kernel + bwd_kv_kernel",
+                         "achieved": tflops, "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tflops / PEAK_FP32_VALU_TFLOPS, "traffic": None,
+                         "algorithmic_flops_per_launch": flops},
             "kernels": "vector (fp32 VALU) gradient kernels; matrix-core state stage"}
+
+
+def token_causal_leg(w, x, steps: int, warmup: int, oracle_frames: int = 2):
+    """The token-causal form (gla_token_causal_forward) on the same workload:
+    state partials, the range prefixes and the tile kernel.  Algorithmic
+    bytes: q, k, v, g read once and out written once.  The fp64 oracle is
+    timed beside it on the first `oracle_frames` latent frames (every head)."""
+    import torch
+
+    from relu_linear_attention_amd import gla
+
+    out = torch.empty_like(x["q"])
+    ws = torch.empty(gla.gla_token_causal_workspace_bytes(w.B, w.H, w.T, w.Hs, w.Ws, w.d,
+                                                          gla.GLA_BF16 if w.dtype == "bf16"
+                                                          else gla.GLA_F32),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call():
+        gla.gla_token_causal_forward(x["q"], x["k"], x["v"], x["g"], out, w.grid, w.theta, w.eps,
+                                     workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    gla.gla_profile_enable(True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        call()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    stages = gla.gla_profile_read()
+    gla.gla_profile_enable(False)
+    ms = start.elapsed_time(stop) / steps
+    nbytes = 5 * w.B * w.N * w.H * w.d * w.elem_bytes
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    stage_ms = {k: (v / n if n else None) for k, (n, v) in stages.items()}
+    tile_ms = stage_ms["causal_apply"]
+    mfma = gla.gla_uses_matrix_cores(w.T, w.Hs, w.Ws, w.d, gla.GLA_BF16 if w.dtype == "bf16"
+                                     else gla.GLA_F32) == 1
+    kname = "causal_mfma_kernel" if mfma else "causal_vector_kernel"
+    tile_gbps = nbytes / (tile_ms * 1e-3) / 1e9
+    res = {"workload": w.name, "ms_per_call": ms, "tokens_per_s": w.B * w.N / (ms * 1e-3),
+           "stages_ms": stage_ms, "algorithmic_bytes_per_call": nbytes, "GBps": gbps,
+           "frac_of_peak": gbps / PEAK_HBM_GBPS,
+           # the tile kernel reads q, k, v, g and writes out: the same five
+           # tensor passes as the whole call (the state stage re-reads k, v)
+           "roofline": {"bound": "hbm", "kernel": kname, "achieved": tile_gbps,
+                        "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": tile_gbps / PEAK_HBM_GBPS,
+                        "traffic": measured_traffic(w.name).get(kname),
+                        "algorithmic_bytes_per_launch": nbytes}}
+    if oracle_frames <= 0:
+        return res
+    try:
+        import oracle
+
+        n = oracle_frames * w.Hs * w.Ws
+        host = {k_: t[:, :n].float().cpu().numpy() for k_, t in x.items()}
+        t0 = time.perf_counter()
+        oracle.token_causal(host["q"], host["k"], host["v"], host["g"],
+                            (oracle_frames, w.Hs, w.Ws), w.theta, w.eps)
+        sec = time.perf_counter() - t0
+        res["oracle"] = {"tokens_per_s": w.B * n / sec, "seconds": sec,
+                         "sample": f"first {oracle_frames} latent frames ({n} tokens), all heads",
+                         "cores": oracle.num_threads()}
+    except Exception as e:  # the oracle is a reported baseline; the GPU figures stand alone
+        res["oracle"] = {"error": str(e)}
+    return res
 
 
 def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
@@ -255,6 +337,10 @@ def main() -> int:
                     help="skip the gated-mixer (write gate + RMSNorm) measurement")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the gradient measurement")
+    ap.add_argument("--no-token-causal", action="store_true",
+                    help="skip the token-causal measurement")
+    ap.add_argument("--only-leg", choices=["gated", "backward", "token_causal", "block_step"],
+                    help="run only this measurement and print its JSON (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
@@ -275,13 +361,26 @@ def main() -> int:
         return 0
 
     w = WORKLOADS[args.workload]
+    if args.only_leg == "block_step":
+        print(json.dumps({"block_step": block_step_leg(args.steps, args.warmup)}))
+        return 0
     x = device_inputs_for(w)
+    if args.only_leg == "backward":
+        print(json.dumps({"backward": backward_leg(w, x, args.steps, args.warmup)}))
+        return 0
+    if args.only_leg == "token_causal":
+        print(json.dumps({"token_causal": token_causal_leg(w, x, args.steps, args.warmup,
+                                                           oracle_frames=0)}))
+        return 0
     q, k, v, g = x["q"], x["k"], x["v"], x["g"]
     out = torch.empty_like(q)
     dtype_code = gla.GLA_BF16 if w.dtype == "bf16" else gla.GLA_F32
     ws = torch.empty(gla.gla_workspace_bytes(w.B, w.H, w.T, w.Hs, w.Ws, w.d, w.frames_per_block,
                                              dtype_code), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
+    if args.only_leg == "gated":
+        print(json.dumps({"gated": gated_leg(w, x, ws, args.steps, args.warmup)}))
+        return 0
 
     def step():
         gla.gla_forward_ws(q, k, v, g, out, w.grid, ws, w.frames_per_block, w.theta, w.eps,
@@ -359,6 +458,8 @@ def main() -> int:
         result["gated"] = gated_leg(w, x, ws, max(3, args.steps // 2), 10)
     if not args.no_backward:
         result["backward"] = backward_leg(w, x, max(3, args.steps // 10), 3)
+    if not args.no_token_causal:
+        result["token_causal"] = token_causal_leg(w, x, max(3, args.steps // 4), 5)
     if not args.no_block_step:
         result["block_step"] = block_step_leg(max(3, args.steps // 4), 5)
     if not args.no_cpu_baseline:
