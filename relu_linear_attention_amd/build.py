@@ -24,7 +24,7 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
-SOURCES = ["gla_common.hip", "gla_vector.hip", "gla_mfma.hip", "gla_backward.hip", "gla_causal.hip",
+SOURCES = ["gla_common.hip", "gla_vector.hip", "gla_mfma.hip", "gla_backward.hip", "gla_backward_mfma.hip", "gla_causal.hip",
            "gla_causal_mfma.hip",            "gla_api.cpp"]
 
 

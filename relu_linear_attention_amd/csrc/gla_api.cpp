@@ -726,7 +726,9 @@ gla_status gla_backward(const void *q, const void *k, const void *v, const void 
   int cus = 0;
   st = device_cus(&cus);
   if (st != GLA_OK) return st;
-  const bool aligned16 = (((uintptr_t)k | (uintptr_t)v) & 15) == 0;
+  // (the matrix-core kernels move 16-byte pieces of k and v and 8-byte
+  // pieces of k, dk and dv)
+  const bool aligned16 = (((uintptr_t)k | (uintptr_t)v | (uintptr_t)dk | (uintptr_t)dv) & 15) == 0;
   Plan P;
   st = make_plan(B, H, T, Hs, Ws, d, F, dtype, rope_theta, eps, cus, aligned16, &P);
   if (st != GLA_OK) return st;

@@ -421,6 +421,8 @@ hipError_t bwd_d(const Plan &p, const void *q, const void *k, const void *v, con
                      dim3(kBlock), 0, stream, partials, grads, p.nb, p.Rb, (int)p.d);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (p.mfma && (D == 64 || D == 128) && sizeof(TIn) == 2)
+    return launch_bwd_kv_mfma(p, k, v, grads, tab, dk, dv, stream);
   const size_t lds_kv = sizeof(float) * (D * kRow<D> + D + 3 * kTokB * D);
   auto kkv = bwd_kv_kernel<TIn, D>;
   e = hipFuncSetAttribute((const void *)kkv, hipFuncAttributeMaxDynamicSharedMemorySize,

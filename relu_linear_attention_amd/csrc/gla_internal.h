@@ -108,6 +108,11 @@ hipError_t launch_backward(const Plan &p, const void *q, const void *k, const vo
                            const float2 *tab, float *partials, float *grads, void *dq, void *dk,
                            void *dv, void *dg, hipStream_t stream);
 
+// Matrix-core kernel of the key/value side of the gradients (bf16, d = 64 or
+// 128): dk, dv from G, Gz (`grads`, [units][d*d + d]); ranges R x Lr.
+hipError_t launch_bwd_kv_mfma(const Plan &p, const void *k, const void *v, const float *grads,
+                              const float2 *tab, void *dk, void *dv, hipStream_t stream);
+
 // Division by a fixed divisor d >= 1 for dividends 0 <= n < 2^31, by a
 // multiply-high and a shift: with s = ceil(log2 d) and
 // m = floor(2^32 (2^s - d) / d) + 1, n / d = (mulhi(n, m) + n) >> s.
