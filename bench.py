@@ -217,21 +217,32 @@ def backward_leg(w, x, steps: int, warmup: int):
     nbytes = 9 * w.B * w.N * w.H * w.d * w.elem_bytes
     gbps = nbytes / (ms * 1e-3) / 1e9
     stage_ms = {k: (v / n if n else None) for k, (n, v) in stages.items()}
-    # the gradient kernels are fp32 FMA work on the vector units: per
-    # token-head, five d x d products (num, S dnum and the dS outer product on
-    # the q side; G v and RoPE(phi(k)) G on the k/v side; the recomputed
-    # forward state is not counted)
-    flops = 2 * 5 * w.d * w.d * w.B * w.N * w.H
+    mfma = gla.gla_uses_matrix_cores(w.T, w.Hs, w.Ws, w.d, gla.GLA_BF16 if w.dtype == "bf16"
+                                     else gla.GLA_F32) == 1
     grad_ms = stage_ms["backward"]
-    tflops = flops / (grad_ms * 1e-3) / 1e12
+    if mfma:
+        # the gradient kernels stream nine tensor passes (q, g, dout, k, v read;
+        # dq, dg, dk, dv written) against their matrix-core products
+        roof = {"bound": "hbm", "kernel": "bwd_q_mfma_kernel + bwd_reduce_kernel + bwd_kv_mfma_kernel",
+                "achieved": nbytes / (grad_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "traffic": None, "algorithmic_bytes_per_launch": nbytes}
+        roof["frac"] = roof["achieved"] / PEAK_HBM_GBPS
+        kernels = "matrix-core gradient kernels (query side, block sums, key/value side)"
+    else:
+        # fp32 FMA work on the vector units: per token-head, five d x d products
+        # (num, S dnum and the dS outer product on the query side; G v and
+        # RoPE(phi(k)) G on the key/value side)
+        flops = 2 * 5 * w.d * w.d * w.B * w.N * w.H
+        tflops = flops / (grad_ms * 1e-3) / 1e12
+        roof = {"bound": "alu", "kernel": "bwd_q_kernel + bwd_reduce_kernel + bwd_kv_kernel",
+                "achieved": tflops, "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
+                "frac": tflops / PEAK_FP32_VALU_TFLOPS, "traffic": None,
+                "algorithmic_flops_per_launch": flops}
+        kernels = "vector (fp32 VALU) gradient kernels"
     return {"workload": w.name, "ms_per_call": ms, "tokens_per_s": w.B * w.N / (ms * 1e-3),
             "stages_ms": stage_ms, "algorithmic_bytes_per_call": nbytes, "GBps": gbps,
-            "frac_of_peak": gbps / PEAK_HBM_GBPS,
-            "roofline": {"bound": "alu", "kernel": "bwd_q_kernel + bwd_reduce_kernel + bwd_kv_kernel",
-                         "achieved": tflops, "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
-                         "frac": tflops / PEAK_FP32_VALU_TFLOPS, "traffic": None,
-                         "algorithmic_flops_per_launch": flops},
-            "kernels": "vector (fp32 VALU) gradient kernels; matrix-core state stage"}
+            "frac_of_peak": gbps / PEAK_HBM_GBPS, "roofline": roof,
+            "kernels": kernels + "; the forward state re-run on the matrix cores"}
 
 
 def token_causal_leg(w, x, steps: int, warmup: int, oracle_frames: int = 2):

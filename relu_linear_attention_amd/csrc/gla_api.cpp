@@ -286,7 +286,10 @@ gla_status make_plan(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, in
   if (P.mfma) off = align256(off + (size_t)P.units * 2 * d * d * sizeof(uint16_t));
   P.total_bytes = off;
   P.off_bpart = off;
-  off = align256(off + (size_t)P.units * P.Rb * gla::kPartialStride(d) * sizeof(float));
+  // (the vector gradient kernels write Rb range partials per unit, the
+  // matrix-core ones R)
+  off = align256(off + (size_t)P.units * std::max(P.Rb, P.R) * gla::kPartialStride(d) *
+                           sizeof(float));
   P.off_grad = off;
   off = align256(off + (size_t)P.units * gla::kPartialStride(d) * sizeof(float));
   P.bwd_total_bytes = off;
@@ -726,9 +729,12 @@ gla_status gla_backward(const void *q, const void *k, const void *v, const void 
   int cus = 0;
   st = device_cus(&cus);
   if (st != GLA_OK) return st;
-  // (the matrix-core kernels move 16-byte pieces of k and v and 8-byte
-  // pieces of k, dk and dv)
-  const bool aligned16 = (((uintptr_t)k | (uintptr_t)v | (uintptr_t)dk | (uintptr_t)dv) & 15) == 0;
+  // (the matrix-core kernels move 16-byte pieces of q, k and v and 8-byte
+  // pieces of every tensor)
+  uintptr_t all = 0;
+  for (const void *t : ins) all |= (uintptr_t)t;
+  for (const void *t : outs) all |= (uintptr_t)t;
+  const bool aligned16 = (all & 15) == 0;
   Plan P;
   st = make_plan(B, H, T, Hs, Ws, d, F, dtype, rope_theta, eps, cus, aligned16, &P);
   if (st != GLA_OK) return st;

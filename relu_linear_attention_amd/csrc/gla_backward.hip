@@ -404,6 +404,19 @@ template <typename TIn, int D>
 hipError_t bwd_d(const Plan &p, const void *q, const void *k, const void *v, const void *g,
                  const void *dout, const float *states, const float2 *tab, float *partials,
                  float *grads, void *dq, void *dk, void *dv, void *dg, hipStream_t stream) {
+  const int64_t stride = kPartialStride(p.d), per_block = (int64_t)kBlock * 4;
+  const dim3 rgrid((unsigned)(p.B * p.H), (unsigned)((stride + per_block - 1) / per_block));
+  if (p.mfma && (D == 64 || D == 128) && sizeof(TIn) == 2 &&
+      bwd_q_mfma_lds_bytes(p) <= 160 * 1024) {
+    // matrix-core kernels over the apply stage's ranges (R x Lr)
+    hipError_t e = launch_bwd_q_mfma(p, q, g, dout, states, tab, dq, dg, partials, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_reduce_kernel, rgrid, dim3(kBlock), 0, stream, partials, grads, p.nb,
+                       p.R, (int)p.d);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_bwd_kv_mfma(p, k, v, grads, tab, dk, dv, stream);
+  }
   const BwdArgs a = make_bargs(p);
   const dim3 grid((unsigned)(p.units * p.Rb));
   const size_t lds_q = sizeof(float) * (D * kRow<D> + D + 4 * kTokB * D + 2 * kTokB);
@@ -415,14 +428,10 @@ hipError_t bwd_d(const Plan &p, const void *q, const void *k, const void *v, con
                      (const TIn *)dout, states, tab, (TIn *)dq, (TIn *)dg, partials, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t stride = kPartialStride(p.d), per_block = (int64_t)kBlock * 4;
-  hipLaunchKernelGGL(bwd_reduce_kernel,
-                     dim3((unsigned)(p.B * p.H), (unsigned)((stride + per_block - 1) / per_block)),
-                     dim3(kBlock), 0, stream, partials, grads, p.nb, p.Rb, (int)p.d);
+  hipLaunchKernelGGL(bwd_reduce_kernel, rgrid, dim3(kBlock), 0, stream, partials, grads, p.nb,
+                     p.Rb, (int)p.d);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (p.mfma && (D == 64 || D == 128) && sizeof(TIn) == 2)
-    return launch_bwd_kv_mfma(p, k, v, grads, tab, dk, dv, stream);
   const size_t lds_kv = sizeof(float) * (D * kRow<D> + D + 3 * kTokB * D);
   auto kkv = bwd_kv_kernel<TIn, D>;
   e = hipFuncSetAttribute((const void *)kkv, hipFuncAttributeMaxDynamicSharedMemorySize,

@@ -35,29 +35,8 @@
 namespace gla {
 namespace {
 
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-
 constexpr int kCausalThreads = 512;  // 8 waves
 constexpr int kCausalStep = 64;      // tokens per step
-
-// LDS layout of the step tiles (RoPE(phi(k)) hi and lo, phi(k), v): row-major
-// [token][feature] bf16, the 16-byte units of row r XOR-permuted by f(r).
-// Two read patterns must spread over the banks:
-//   - 16-byte row pieces, 16 lanes on 16 consecutive rows, one unit (the key
-//     operand of the scores): f takes 16 distinct values over 16 rows at
-//     d = 128;
-//   - transposing reads, 4 consecutive rows x 2 adjacent units per 16 lanes
-//     (the operands of the state update and of scores x v): f(r) differs in
-//     bits 2-3 over 4 consecutive rows, so the 8 units are distinct.
-template <int D>
-struct KRow {
-  static __device__ __forceinline__ int f(int row) {
-    return D == 128 ? 4 * (row & 3) + ((row >> 2) & 3) : 2 * (row & 3) + ((row >> 2) & 1);
-  }
-  static __device__ __forceinline__ int off(int row, int unit) {
-    return row * (2 * D) + ((unit ^ f(row)) << 4);
-  }
-};
 
 template <int D>
 struct CausalCfg {
@@ -77,28 +56,6 @@ struct CausalCfg {
   static constexpr size_t kFixedLds =
       (size_t)D * D * 4 + 4 * (size_t)TILE + (size_t)D * 4 + (size_t)NW * D * 4;
 };
-
-// 8-byte buffer accesses (four bf16 of one token row)
-__device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kCacheNormal);
-  return make_uint2(v.x, v.y);
-}
-__device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t off, uint2 x) {
-  const u32x2 v = {x.x, x.y};
-  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, kCacheNormal);
-}
-
-// Sixteen wait states after the last matrix-core instruction of an
-// accumulation chain, with the scheduler kept from moving anything across:
-// the vector instructions that follow may read the chain's result or write
-// its accumulator registers.  (Without it the compiler let a vector read of
-// an 8-pass v_mfma_f32_16x16x32_bf16 result follow a branch one wait state
-// after the instruction issued, and the read saw the previous value.)
-__device__ __forceinline__ void mfma_drain() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
 
 template <int D>
 __global__ __launch_bounds__(kCausalThreads) void causal_mfma_kernel(

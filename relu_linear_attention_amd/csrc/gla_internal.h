@@ -110,6 +110,13 @@ hipError_t launch_backward(const Plan &p, const void *q, const void *k, const vo
 
 // Matrix-core kernel of the key/value side of the gradients (bf16, d = 64 or
 // 128): dk, dv from G, Gz (`grads`, [units][d*d + d]); ranges R x Lr.
+// Matrix-core kernel of the query side of the gradients (bf16, d = 64 or
+// 128): dq, dg and the per-range dS, dz partials ([units][R][d*d + d]) from
+// the forward states; ranges R x Lr (Lr a multiple of 64).
+hipError_t launch_bwd_q_mfma(const Plan &p, const void *q, const void *g, const void *dout,
+                             const float *states, const float2 *tab, void *dq, void *dg,
+                             float *partials, hipStream_t stream);
+size_t bwd_q_mfma_lds_bytes(const Plan &p);
 hipError_t launch_bwd_kv_mfma(const Plan &p, const void *k, const void *v, const float *grads,
                               const float2 *tab, void *dk, void *dv, hipStream_t stream);
 

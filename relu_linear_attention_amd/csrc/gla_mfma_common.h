@@ -56,6 +56,29 @@ __device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t o
   __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, Policy);
 }
 
+// 8-byte buffer accesses (four bf16 of one token row)
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kCacheNormal);
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t off, uint2 x) {
+  const u32x2 v = {x.x, x.y};
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, kCacheNormal);
+}
+
+// Sixteen wait states after the last matrix-core instruction of an
+// accumulation chain, with the scheduler kept from moving anything across:
+// the vector instructions that follow may read the chain's result.  (Without
+// it the compiler let a vector read of an 8-pass v_mfma_f32_16x16x32_bf16
+// result follow a branch one wait state after the instruction issued, and
+// the read saw the previous value.)
+__device__ __forceinline__ void mfma_drain() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Token index (within a batch entry, < 2^31) -> (t, h, w) of the t-major grid.
 __device__ __forceinline__ void token_pos(const MArgs &a, int64_t n, int &t, int &h, int &w) {
   const uint32_t u = (uint32_t)n;
@@ -220,6 +243,25 @@ struct SRow {
     return row * (2 * D) + ((unit ^ f(row)) << 4);
   }
 };
+
+// LDS layout of token tiles (the rows of one step of tokens): row-major
+// [token][feature] bf16, the 16-byte units of row r XOR-permuted by f(r).
+// Two read patterns must spread over the banks:
+//   - 16-byte row pieces, 16 lanes on 16 consecutive rows, one unit: f takes
+//     16 distinct values over 16 rows at d = 128;
+//   - transposing reads, 4 consecutive rows x 2 adjacent units per 16 lanes
+//     (operands whose contraction runs over tokens): f(r) differs in bits
+//     2-3 over 4 consecutive rows, so the 8 units are distinct.
+template <int D>
+struct KRow {
+  static __device__ __forceinline__ int f(int row) {
+    return D == 128 ? 4 * (row & 3) + ((row >> 2) & 3) : 2 * (row & 3) + ((row >> 2) & 1);
+  }
+  static __device__ __forceinline__ int off(int row, int unit) {
+    return row * (2 * D) + ((unit ^ f(row)) << 4);
+  }
+};
+
 inline MArgs make_margs(const Plan &p) {
   MArgs a;
   a.N = p.N; a.H = p.H; a.Hs = p.Hs; a.Ws = p.Ws;

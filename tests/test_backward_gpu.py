@@ -50,6 +50,9 @@ CASES = [
     ("bf16_d64", 1, 4, 6, 5, 3, 64, "bf16", 0),
     ("bf16_d112", 1, 2, 5, 5, 2, 112, "bf16", 1),
     ("f32_d16_ragged", 1, 3, 7, 5, 1, 16, "f32", 0),
+    # long enough for several token ranges per (batch, head, block), ragged tails
+    ("bf16_d128_many_ranges", 1, 7, 13, 11, 2, 128, "bf16", 0),
+    ("bf16_d64_many_ranges_blocks", 1, 6, 13, 11, 2, 64, "bf16", 2),
 ]
 
 
