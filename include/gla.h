@@ -190,8 +190,9 @@ gla_status gla_block_step(const void *q, const void *k, const void *v, const voi
  * "SANA-Video" Sections 3.2 and 3.4); the derivative of ReLU at 0 is taken
  * as 0, and in block-causal mode a block's keys and values receive the
  * gradients of every later block that reads them.  The call re-runs the
- * state stage, then the gradient kernels (fp32 arithmetic on the vector
- * units for every supported d).
+ * state stage, then the gradient kernels: on the matrix cores for bf16 with
+ * d = 64 or 128 and 16-byte aligned tensors (bf16 hi + lo operands, fp32
+ * accumulation), else fp32 arithmetic on the vector units.
  * workspace: NULL (taken stream-ordered on `stream`) or at least
  * gla_backward_workspace_bytes() bytes of device memory, 256-byte aligned.
  */
