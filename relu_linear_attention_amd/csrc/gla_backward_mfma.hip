@@ -35,7 +35,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_kernel(
   unsigned char *s_gh = lds;              // G hi, row-major [p][e], units permuted (SRow)
   unsigned char *s_gl = lds + D * D * 2;  // G lo
   float *s_gz = reinterpret_cast<float *>(lds + D * D * 4);  // Gz (D)
-  float2 *s_tab = reinterpret_cast<float2 *>(s_gz + D);
+  unsigned char *s_stage = reinterpret_cast<unsigned char *>(s_gz + D);  // NW staging tiles
+  float2 *s_tab = reinterpret_cast<float2 *>(s_stage + NW * Stage<D>::kBytes);
 
   const int64_t wg = blockIdx.x;
   const int64_t unit = wg / a.R, r = wg % a.R;
@@ -98,6 +99,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_kernel(
     int t, h, w;
     token_pos(a, n < n_end ? n : n_end - 1, t, h, w);
     const uint32_t toff = ((uint32_t)(tile - n_begin) + nl) * row_bytes + 8 * kg;
+    const uint32_t row0 = (uint32_t)(tile - n_begin) * row_bytes;
+    unsigned char *stage = s_stage + wave * Stage<D>::kBytes;
 
     // ---- dv = RoPE(phi(k)) G
     {
@@ -149,10 +152,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_kernel(
       }
       mfma_drain();
       // value i of acc[et]: feature 16*et + 4*kg + i of token nl
+      uint2 vals[ET];
 #pragma unroll
       for (int et = 0; et < ET; ++et)
-        buf_store8(rdv, toff + 32 * et,
-                   make_uint2(pack_bf16x2(acc[et][0], acc[et][1]), pack_bf16x2(acc[et][2], acc[et][3])));
+        vals[et] = make_uint2(pack_bf16x2(acc[et][0], acc[et][1]), pack_bf16x2(acc[et][2], acc[et][3]));
+      store_tile_rows<D>(stage, vals, rdv, row0, row_bytes);
     }
 
     // ---- dk = [RoPE^T(G v) + Gz] * 1[k > 0]
@@ -178,6 +182,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_kernel(
 #pragma unroll
       for (int pt = 0; pt < ET; ++pt) kc[pt] = buf_load8(rk, toff + 32 * pt);
       mfma_drain();
+      uint2 vals[ET];
 #pragma unroll
       for (int pt = 0; pt < ET; ++pt) {
         // features p0..p0+3 = pairs P0, P0 + 1 (half of a table group)
@@ -199,8 +204,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_kernel(
                              hi_bf16(kc[pt].y)};
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] = kv[i] > 0.f ? o[i] : 0.f;
-        buf_store8(rdk, toff + 32 * pt, make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])));
+        vals[pt] = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
       }
+      store_tile_rows<D>(stage, vals, rdk, row0, row_bytes);
     }
   };
 
@@ -602,7 +608,8 @@ hipError_t bwd_q_d(const Plan &p, const void *q, const void *g, const void *dout
 
 template <int D>
 size_t bwd_kv_lds(const Plan &p) {
-  return (size_t)D * D * 4 + (size_t)D * 4 + (size_t)tab_slice_entries(p, p.Lr) * sizeof(float2);
+  return (size_t)D * D * 4 + (size_t)D * 4 + (size_t)(kBwdThreads / 64) * Stage<D>::kBytes +
+         (size_t)tab_slice_entries(p, p.Lr) * sizeof(float2);
 }
 
 template <int D>

@@ -284,18 +284,6 @@ __global__ __launch_bounds__(kStateThreads<D>, kStateThreads<D> / 128) void stat
 // do not.
 constexpr int kApplyThreads = 512;
 
-// per-wave LDS staging tile of the epilogue: 16 token rows of D bf16, rows
-// 2D + 16 bytes apart (an odd number of 16-byte units), so that the 16
-// rows read by a fragment-wise 8-B access start in 16 different 4-bank
-// groups and the row-wise 16-B accesses stay contiguous
-template <int D>
-struct Stage {
-  static constexpr int kRowBytes = 2 * D + 16;
-  static constexpr int kBytes = 16 * kRowBytes;
-  static constexpr int kLanesPerRow = D / 8;             // 16 B per lane
-  static constexpr int kRowsPerPass = 64 / kLanesPerRow;  // token rows per instruction
-  static constexpr int kPasses = 16 / kRowsPerPass;
-};
 
 //
 // kNorm: the RMSNorm of "SANA-Video 2.0" Eq. (1) between num/den and the

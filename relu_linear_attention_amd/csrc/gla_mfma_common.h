@@ -262,6 +262,49 @@ struct KRow {
   }
 };
 
+// per-wave LDS staging tile of the epilogue: 16 token rows of D bf16, rows
+// 2D + 16 bytes apart (an odd number of 16-byte units), so that the 16
+// rows read by a fragment-wise 8-B access start in 16 different 4-bank
+// groups and the row-wise 16-B accesses stay contiguous
+template <int D>
+struct Stage {
+  static constexpr int kRowBytes = 2 * D + 16;
+  static constexpr int kBytes = 16 * kRowBytes;
+  static constexpr int kLanesPerRow = D / 8;             // 16 B per lane
+  static constexpr int kRowsPerPass = 64 / kLanesPerRow;  // token rows per instruction
+  static constexpr int kPasses = 16 / kRowsPerPass;
+};
+
+// Writes a wave's 16-token output tile to HBM as whole rows through its
+// staging tile.  vals[et] holds four bf16 (packed) of token l % 16, features
+// 16*et + 4*(l/16)..+3: the accumulator layout of a 16x16 product whose
+// columns are tokens.  row_off is the byte offset of the tile's first token
+// row in `dst`; rows past the resource's end are dropped.
+template <int D, int Policy = kCacheNormal>
+__device__ __forceinline__ void store_tile_rows(unsigned char *stage, const uint2 (&vals)[D / 16],
+                                                __amdgpu_buffer_rsrc_t dst, uint32_t row_off,
+                                                uint32_t row_bytes) {
+  using St = Stage<D>;
+  const int lane = threadIdx.x & 63, nl = lane & 15, kg = lane >> 4;
+#pragma unroll
+  for (int et = 0; et < D / 16; ++et)
+    *reinterpret_cast<uint2 *>(stage + nl * St::kRowBytes + 2 * (16 * et + 4 * kg)) = vals[et];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int rl = lane / St::kLanesPerRow, rc = 8 * (lane % St::kLanesPerRow);
+#pragma unroll
+  for (int i = 0; i < St::kPasses; ++i) {
+    const int tok = i * St::kRowsPerPass + rl;
+    const uint4 ov = *reinterpret_cast<const uint4 *>(stage + tok * St::kRowBytes + 2 * rc);
+    buf_store16<Policy>(dst, row_off + (uint32_t)tok * row_bytes + 2 * rc, ov);
+  }
+  // the next writes into the tile must not overtake these reads
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 inline MArgs make_margs(const Plan &p) {
   MArgs a;
   a.N = p.N; a.H = p.H; a.Hs = p.Hs; a.Ws = p.Ws;
