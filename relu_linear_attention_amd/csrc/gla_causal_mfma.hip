@@ -173,6 +173,38 @@ __global__ __launch_bounds__(kCausalThreads) void causal_mfma_kernel(
     for (int u = 0; u < ETW; ++u) graw[u] = buf_load8(rg, goff + 32 * (eh * ETW + u));
   };
 
+  // LDS offsets of the read patterns of a step.  The row swizzles of both
+  // layouts depend only on the low row bits (KRow: bits 0-3; SRow: bits 0, 1
+  // and 3), which the tile, key-step and k-step offsets below leave alone,
+  // so every read is a lane-constant base plus a uniform offset.
+  int kbase[KS];  // key rows of key tile 0: + kt * 16 rows
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) kbase[ks] = KRow<D>::off(nl, 4 * ks + kg);
+  int vbase[ETW];  // v^T reads of keys 4*kg.. (+ 32*js rows, + 16 rows)
+  int sbase[ETW];  // S^T fragments (+ 32*ks rows, + 4 rows)
+#pragma unroll
+  for (int u = 0; u < ETW; ++u) {
+    const int et = eh * ETW + u;
+    const int c = 16 * et + 4 * (nl & 3);
+    vbase[u] = KRow<D>::off(4 * kg + (nl >> 2), c >> 3) + 2 * (c & 7);
+    sbase[u] = SRow<D>::off(8 * kg + (nl >> 2), 2 * et + ((nl & 3) >> 1)) + 8 * (nl & 1);
+  }
+  int pv[STW][2], pk[STW][2];  // state-update reads (+ 16*kk rows)
+  {
+    const int g16 = lane >> 4, s16 = lane & 15;
+    const int r0 = 8 * (g16 >> 1) + (s16 >> 2);
+#pragma unroll
+    for (int t = 0; t < STW; ++t) {
+      const int ce = 32 * t_e[t] + 16 * (g16 & 1) + 4 * (s16 & 3);
+      const int cp = 32 * t_p[t] + 16 * (g16 & 1) + 4 * (s16 & 3);
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        pv[t][hh] = KRow<D>::off(r0 + 4 * hh, ce >> 3) + 2 * (ce & 7);
+        pk[t][hh] = KRow<D>::off(r0 + 4 * hh, cp >> 3) + 2 * (cp & 7);
+      }
+    }
+  }
+
   load_kvq(n_begin);
   load_g(n_begin);
 
@@ -286,7 +318,7 @@ __global__ __launch_bounds__(kCausalThreads) void causal_mfma_kernel(
       dm = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int o = KRow<D>::off(16 * kt + nl, 4 * ks + kg);
+        const int o = kbase[ks] + kt * (32 * D);
         const bf16x8 fh = *reinterpret_cast<const bf16x8 *>(s_kh + o);
         const bf16x8 fl = *reinterpret_cast<const bf16x8 *>(s_kl + o);
         const bf16x8 fp = *reinterpret_cast<const bf16x8 *>(s_kp + o);
@@ -329,13 +361,11 @@ __global__ __launch_bounds__(kCausalThreads) void causal_mfma_kernel(
       split_bf16x2(at[1][2], at[1][3], ah[3], al[3]);
       const bf16x8 bh = __builtin_bit_cast(bf16x8, make_uint4(ah[0], ah[1], ah[2], ah[3]));
       const bf16x8 bl = __builtin_bit_cast(bf16x8, make_uint4(al[0], al[1], al[2], al[3]));
-      const int row0 = 32 * js + 4 * kg + (nl >> 2);
 #pragma unroll
       for (int u = 0; u < ETW; ++u) {
-        const int c = 16 * (eh * ETW + u) + 4 * (nl & 3);
-        const int cu = c >> 3, cb = 2 * (c & 7);
-        const uint2 v0 = lds_read_tr16(s_v + KRow<D>::off(row0, cu) + cb);
-        const uint2 v1 = lds_read_tr16(s_v + KRow<D>::off(row0 + 16, cu) + cb);
+        const int o = vbase[u] + js * (64 * D);  // keys 32*js + 4*kg.. and + 16
+        const uint2 v0 = lds_read_tr16(s_v + o);
+        const uint2 v1 = lds_read_tr16(s_v + o + 16 * (2 * D));
         const bf16x8 vt = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
         acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, bl, acc[u], 0, 0, 0);
         acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, bh, acc[u], 0, 0, 0);
@@ -349,11 +379,8 @@ __global__ __launch_bounds__(kCausalThreads) void causal_mfma_kernel(
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int u = 0; u < ETW; ++u) {
-        const int et = eh * ETW + u;
-        const int o0 = SRow<D>::off(8 * kg + (nl >> 2) + 32 * ks, 2 * et + ((nl & 3) >> 1)) +
-                       8 * (nl & 1);
-        const int o1 = SRow<D>::off(8 * kg + (nl >> 2) + 32 * ks + 4, 2 * et + ((nl & 3) >> 1)) +
-                       8 * (nl & 1);
+        const int o0 = sbase[u] + (32 * ks) * (2 * D);
+        const int o1 = o0 + 4 * (2 * D);
         const uint2 h0 = lds_read_tr16(s_sh + o0), h1 = lds_read_tr16(s_sh + o1);
         const uint2 l0 = lds_read_tr16(s_sl + o0), l1 = lds_read_tr16(s_sl + o1);
         const bf16x8 fa = __builtin_bit_cast(bf16x8, make_uint4(h0.x, h0.y, h1.x, h1.y));
@@ -390,18 +417,12 @@ __global__ __launch_bounds__(kCausalThreads) void causal_mfma_kernel(
 
     // ---------------- state: S^T += v^T RoPE(phi(k)) over the step's keys
     if (s_owner) {
-      const int g16 = lane >> 4, s16 = lane & 15;
 #pragma unroll
       for (int t = 0; t < STW; ++t) {
-        const int ce = 32 * t_e[t] + 16 * (g16 & 1) + 4 * (s16 & 3);
-        const int cp = 32 * t_p[t] + 16 * (g16 & 1) + 4 * (s16 & 3);
 #pragma unroll
         for (int kk = 0; kk < STEP / 16; ++kk) {
-          const int row = 16 * kk + 8 * (g16 >> 1) + (s16 >> 2);
-          const int ov0 = KRow<D>::off(row, ce >> 3) + 2 * (ce & 7);
-          const int ov1 = KRow<D>::off(row + 4, ce >> 3) + 2 * (ce & 7);
-          const int ok0 = KRow<D>::off(row, cp >> 3) + 2 * (cp & 7);
-          const int ok1 = KRow<D>::off(row + 4, cp >> 3) + 2 * (cp & 7);
+          const int ov0 = pv[t][0] + kk * (32 * D), ov1 = pv[t][1] + kk * (32 * D);
+          const int ok0 = pk[t][0] + kk * (32 * D), ok1 = pk[t][1] + kk * (32 * D);
           const uint2 v0 = lds_read_tr16(s_v + ov0), v1 = lds_read_tr16(s_v + ov1);
           const uint2 h0 = lds_read_tr16(s_kh + ok0), h1 = lds_read_tr16(s_kh + ok1);
           const uint2 l0 = lds_read_tr16(s_kl + ok0), l1 = lds_read_tr16(s_kl + ok1);
