@@ -353,6 +353,37 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_kernel(
       qc[u] = buf_load8(rq, o);
     }
   };
+  // LDS offsets of the read patterns (the row swizzles depend only on low
+  // row bits, which tile and k-step offsets leave alone): lane-constant
+  // bases plus uniform offsets
+  int tbase[KS];  // the query tile's rows in the token tiles (+ 0 per k-step unit)
+  int srow[KS];   // S rows of tile 0 (+ 16 rows per tile)
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    tbase[ks] = KRow<D>::off(nl, 4 * ks + kg) + qt * (32 * D);
+    srow[ks] = SRow<D>::off(nl, 4 * ks + kg);
+  }
+  int sbase[ETW];  // S^T fragments of the output tiles of half eh (+ 32*ks rows, + 4 rows)
+#pragma unroll
+  for (int u = 0; u < ETW; ++u) {
+    const int et = eh * ETW + u;
+    sbase[u] = SRow<D>::off(8 * kg + (nl >> 2), 2 * et + ((nl & 3) >> 1)) + 8 * (nl & 1);
+  }
+  int pe[STW][2], pp[STW][2];  // dS^T update reads (+ 16*kk rows)
+  {
+    const int g16 = lane >> 4, s16 = lane & 15;
+    const int r0 = 8 * (g16 >> 1) + (s16 >> 2);
+#pragma unroll
+    for (int tt = 0; tt < STW; ++tt) {
+      const int ce = 32 * t_e[tt] + 16 * (g16 & 1) + 4 * (s16 & 3);
+      const int cp = 32 * t_p[tt] + 16 * (g16 & 1) + 4 * (s16 & 3);
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        pe[tt][hh] = KRow<D>::off(r0 + 4 * hh, ce >> 3) + 2 * (ce & 7);
+        pp[tt][hh] = KRow<D>::off(r0 + 4 * hh, cp >> 3) + 2 * (cp & 7);
+      }
+    }
+  }
   load_step(n_begin);
 
   for (int64_t n0 = n_begin; n0 < n_end; n0 += STEP) {
@@ -398,7 +429,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_kernel(
       qh[ks] = __builtin_bit_cast(bf16x8, make_uint4(hw4[0], hw4[1], hw4[2], hw4[3]));
       ql[ks] = __builtin_bit_cast(bf16x8, make_uint4(lw4[0], lw4[1], lw4[2], lw4[3]));
       if ((ks >= KS / 2) == (eh == 1)) {  // this wave's half of the features
-        const int o = KRow<D>::off(16 * qt + nl, 4 * ks + kg);
+        const int o = tbase[ks];
         *reinterpret_cast<bf16x8 *>(s_rh + o) = qh[ks];
         *reinterpret_cast<bf16x8 *>(s_rl + o) = ql[ks];
       }
@@ -415,9 +446,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_kernel(
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int u = 0; u < ETW; ++u) {
-        const int et = eh * ETW + u;
-        const int o0 = SRow<D>::off(8 * kg + (nl >> 2) + 32 * ks, 2 * et + ((nl & 3) >> 1)) +
-                       8 * (nl & 1);
+        const int o0 = sbase[u] + (32 * ks) * (2 * D);
         const int o1 = o0 + 4 * (2 * D);
         const uint2 h0 = lds_read_tr16(s_sh + o0), h1 = lds_read_tr16(s_sh + o1);
         const uint2 l0 = lds_read_tr16(s_sl + o0), l1 = lds_read_tr16(s_sl + o1);
@@ -479,12 +508,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_kernel(
     for (int u = 0; u < ETW; ++u) acc2[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int on = KRow<D>::off(16 * qt + nl, 4 * ks + kg);
+      const int on = tbase[ks];
       const bf16x8 nh = *reinterpret_cast<const bf16x8 *>(s_nh + on);
       const bf16x8 nlo = *reinterpret_cast<const bf16x8 *>(s_nl + on);
 #pragma unroll
       for (int u = 0; u < ETW; ++u) {
-        const int o = SRow<D>::off(16 * (eh * ETW + u) + nl, 4 * ks + kg);
+        const int o = srow[ks] + (eh * ETW + u) * (32 * D);
         const bf16x8 sh = *reinterpret_cast<const bf16x8 *>(s_sh + o);
         const bf16x8 sl = *reinterpret_cast<const bf16x8 *>(s_sl + o);
         acc2[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sl, nh, acc2[u], 0, 0, 0);
@@ -523,18 +552,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_kernel(
     }
     // dS^T += dnum^T RoPE(phi(q)) over the step's 64 tokens
     if (s_owner) {
-      const int g16 = lane >> 4, s16 = lane & 15;
 #pragma unroll
       for (int tt = 0; tt < STW; ++tt) {
-        const int ce = 32 * t_e[tt] + 16 * (g16 & 1) + 4 * (s16 & 3);
-        const int cp = 32 * t_p[tt] + 16 * (g16 & 1) + 4 * (s16 & 3);
 #pragma unroll
         for (int kk = 0; kk < STEP / 16; ++kk) {
-          const int row = 16 * kk + 8 * (g16 >> 1) + (s16 >> 2);
-          const int oe0 = KRow<D>::off(row, ce >> 3) + 2 * (ce & 7);
-          const int oe1 = KRow<D>::off(row + 4, ce >> 3) + 2 * (ce & 7);
-          const int op0 = KRow<D>::off(row, cp >> 3) + 2 * (cp & 7);
-          const int op1 = KRow<D>::off(row + 4, cp >> 3) + 2 * (cp & 7);
+          const int oe0 = pe[tt][0] + kk * (32 * D), oe1 = pe[tt][1] + kk * (32 * D);
+          const int op0 = pp[tt][0] + kk * (32 * D), op1 = pp[tt][1] + kk * (32 * D);
           const uint2 a0 = lds_read_tr16(s_nh + oe0), a1 = lds_read_tr16(s_nh + oe1);
           const uint2 b0 = lds_read_tr16(s_nl + oe0), b1 = lds_read_tr16(s_nl + oe1);
           const uint2 c0 = lds_read_tr16(s_rh + op0), c1 = lds_read_tr16(s_rh + op1);
