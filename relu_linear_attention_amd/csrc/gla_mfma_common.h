@@ -245,17 +245,21 @@ struct SRow {
 };
 
 // LDS layout of token tiles (the rows of one step of tokens): row-major
-// [token][feature] bf16, the 16-byte units of row r XOR-permuted by f(r).
-// Two read patterns must spread over the banks:
-//   - 16-byte row pieces, 16 lanes on 16 consecutive rows, one unit: f takes
-//     16 distinct values over 16 rows at d = 128;
-//   - transposing reads, 4 consecutive rows x 2 adjacent units per 16 lanes
-//     (operands whose contraction runs over tokens): f(r) differs in bits
-//     2-3 over 4 consecutive rows, so the 8 units are distinct.
+// [token][feature] bf16, the 16-byte units of row r XOR-permuted by f(r),
+// which depends on row bits 0-3 only.  The transposing reads of these tiles
+// serve 32 lanes per LDS cycle: two 16-lane groups, each on 4 consecutive
+// rows and 2 adjacent units, either on the same rows and the next unit pair
+// (the contractions over a step's tokens) or on the next 4 rows and the same
+// units (scores x v).  At d = 128, f(r) = 4(r&3) + 2((r>>2)&1) + ((r>>3)&1)
+// puts both pairs of groups on 16 distinct units (measured on MI355X with
+// rocprofv3 SQ_LDS_BANK_CONFLICT: no conflict cycles for either, where the
+// previous 4(r&3) + ((r>>2)&3) doubled the second pattern).  16-byte row
+// pieces cost the same under any permutation.
 template <int D>
 struct KRow {
   static __device__ __forceinline__ int f(int row) {
-    return D == 128 ? 4 * (row & 3) + ((row >> 2) & 3) : 2 * (row & 3) + ((row >> 2) & 1);
+    return D == 128 ? 4 * (row & 3) + 2 * ((row >> 2) & 1) + ((row >> 3) & 1)
+                    : 2 * (row & 3) + ((row >> 2) & 1);
   }
   static __device__ __forceinline__ int off(int row, int unit) {
     return row * (2 * D) + ((unit ^ f(row)) << 4);
