@@ -107,3 +107,31 @@ def test_full_size_backward_480p():
         err = grad_err(a.float().cpu().numpy(), r)
         print(f"  {gname}: err {err:.3e}", flush=True)
         assert err <= TOL["bf16"], gname
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("wname", ["720p_81f", "720p_block_causal"])
+def test_full_size_backward_sampled_heads(wname):
+    # the full 720p layers (non-causal and 7 blocks of 3 frames): the GPU
+    # computes every head, the oracle three of them over every token (heads
+    # are independent)
+    import torch
+
+    w = WORKLOADS[wname]
+    print(f"workload {w.name} backward: grid {w.T}x{w.Hs}x{w.Ws} H={w.H} F={w.frames_per_block}",
+          flush=True)
+    dev = device_inputs_for(w)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed + 9)
+    dout = torch.randn(dev["q"].shape, generator=gen, device="cuda").to(torch.bfloat16)
+    got = _run(dev, dout, w.grid, w.frames_per_block)
+    heads = [0, 13, w.H - 1]
+    idx = torch.tensor(heads, device="cuda")
+    hs = {n: t.index_select(2, idx).float().cpu().numpy() for n, t in dev.items()}
+    ref = oracle.backward(hs["q"], hs["k"], hs["v"], hs["g"],
+                          dout.index_select(2, idx).float().cpu().numpy(), w.grid,
+                          w.frames_per_block)
+    for gname, a, r in zip(("dq", "dk", "dv", "dg"), got, ref):
+        err = grad_err(a.index_select(2, idx).float().cpu().numpy(), r)
+        print(f"  {gname}: err {err:.3e}", flush=True)
+        assert err <= TOL["bf16"], gname

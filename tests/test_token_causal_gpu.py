@@ -107,3 +107,22 @@ def test_full_size_token_causal(wname):
     err = max_rel_err(got.float().cpu().numpy(), ref)
     print(f"  max rel err {err:.3e}", flush=True)
     assert err <= TOL["bf16"]
+
+
+@pytest.mark.slow
+def test_long_video_token_causal_sampled_heads():
+    # the 60 s video (867,600 tokens x 24 heads, tensors of 2.67e9 elements):
+    # the GPU computes every head, the oracle five of them over every token
+    import torch
+
+    w = WORKLOADS["720p_60s"]
+    print(f"workload {w.name} token-causal: N={w.N} H={w.H}", flush=True)
+    dev = device_inputs_for(w)
+    got = _run(dev, w.grid)
+    heads = [0, 5, 11, 17, 23]
+    idx = torch.tensor(heads, device="cuda")
+    hs = {n: t.index_select(2, idx).float().cpu().numpy() for n, t in dev.items()}
+    ref = oracle.token_causal(hs["q"], hs["k"], hs["v"], hs["g"], w.grid)
+    err = max_rel_err(got.index_select(2, idx).float().cpu().numpy(), ref)
+    print(f"  {len(heads)} heads x {w.N} tokens: max rel err {err:.3e}", flush=True)
+    assert err <= TOL["bf16"]
