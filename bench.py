@@ -223,9 +223,14 @@ def backward_leg(w, x, steps: int, warmup: int):
     if mfma:
         # the gradient kernels stream nine tensor passes (q, g, dout, k, v read;
         # dq, dg, dk, dv written) against their matrix-core products
-        roof = {"bound": "hbm", "kernel": "bwd_q_mfma_kernel + bwd_reduce_kernel + bwd_kv_mfma_kernel",
+        names = ("bwd_q_mfma_kernel", "bwd_reduce_kernel", "bwd_kv_mfma_kernel")
+        measured = measured_traffic(w.name)
+        roof = {"bound": "hbm", "kernel": " + ".join(names),
                 "achieved": nbytes / (grad_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "traffic": None, "algorithmic_bytes_per_launch": nbytes}
+                "traffic": (sum(measured[n] for n in names)
+                            if w.frames_per_block == 0 and all(n in measured for n in names)
+                            else None),
+                "algorithmic_bytes_per_launch": nbytes}
         roof["frac"] = roof["achieved"] / PEAK_HBM_GBPS
         kernels = "matrix-core gradient kernels (query side, block sums, key/value side)"
     else:

@@ -85,8 +85,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_kernel(
     const uint32_t off = ((uint32_t)(tile - n_begin) + nl) * row_bytes + 16 * kg;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      kb[ks] = buf_load16<kCacheStream>(rk, off + 64 * ks);
-      vb[ks] = buf_load16<kCacheStream>(rv, off + 64 * ks);
+      kb[ks] = buf_load16<kCacheNormal>(rk, off + 64 * ks);
+      vb[ks] = buf_load16<kCacheNormal>(rv, off + 64 * ks);
     }
   };
 
@@ -98,9 +98,32 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_kernel(
     const int64_t n = tile + nl;
     int t, h, w;
     token_pos(a, n < n_end ? n : n_end - 1, t, h, w);
-    const uint32_t toff = ((uint32_t)(tile - n_begin) + nl) * row_bytes + 8 * kg;
     const uint32_t row0 = (uint32_t)(tile - n_begin) * row_bytes;
     unsigned char *stage = s_stage + wave * Stage<D>::kBytes;
+    // the ReLU mask of dk in the accumulator layout (bit 4*pt + i: feature
+    // 16*pt + 4*kg + i of token nl).  Each lane marks its own k values
+    // (bit 8*ks + jj: feature 32*ks + 8*kg + jj); feature p sits in lane
+    // (nl, kg' = (p % 32) / 8) at bit 8*(p / 32) + p % 8, so the two lanes
+    // kg' = 2*b + kg/2 (b = 0, 1) hold everything this lane needs.
+    uint32_t kmask = 0;
+    {
+      uint32_t own = 0;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint32_t kw[4] = {kb[ks].x, kb[ks].y, kb[ks].z, kb[ks].w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          own |= (lo_bf16(kw[m]) > 0.f ? 1u : 0u) << (8 * ks + 2 * m);
+          own |= (hi_bf16(kw[m]) > 0.f ? 1u : 0u) << (8 * ks + 2 * m + 1);
+        }
+      }
+      const uint32_t m0 = (uint32_t)__shfl((int)own, nl + 16 * (kg >> 1));
+      const uint32_t m1 = (uint32_t)__shfl((int)own, nl + 16 * (2 + (kg >> 1)));
+      const int sh = 4 * (kg & 1);
+#pragma unroll
+      for (int pt = 0; pt < ET; ++pt)
+        kmask |= (((pt & 1 ? m1 : m0) >> (8 * (pt >> 1) + sh)) & 0xFu) << (4 * pt);
+    }
 
     // ---- dv = RoPE(phi(k)) G
     {
@@ -177,10 +200,6 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_kernel(
           acc[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bv, acc[pt], 0, 0, 0);
         }
       }
-      // k in the accumulator layout, for the ReLU mask
-      uint2 kc[ET];
-#pragma unroll
-      for (int pt = 0; pt < ET; ++pt) kc[pt] = buf_load8(rk, toff + 32 * pt);
       mfma_drain();
       uint2 vals[ET];
 #pragma unroll
@@ -200,10 +219,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_kernel(
         o[1] = -d0 * c0.y + d1 * c0.x + gz.y;
         o[2] = d2 * c1.x + d3 * c1.y + gz.z;
         o[3] = -d2 * c1.y + d3 * c1.x + gz.w;
-        const float kv[4] = {lo_bf16(kc[pt].x), hi_bf16(kc[pt].x), lo_bf16(kc[pt].y),
-                             hi_bf16(kc[pt].y)};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = kv[i] > 0.f ? o[i] : 0.f;
+        for (int i = 0; i < 4; ++i) o[i] = (kmask >> (4 * pt + i)) & 1u ? o[i] : 0.f;
         vals[pt] = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
       }
       store_tile_rows<D>(stage, vals, rdk, row0, row_bytes);
