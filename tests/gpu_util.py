@@ -42,3 +42,23 @@ def rel_l2(got, ref) -> float:
 
 # tolerances of the operator's outputs (max |err| / (|ref| + 1e-3))
 TOL = {"f32": 1e-4, "bf16": 1e-2}
+
+
+def unaligned_copies(x: dict, dtype: str = "bf16"):
+    """Device copies of the arrays that start one element into their
+    allocations (too misaligned for 16-byte loads), plus a maker of output
+    tensors placed the same way."""
+    import torch
+
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+
+    def place(shape):
+        n = int(np.prod(shape))
+        return torch.empty(n + 1, dtype=tdt, device="cuda")[1:].view(*shape)
+
+    ts = {}
+    for name, a in x.items():
+        t = place(a.shape)
+        t.copy_(torch.from_numpy(np.ascontiguousarray(a)).to(tdt))
+        ts[name] = t
+    return ts, place

@@ -135,3 +135,38 @@ def test_full_size_backward_sampled_heads(wname):
         err = grad_err(a.index_select(2, idx).float().cpu().numpy(), r)
         print(f"  {gname}: err {err:.3e}", flush=True)
         assert err <= TOL["bf16"], gname
+
+
+def test_unaligned_tensors_other_stream_and_small_workspace():
+    # misaligned tensors take the vector gradient kernels; a non-default
+    # stream gives the default stream's bits; a short workspace is refused
+    import torch
+
+    from tests.gpu_util import unaligned_copies
+
+    B, T, Hs, Ws, H, d, F = 1, 4, 5, 6, 2, 128, 2
+    x = host_inputs(B, T, Hs, Ws, H, d, "bf16", seed=55)
+    dout = _dout(x["q"].shape, "bf16", 56)
+    ts, place = unaligned_copies(dict(x, o=dout))
+    outs = [place(ts["q"].shape) for _ in range(4)]
+    gla.gla_backward(ts["q"], ts["k"], ts["v"], ts["g"], ts["o"], *outs, (T, Hs, Ws), F)
+    torch.cuda.synchronize()
+    ref = oracle.backward(x["q"], x["k"], x["v"], x["g"], dout, (T, Hs, Ws), F)
+    for gname, a, r in zip(("dq", "dk", "dv", "dg"), outs, ref):
+        assert grad_err(to_host_f32(a), r) <= TOL["bf16"], gname
+
+    dev = to_device(x, "bf16")
+    ddev = to_device({"o": dout}, "bf16")["o"]
+    a = _run(dev, ddev, (T, Hs, Ws), F)
+    s = torch.cuda.Stream()
+    b = [torch.empty_like(dev["q"]) for _ in range(4)]
+    with torch.cuda.stream(s):
+        gla.gla_backward(dev["q"], dev["k"], dev["v"], dev["g"], ddev, *b, (T, Hs, Ws), F,
+                         stream=s)
+    s.synchronize()
+    for u, v_ in zip(a, b):
+        assert torch.equal(u.view(torch.int16), v_.view(torch.int16))
+    nbytes = gla.gla_backward_workspace_bytes(B, H, T, Hs, Ws, d, F, gla.GLA_BF16)
+    ws = torch.empty(nbytes // 2, dtype=torch.uint8, device="cuda")
+    with pytest.raises(gla.GlaError):
+        _run(dev, ddev, (T, Hs, Ws), F, workspace=ws)

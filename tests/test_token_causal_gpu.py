@@ -126,3 +126,30 @@ def test_long_video_token_causal_sampled_heads():
     err = max_rel_err(got.index_select(2, idx).float().cpu().numpy(), ref)
     print(f"  {len(heads)} heads x {w.N} tokens: max rel err {err:.3e}", flush=True)
     assert err <= TOL["bf16"]
+
+
+def test_unaligned_tensors_and_other_stream():
+    # tensors one element into their allocations take the vector tile kernel;
+    # a call on a non-default stream gives the default stream's bits
+    import torch
+
+    from tests.gpu_util import unaligned_copies
+
+    B, T, Hs, Ws, H, d = 1, 3, 7, 9, 2, 128
+    x = host_inputs(B, T, Hs, Ws, H, d, "bf16", seed=53)
+    ts, place = unaligned_copies(x)
+    out = place(ts["q"].shape)
+    gla.gla_token_causal_forward(ts["q"], ts["k"], ts["v"], ts["g"], out, (T, Hs, Ws))
+    torch.cuda.synchronize()
+    ref = oracle.token_causal(x["q"], x["k"], x["v"], x["g"], (T, Hs, Ws))
+    assert max_rel_err(to_host_f32(out), ref) <= TOL["bf16"]
+
+    dev = to_device(x, "bf16")
+    a = _run(dev, (T, Hs, Ws))
+    s = torch.cuda.Stream()
+    b = torch.empty_like(dev["q"])
+    with torch.cuda.stream(s):
+        gla.gla_token_causal_forward(dev["q"], dev["k"], dev["v"], dev["g"], b, (T, Hs, Ws),
+                                     stream=s)
+    s.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
