@@ -29,8 +29,8 @@ namespace {
 // Policies of the streams of the two stages.  Measured over whole
 // forward calls at 720p/81f: streaming the k and v reads of the state stage
 // saves about 3% per call; streaming the q and g reads or the out writes of
-// the apply stage only moves time between the stages (a normal write of out
-// is paid for when its dirty lines are evicted during the next state stage).
+// the apply stage (non-temporal, also at system scope) changes nothing
+// measurable, since apply's limit is its operand-layout q loads.
 constexpr int kStateLoadPolicy = kCacheStream;
 constexpr int kApplyLoadPolicy = kCacheNormal;
 constexpr int kApplyStorePolicy = kCacheNormal;
