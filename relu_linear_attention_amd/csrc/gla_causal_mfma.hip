@@ -112,21 +112,28 @@ __global__ __launch_bounds__(kCausalThreads) void causal_mfma_kernel(
       sacc[t][i] = s_owner ? stt[p * D + e] : 0.f;
     }
   }
-  // S -> bf16 hi + lo in LDS: four consecutive e of row p per 8-byte write
+  // S -> bf16 hi + lo in LDS.  Lanes l and l + 32 hold e0..e0+3 and
+  // e0+4..e0+7 of row p; one lane swap per dword (gfx950 permlane32 swap:
+  // the upper half of its first operand trades places with the lower half of
+  // its second) leaves the lower lane with the row's 16-byte hi unit and the
+  // upper lane with its lo unit, one 16-byte store each (half the stores of
+  // 8-byte pieces, and fewer bank conflicts).
   auto publish = [&]() {
     if (!s_owner) return;
+    unsigned char *dst = s_sh + (lane >> 5) * (D * D * 2);  // hi, or lo (s_sl)
 #pragma unroll
     for (int t = 0; t < STW; ++t) {
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        const int e0 = 32 * t_e[t] + 8 * i4 + 4 * (lane >> 5);
+        const int e0 = 32 * t_e[t] + 8 * i4;
         const int p = 32 * t_p[t] + (lane & 31);
         uint32_t h0, l0, h1, l1;
         split_bf16x2(sacc[t][4 * i4], sacc[t][4 * i4 + 1], h0, l0);
         split_bf16x2(sacc[t][4 * i4 + 2], sacc[t][4 * i4 + 3], h1, l1);
-        const int o = SRow<D>::off(p, e0 >> 3) + 2 * (e0 & 7);
-        *reinterpret_cast<uint2 *>(s_sh + o) = make_uint2(h0, h1);
-        *reinterpret_cast<uint2 *>(s_sl + o) = make_uint2(l0, l1);
+        const auto s0 = __builtin_amdgcn_permlane32_swap(h0, l0, false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(h1, l1, false, false);
+        *reinterpret_cast<uint4 *>(dst + SRow<D>::off(p, e0 >> 3)) =
+            make_uint4(s0[0], s1[0], s0[1], s1[1]);
       }
     }
   };
