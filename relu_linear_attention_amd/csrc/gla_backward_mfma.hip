@@ -478,7 +478,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_kernel(
 
     // y, dg, dnum, dout*s . y (value i of acc[u]: feature 16*et + 4*kg + i, token nl)
     const uint32_t coff = ((uint32_t)(n0 - n_begin) + 16 * qt + nl) * row_bytes + 8 * kg;
-    const float inv_den = 1.f / den;
+    const float inv_den = __builtin_amdgcn_rcpf(den);
     float dyy = 0.f;
 #pragma unroll
     for (int u = 0; u < ETW; ++u) {
@@ -491,7 +491,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_mfma_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float y = acc[u][i] * inv_den;
-        const float sg = 1.f / (1.f + __expf(-gv[i]));
+        const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-gv[i]));
         const float dy = dv[i] * sg;
         dgo[i] = dy * y * (1.f - sg);
         dn[i] = dy * inv_den;
