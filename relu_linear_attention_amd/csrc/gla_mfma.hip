@@ -104,12 +104,7 @@ __global__ __launch_bounds__(kStateThreads<D>, kStateThreads<D> / 128) void stat
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform across the wave
 
-  const TabSlice<D> ts = load_tab_slice<D>(s_tab, tab, a, n_begin, n_end);
-
   const int fc = tid % FPT, tg = tid / FPT;
-  int axis, pia;
-  pair_axis<D>(4 * fc, axis, pia);
-  const typename TabSlice<D>::Lookup tl = ts.lookup(axis, pia);
   // this thread's rows of a tile: tg + TPP*r, 16-byte unit fc
   const int wr_off = Cfg::off(tg, fc);
 
@@ -165,6 +160,21 @@ __global__ __launch_bounds__(kStateThreads<D>, kStateThreads<D> / 128) void stat
     }
   };
 
+  // The table slice goes to LDS while the first step's rows are in flight:
+  // its loads, then the rows' loads, then its stores (which wait for the
+  // older table loads alone).  The compiler-only barriers keep the two groups
+  // of loads in that order.
+  TabLoad<D> tload;
+  tload.issue(tab, a, n_begin, n_end);
+  asm volatile("" ::: "memory");
+  load_rows(n_begin);
+  asm volatile("" ::: "memory");
+  tload.store(s_tab, tab);
+  const TabSlice<D> ts = tload.ts;
+  int axis, pia;
+  pair_axis<D>(4 * fc, axis, pia);
+  const typename TabSlice<D>::Lookup tl = ts.lookup(axis, pia);
+
   f32x16 acc[Cfg::TPW];
 #pragma unroll
   for (int t = 0; t < Cfg::TPW; ++t)
@@ -177,7 +187,6 @@ __global__ __launch_bounds__(kStateThreads<D>, kStateThreads<D> / 128) void stat
   // Each 64-token step: ReLU/RoPE/split of the rows in (kr, vr) into the LDS
   // tiles; once they are there, the same registers are refilled with the
   // next step's rows, which stay in flight during the matrix-core phase.
-  load_rows(n_begin);
   for (int64_t n0 = n_begin; n0 < n_end; n0 += kStateTile) {
     __syncthreads();  // the previous step's operand reads are done
 #pragma unroll

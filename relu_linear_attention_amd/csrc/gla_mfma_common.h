@@ -176,26 +176,62 @@ struct TabSlice {
   }
 };
 
+// Copy of the table rows of tokens [n_begin, n_end) into LDS in two parts:
+// issue() loads the first kBatch entries per thread into registers, store()
+// writes them to s_tab and copies any further entries.  A kernel issues the
+// first loads of its main loop (and any other set-up loads) between the two,
+// so that their HBM latency overlaps the table's: the stores wait only for
+// the older table loads.  Indices are clamped so that every load is
+// unconditional.
+template <int D, int kBatch = 8>
+struct TabLoad {
+  TabSlice<D> ts;
+  int sp_entries, entries;
+  int64_t h_off, t_off;
+  float2 v[kBatch];
+  __device__ __forceinline__ float2 fetch(const float2 *__restrict__ tab, int i) const {
+    return i < sp_entries ? tab[h_off + i] : tab[t_off + (i - sp_entries)];
+  }
+  // entry i = pair i % 4 of group i / 4
+  __device__ __forceinline__ int slot(int i) const {
+    return (i & 2) * ts.groups + 2 * (i >> 2) + (i & 1);
+  }
+  __device__ __forceinline__ void issue(const float2 *__restrict__ tab, const MArgs &a,
+                                        int64_t n_begin, int64_t n_end) {
+    constexpr int ph = 3 * D / 16;
+    const int64_t hw = a.Hs * a.Ws;
+    ts.Hs = (int)a.Hs;
+    sp_entries = (int)((a.Hs + a.Ws) * ph);
+    ts.sp_groups = sp_entries / 4;
+    ts.t_lo = (int)(n_begin / hw);
+    const int t_hi = (int)((n_end - 1) / hw);
+    entries = sp_entries + (t_hi - ts.t_lo + 1) * (D / 8);
+    ts.groups = entries / 4;
+    h_off = a.tab_h_off;
+    t_off = (int64_t)ts.t_lo * (D / 8);
+    const int nt = blockDim.x;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      v[j] = fetch(tab, min((int)threadIdx.x + j * nt, entries - 1));
+  }
+  __device__ __forceinline__ void store(float2 *s_tab, const float2 *__restrict__ tab) const {
+    const int nt = blockDim.x;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int i = (int)threadIdx.x + j * nt;
+      if (i < entries) s_tab[slot(i)] = v[j];
+    }
+    for (int i = (int)threadIdx.x + kBatch * nt; i < entries; i += nt) s_tab[slot(i)] = fetch(tab, i);
+  }
+};
+
 template <int D>
 __device__ TabSlice<D> load_tab_slice(float2 *s_tab, const float2 *__restrict__ tab,
                                       const MArgs &a, int64_t n_begin, int64_t n_end) {
-  constexpr int ph = 3 * D / 16;
-  const int64_t hw = a.Hs * a.Ws;
-  TabSlice<D> ts;
-  ts.Hs = (int)a.Hs;
-  const int sp_entries = (int)((a.Hs + a.Ws) * ph);
-  ts.sp_groups = sp_entries / 4;
-  ts.t_lo = (int)(n_begin / hw);
-  const int t_hi = (int)((n_end - 1) / hw);
-  const int entries = sp_entries + (t_hi - ts.t_lo + 1) * (D / 8);
-  ts.groups = entries / 4;
-  for (int i = threadIdx.x; i < entries; i += blockDim.x) {
-    const float2 cs = i < sp_entries ? tab[a.tab_h_off + i]
-                                     : tab[(int64_t)ts.t_lo * (D / 8) + (i - sp_entries)];
-    // entry i = pair i % 4 of group i / 4
-    s_tab[(i & 2) * ts.groups + 2 * (i >> 2) + (i & 1)] = cs;
-  }
-  return ts;
+  TabLoad<D> tl;
+  tl.issue(tab, a, n_begin, n_end);
+  tl.store(s_tab, tab);
+  return tl.ts;
 }
 
 // Rotate four adjacent pairs x[0..7] by the (cos, sin) entries cs[0..3].
@@ -216,7 +252,7 @@ __device__ __forceinline__ void rotate4(float *x, const float2 *cs) {
 // [token][feature] tile, lane i receives X[tok0 + k][c0 + i], k = 0..3: four
 // consecutive tokens of one feature, half of the eight a lane contributes to
 // a matrix-core operand whose contraction runs over tokens.  This read moves
-// 512 B in two LDS cycles, twice the rate of plain 16-B reads.
+// 512 B in two LDS cycles (plain 16-byte reads: 1 KiB in four).
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint2 lds_read_tr16(const unsigned char *p) {
   const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
