@@ -6,10 +6,11 @@ HBM, through the C ABI (gla_forward_ws with a pre-allocated workspace).
 
     python bench.py [--steps K] [--warmup W] [--workload 720p_81f]
 
-Prints one JSON line: tokens/s of the whole job, the per-stage launch times
-(HIP events on the launch stream, recorded by the library around each
-kernel), the HBM roofline of the dominant kernel, and the fp64 oracle timed on
-the host cores as a CPU baseline.
+Prints one JSON line: tokens/s of the whole job (K timed steps), the
+per-stage launch times (HIP events on the launch stream, recorded by the
+library around each kernel in a second pass of K steps), the HBM roofline of
+the dominant kernel, and the fp64 oracle timed on the host cores as a CPU
+baseline.
 """
 from __future__ import annotations
 
@@ -85,6 +86,35 @@ def cpu_baseline(w, dev_inputs):
                    f"{w.H} heads, d={w.d}) on the host, inputs copied from HBM; "
                    f"{dt:.2f} s"),
     }
+
+
+def timed_calls(call, steps: int, stream, profile: bool):
+    """`steps` calls bracketed by events on `stream`, with a device
+    synchronization on both sides.  Returns (ms per call, wall seconds, the
+    library's per-stage records or None).  With `profile` the library also
+    brackets every kernel launch with HIP events on the stream; those events
+    cost a few microseconds per launch, so the headline timing runs without
+    them and the stage durations come from a second pass with them."""
+    import torch
+
+    from relu_linear_attention_amd import gla
+
+    if profile:
+        gla.gla_profile_enable(True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        call()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stages = None
+    if profile:
+        stages = gla.gla_profile_read()
+        gla.gla_profile_enable(False)
+    return start.elapsed_time(stop) / steps, wall, stages
 
 
 def block_step_leg(steps: int, warmup: int, workload: str = "720p_block_causal"):
@@ -203,17 +233,8 @@ def backward_leg(w, x, steps: int, warmup: int):
 
     for _ in range(warmup):
         call()
-    torch.cuda.synchronize()
-    gla.gla_profile_enable(True)
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(steps):
-        call()
-    stop.record(stream)
-    torch.cuda.synchronize()
-    stages = gla.gla_profile_read()
-    gla.gla_profile_enable(False)
-    ms = start.elapsed_time(stop) / steps
+    ms, _, _ = timed_calls(call, steps, stream, profile=False)
+    _, _, stages = timed_calls(call, steps, stream, profile=True)
     nbytes = 9 * w.B * w.N * w.H * w.d * w.elem_bytes
     gbps = nbytes / (ms * 1e-3) / 1e9
     stage_ms = {k: (v / n if n else None) for k, (n, v) in stages.items()}
@@ -272,17 +293,8 @@ def token_causal_leg(w, x, steps: int, warmup: int, oracle_frames: int = 2):
 
     for _ in range(warmup):
         call()
-    torch.cuda.synchronize()
-    gla.gla_profile_enable(True)
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(steps):
-        call()
-    stop.record(stream)
-    torch.cuda.synchronize()
-    stages = gla.gla_profile_read()
-    gla.gla_profile_enable(False)
-    ms = start.elapsed_time(stop) / steps
+    ms, _, _ = timed_calls(call, steps, stream, profile=False)
+    _, _, stages = timed_calls(call, steps, stream, profile=True)
     nbytes = 5 * w.B * w.N * w.H * w.d * w.elem_bytes
     gbps = nbytes / (ms * 1e-3) / 1e9
     stage_ms = {k: (v / n if n else None) for k, (n, v) in stages.items()}
@@ -406,21 +418,11 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps, each kernel bracketed by HIP events on `stream`
-    gla.gla_profile_enable(True)
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    stop.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    stages = gla.gla_profile_read()
-    gla.gla_profile_enable(False)
-    total_ms = start.elapsed_time(stop)
-    ms_per_step = total_ms / args.steps
+    # timed region: K steps between events on `stream`; then K more steps with
+    # every kernel bracketed by HIP events on `stream` for the per-kernel
+    # durations (the roofline of the dominant kernel)
+    ms_per_step, wall, _ = timed_calls(step, args.steps, stream, profile=False)
+    _, _, stages = timed_calls(step, args.steps, stream, profile=True)
     tokens = w.B * w.N
     elem = w.B * w.N * w.H * w.d * w.elem_bytes
     algo_bytes = {"state_partials": 2 * elem, "apply": 3 * elem}
