@@ -350,7 +350,7 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
                       "ms": ms, "GBps_read_plus_write": 2 * nbytes / ms / 1e6}))
 
 
-def main() -> int:
+def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     # The GPU reaches its steady clocks only after a few dozen calls: with 8
@@ -370,11 +370,12 @@ def main() -> int:
     ap.add_argument("--only-leg", choices=["gated", "backward", "token_causal", "block_step"],
                     help="run only this measurement and print its JSON (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true")
-    args = ap.parse_args()
+    args = ap.parse_args(argv)
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the operator is "
-              "benchmarked at one GPU's share; see the sharding notes in DESIGN.md",
+              "benchmarked at one GPU's share; more GPUs would shard the (batch, head) units or the "
+              "token axis, which is not built",
               file=sys.stderr)
         return 2
 
