@@ -274,14 +274,7 @@ __global__ __launch_bounds__(kBlock) void bwd_reduce_kernel(const float *__restr
   float4 run = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int64_t blk = nb - 1; blk >= 0; --blk) {
     const int64_t unit = bh * nb + blk;
-    const float *src = partials + unit * Rb * stride + i4;
-    for (int64_t c = 0; c < Rb; ++c) {
-      const float4 x = *reinterpret_cast<const float4 *>(src + c * stride);
-      run.x += x.x;
-      run.y += x.y;
-      run.z += x.z;
-      run.w += x.w;
-    }
+    add_partials(run, partials + unit * Rb * stride + i4, stride, 0, Rb);
     *reinterpret_cast<float4 *>(grads + unit * stride + i4) = run;
   }
 }

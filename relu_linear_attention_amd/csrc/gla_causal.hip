@@ -44,13 +44,9 @@ __global__ __launch_bounds__(kBlock) void range_prefix_kernel(const float *__res
   int64_t c = 0;
   for (int64_t r = 0; r < R; ++r) {
     *reinterpret_cast<float4 *>(dst + r * stride) = run;
-    for (const int64_t c_end = min((r + 1) * m, C); c < c_end; ++c) {
-      const float4 x = *reinterpret_cast<const float4 *>(src + c * stride);
-      run.x += x.x;
-      run.y += x.y;
-      run.z += x.z;
-      run.w += x.w;
-    }
+    const int64_t c_end = min((r + 1) * m, C);
+    add_partials(run, src, stride, c, c_end);
+    c = max(c, c_end);
   }
 }
 

@@ -81,14 +81,7 @@ __global__ __launch_bounds__(kBlock) void reduce_prefix_kernel(
   }
   for (int64_t blk = 0; blk < nb; ++blk) {
     const int64_t unit = bh * nb + blk;
-    const float *src = partials + unit * C * stride + i4;
-    for (int64_t c = 0; c < C; ++c) {
-      float4 x = *reinterpret_cast<const float4 *>(src + c * stride);
-      run.x += x.x;
-      run.y += x.y;
-      run.z += x.z;
-      run.w += x.w;
-    }
+    add_partials(run, partials + unit * C * stride + i4, stride, 0, C);
     *reinterpret_cast<float4 *>(states + unit * stride + i4) = run;
     if (frags != nullptr && i4 < (int64_t)d * d) {
       const float vals[4] = {run.x, run.y, run.z, run.w};

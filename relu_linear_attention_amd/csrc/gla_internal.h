@@ -46,6 +46,32 @@ constexpr int64_t kStateTile = 64;   // tokens per step of the matrix-core state
 constexpr int64_t kApplyTile = 16;   // tokens per wave step of the matrix-core apply kernel (8 waves)
 constexpr int64_t kPartialStride(int64_t d) { return d * d + d; }
 
+// run += src[c * stride .. + 3] for c = c0, c0 + 1, ..., c1 - 1, added in
+// that order (so the sum is bitwise that of the plain loop), with eight
+// loads in flight: the reduce kernels are latency-bound with one partial per
+// round trip.  Indices past c1 - 1 are clamped (their values are loaded and
+// dropped), so every load is unconditional.
+__device__ __forceinline__ void add_partials(float4 &run, const float *src, int64_t stride,
+                                             int64_t c0, int64_t c1) {
+  for (int64_t c = c0; c < c1; c += 8) {
+    float4 x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t cj = c + j < c1 ? c + j : c1 - 1;
+      x[j] = *reinterpret_cast<const float4 *>(src + cj * stride);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (c + j < c1) {
+        run.x += x[j].x;
+        run.y += x[j].y;
+        run.z += x[j].z;
+        run.w += x[j].w;
+      }
+    }
+  }
+}
+
 // LDS budget of the RoPE table slice kept by the matrix-core kernels
 // (float2 entries).
 constexpr int64_t kStateTabEntries = 6144;  // 48 KiB
