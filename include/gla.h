@@ -33,8 +33,10 @@
  *   pos_axis * rope_theta^(-2i/d_axis).  rope_theta <= 0 disables the
  *   rotation.  Positions are the integer grid indices starting at 0.
  * Supported sizes.  B, H, T, Hs, Ws >= 1; 16 <= d <= 128 with d % 16 == 0.
- *   bf16 with d = 64 or d = 128 runs on the matrix-core kernels; every other
- *   supported case runs on the vector kernels.
+ *   bf16 with d = 64 or d = 128 and 16-byte-aligned tensors runs on the
+ *   matrix-core kernels; every other supported case (fp32, other d,
+ *   misaligned tensors, grids whose table slices exceed the kernels' LDS)
+ *   runs on the vector kernels.
  * Memory.  Every tensor pointer is device memory owned by the caller; the
  *   library neither frees nor keeps any of them.  out may not overlap an
  *   input.
