@@ -1,7 +1,13 @@
 """Parity of the gated mixer (gla_gated_forward: write gate beta and RMSNorm
 of num/den, "SANA-Video 2.0" Section 2 Eq. (1) short of W_o) with the fp64
-oracle, through the C ABI.  Bar: max |gpu - oracle| / (|oracle| + 1e-3)
-<= 1e-4 (fp32), <= 1e-2 (bf16)."""
+oracle, through the C ABI.  Bar: max |gpu - oracle| / (|oracle| + floor)
+<= 1e-4 (fp32), <= 1e-2 (bf16), with the operator's floor of 1e-3 without
+the RMSNorm.  The RMSNorm rescales every token's output to the scale of its
+weight (about 1, where the plain operator's outputs are about 0.23/sqrt(N)),
+so there the floor is relative to that scale, as for the gradients: 1e-2 *
+max|oracle| (fp32), 1e-3 * max|oracle| (bf16).  An absolute 1e-3 would ask
+fp32 for one rounding unit of the scale near zero crossings (measured: rel-l2
+1.9e-7, largest error 4.5e-7 of max|oracle| on 594 tokens)."""
 import numpy as np
 import pytest
 
@@ -21,6 +27,20 @@ def _gates(B, N, H, d, dtype, seed):
     if dtype == "bf16":
         beta, w = round_to_bf16(beta), round_to_bf16(w)
     return beta, w
+
+
+NORM_FLOOR = {"f32": 1e-2, "bf16": 1e-3}
+
+
+def gated_err(got, ref, dtype: str, rms: bool) -> float:
+    """The bar's error: the operator's floor (1e-3) without the RMSNorm, a
+    floor relative to the output scale with it."""
+    if not rms:
+        return max_rel_err(got, ref)
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    floor = NORM_FLOOR[dtype] * float(np.max(np.abs(ref)))
+    return float(np.max(np.abs(got - ref) / (np.abs(ref) + floor)))
 
 
 def _dev(a, dtype):
@@ -59,7 +79,7 @@ def test_gated_matches_oracle(case, use_beta, use_w):
                           None if w is None else _dev(w, dtype), out, (T, Hs, Ws), F)
     torch.cuda.synchronize()
     ref = oracle.gated_forward(x["q"], x["k"], x["v"], x["g"], beta, w, (T, Hs, Ws), F)
-    err = max_rel_err(to_host_f32(out), ref)
+    err = gated_err(to_host_f32(out), ref, dtype, w is not None)
     print(f"  max rel err {err:.3e}", flush=True)
     assert err <= TOL[dtype]
 
@@ -97,6 +117,6 @@ def test_full_size_gated_720p():
     torch.cuda.synchronize()
     host = {n: t.float().cpu().numpy() for n, t in dev.items()}
     ref = oracle.gated_forward(host["q"], host["k"], host["v"], host["g"], beta, w, w_.grid)
-    err = max_rel_err(out.float().cpu().numpy(), ref)
+    err = gated_err(out.float().cpu().numpy(), ref, "bf16", True)
     print(f"  max rel err {err:.3e}", flush=True)
     assert err <= TOL["bf16"]
