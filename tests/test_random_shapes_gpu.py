@@ -2,8 +2,9 @@
 batch 1-2, grids up to 12 x 24 x 30 (one to several token ranges, ragged
 tails), 1-3 heads, bf16 at d = 64, 128 (matrix-core kernels) and fp32 at
 d = 16..128 (vector kernels), non-causal and block-causal.  Each case runs the
-forward, the token-causal form, the gradients and the gated mixer (beta and
-RMSNorm) with the bars of their own tests; dq and dk of blocks under four
+forward (block-causal cases also streamed through the block step), the
+token-causal form, the gradients and the gated mixer (beta and RMSNorm) with
+the bars of their own tests; dq and dk of blocks under four
 tokens are left to test_one_token_blocks_backward (their terms cancel)."""
 import random
 
@@ -57,8 +58,24 @@ def test_random_shape(case):
     out_tc = torch.empty_like(dev["q"])
     gla.gla_token_causal_forward(dev["q"], dev["k"], dev["v"], dev["g"], out_tc, grid)
     torch.cuda.synchronize()
-    assert max_rel_err(out.float().cpu().numpy(),
-                       oracle.forward(x["q"], x["k"], x["v"], x["g"], grid, F)) <= tol
+    ref_fwd = oracle.forward(x["q"], x["k"], x["v"], x["g"], grid, F)
+    assert max_rel_err(out.float().cpu().numpy(), ref_fwd) <= tol
+    if F:
+        # the same layer streamed block by block through gla_block_step (the
+        # inclusive step equals the block-causal output of its block)
+        hw = Hs * Ws
+        S = torch.zeros((B, H, d, d), dtype=torch.float32, device="cuda")
+        z = torch.zeros((B, H, d), dtype=torch.float32, device="cuda")
+        out_bs = torch.empty_like(dev["q"])
+        for t0 in range(0, T, F):
+            sl = slice(t0 * hw, (t0 + F) * hw)
+            blk = {n: t[:, sl].contiguous() for n, t in dev.items()}
+            o = torch.empty_like(blk["q"])
+            gla.gla_block_step(blk["q"], blk["k"], blk["v"], blk["g"], o, S, z, (F, Hs, Ws), t0,
+                               True)
+            out_bs[:, sl] = o
+        torch.cuda.synchronize()
+        assert max_rel_err(out_bs.float().cpu().numpy(), ref_fwd) <= tol
     assert max_rel_err(out_tc.float().cpu().numpy(),
                        oracle.token_causal(x["q"], x["k"], x["v"], x["g"], grid)) <= tol
 
