@@ -392,8 +392,12 @@ gla_status timed_launch(int stage, hipStream_t stream, const char *what, F &&lau
   }
   StageRecord rec{stage, nullptr, nullptr};
   if (on) {
-    hipError_t e = hipEventCreate(&rec.start);
-    if (e == hipSuccess) e = hipEventCreate(&rec.stop);
+    // timing-only events: without the system-scope fence (a write-back and
+    // invalidation of the caches) a recorded event does not change how the
+    // next kernel runs, so each stage takes the time it takes between the
+    // other stages of an unprofiled call
+    hipError_t e = hipEventCreateWithFlags(&rec.start, hipEventDisableSystemFence);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&rec.stop, hipEventDisableSystemFence);
     if (e == hipSuccess) e = hipEventRecord(rec.start, stream);
     if (e != hipSuccess) return hip_fail(e, "stage timing event");
   }

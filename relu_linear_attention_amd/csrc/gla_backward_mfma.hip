@@ -231,17 +231,17 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_kernel(
   constexpr int64_t kStep = 16 * NW;
   uint4 ka[KS], va[KS], kb2[KS], vb2[KS];
   int64_t tile = n_begin + 16 * wave;
-  if (tile < n_end) fetch(tile, ka, va);
-  if (tile + kStep < n_end) fetch(tile + kStep, kb2, vb2);
+  fetch(tile, ka, va);
+  asm volatile("" ::: "memory");  // the first tile's loads are issued first
+  fetch(tile + kStep, kb2, vb2);
   while (tile < n_end) {
     process(tile, ka, va);
-    if (tile + 2 * kStep < n_end) fetch(tile + 2 * kStep, ka, va);
-    tile += kStep;
-    if (tile >= n_end) break;
-    process(tile, kb2, vb2);
-    if (tile + 2 * kStep < n_end) fetch(tile + 2 * kStep, kb2, vb2);
-    tile += kStep;
+    fetch(tile + 2 * kStep, ka, va);
+    if (tile + kStep < n_end) process(tile + kStep, kb2, vb2);
+    fetch(tile + 3 * kStep, kb2, vb2);
+    tile += 2 * kStep;
   }
+  __builtin_amdgcn_s_waitcnt(0);  // prefetches past the range are still in flight
 }
 
 // ---------------------------------------------------------------- query side

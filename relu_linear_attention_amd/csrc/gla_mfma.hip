@@ -526,21 +526,25 @@ __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
 
   // Two tiles of loads stay in flight per wave: buffer A holds tile i while
   // B receives tile i+1; once tile i is done, A is refilled with tile i+2
-  // before tile i+1 (in B) is processed, and so on.
+  // before tile i+1 (in B) is processed, and so on.  The refills are
+  // unconditional (tiles past the range read as zeros and are never
+  // processed): with a branch around them the compiler cannot tell which
+  // loads are still outstanding at the top of the loop and waits for all of
+  // them, the next tile's included, which leaves one tile in flight.
   constexpr int64_t kStep = 16 * NW;
   uint4 qa[KS], ga[St::kPasses], qb[KS], gb[St::kPasses];
   int64_t tile = n_begin + 16 * wave;
-  if (tile < n_end) fetch(tile, qa, ga);
-  if (tile + kStep < n_end) fetch(tile + kStep, qb, gb);
+  fetch(tile, qa, ga);
+  asm volatile("" ::: "memory");  // the first tile's loads are issued first
+  fetch(tile + kStep, qb, gb);
   while (tile < n_end) {
     process(tile, qa, ga);
-    if (tile + 2 * kStep < n_end) fetch(tile + 2 * kStep, qa, ga);
-    tile += kStep;
-    if (tile >= n_end) break;
-    process(tile, qb, gb);
-    if (tile + 2 * kStep < n_end) fetch(tile + 2 * kStep, qb, gb);
-    tile += kStep;
+    fetch(tile + 2 * kStep, qa, ga);
+    if (tile + kStep < n_end) process(tile + kStep, qb, gb);
+    fetch(tile + 3 * kStep, qb, gb);
+    tile += 2 * kStep;
   }
+  __builtin_amdgcn_s_waitcnt(0);  // prefetches past the range are still in flight
 }
 
 template <int D, bool kBeta>
