@@ -241,8 +241,10 @@ gla_status make_plan(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, in
   if (P.mfma) {
     // buffer offsets of a token range are 32-bit: keep range bytes < 2^31
     const int64_t row_bytes = H * d * 2;
-    // (the state kernel also addresses up to three 64-token steps past a chunk)
-    const int64_t max_tokens = (((int64_t)1 << 31) - 2 * d) / row_bytes - 3 * gla::kStateTile;
+    // (the state kernel also addresses up to three 64-token steps past a
+    // chunk, the apply and key/value gradient kernels up to three 128-token
+    // wave steps past a range: 512 rows cover both)
+    const int64_t max_tokens = (((int64_t)1 << 31) - 2 * d) / row_bytes - 512;
     if (P.Lc > max_tokens) {
       P.Lc = std::max<int64_t>(tile_s, max_tokens / tile_s * tile_s);
       P.C = ceil_div(P.L, P.Lc);
