@@ -117,6 +117,31 @@ def timed_calls(call, steps: int, stream, profile: bool):
     return start.elapsed_time(stop) / steps, wall, stages
 
 
+def same_bytes_reference(x, steps: int, warmup: int) -> dict:
+    """A library elementwise kernel over the apply kernel's algorithmic bytes:
+    torch.add(q, g) into a third tensor (two tensors read, one written, the
+    same shapes and dtype), timed like the headline pass.  Context for the
+    apply kernel's roofline fraction: what a plain two-in/one-out stream of
+    these tensors reaches on the same GPU in the same run."""
+    import torch
+
+    q, g = x["q"], x["g"]
+    o = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        torch.add(q, g, out=o)
+
+    for _ in range(warmup):
+        call()
+    ms, _, _ = timed_calls(call, steps, stream, profile=False)
+    nbytes = 3 * q.numel() * q.element_size()
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"op": f"torch.add(q, g, out=o), {str(q.dtype).replace('torch.', '')}",
+            "bytes_per_call": nbytes, "ms_per_call": ms, "GBps": gbps,
+            "frac": gbps / PEAK_HBM_GBPS}
+
+
 def block_step_leg(steps: int, warmup: int, workload: str = "720p_block_causal"):
     """The streaming block-causal step (gla_block_step): the layer's blocks of
     frames_per_block latent frames fed one at a time through the fp32 cache,
@@ -465,6 +490,7 @@ def main(argv=None) -> int:
             "algorithmic_bytes_per_launch": algo_bytes[dominant],
         },
         "stages_ms": stage_ms,
+        "same_bytes_reference": same_bytes_reference(x, args.steps, min(args.warmup, 20)),
         "path": {
             "algorithmic_bytes_per_step": 5 * elem,
             "GBps": 5 * elem / (ms_per_step * 1e-3) / 1e9,

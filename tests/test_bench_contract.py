@@ -39,6 +39,9 @@ def test_bench_line_480p(capsys):
     assert roof["frac"] == pytest.approx(roof["achieved"] / roof["peak"], rel=1e-9)
     assert 0.0 < roof["frac"] < 1.0
     assert roof["kernel"] in ("apply_mfma_kernel", "state_mfma_kernel")
+    ref = r["same_bytes_reference"]
+    assert ref["bytes_per_call"] == roof["algorithmic_bytes_per_launch"] or roof["kernel"] != "apply_mfma_kernel"
+    assert 0.0 < ref["frac"] < 1.0
     # the per-stage durations of the dominant kernel fit inside a step
     assert all(v is None or 0.0 < v < r["ms_per_step"] for v in r["stages_ms"].values())
     for leg in ("backward", "token_causal"):
