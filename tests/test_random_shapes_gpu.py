@@ -1,4 +1,4 @@
-"""Seeded random shapes through every entry point against the fp64 oracle:
+"""48 seeded random shapes through every entry point against the fp64 oracle:
 batch 1-2, grids up to 12 x 24 x 30 (one to several token ranges, ragged
 tails), 1-3 heads, bf16 at d = 64, 128 (matrix-core kernels) and fp32 at
 d = 16..128 (vector kernels), non-causal and block-causal.  Each case runs the
@@ -22,10 +22,10 @@ from tests.test_token_causal_gpu import token_causal_err
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
 
 
-def _cases(seed: int, n: int):
+def _cases(seed: int, n: int, first: int = 0):
     rng = random.Random(seed)
     out = []
-    for i in range(n):
+    for i in range(first, first + n):
         big = i % 3 == 2
         B = rng.choice([1, 1, 2])
         T = rng.randint(1, 12 if big else 6)
@@ -39,7 +39,8 @@ def _cases(seed: int, n: int):
     return out
 
 
-@pytest.mark.parametrize("case", _cases(2024, 24), ids=lambda c: f"case{c[0]}")
+@pytest.mark.parametrize("case", _cases(2024, 24) + _cases(2025, 24, first=24),
+                         ids=lambda c: f"case{c[0]}")
 def test_random_shape(case):
     import torch
 
