@@ -119,6 +119,24 @@ gla_status gla_forward_ws(const void *q, const void *k, const void *v, const voi
                           void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * gla_forward_ws without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, results and errors as gla_forward_ws (frames_per_block = 0:
+ * non-causal), bitwise identical to it.  The kernels use a static scratch
+ * array of 64 MiB that the library holds on each device it runs on until
+ * the process ends; a call whose workspace (gla_workspace_bytes) exceeds it
+ * returns GLA_ERR_UNSUPPORTED before enqueueing anything.  Every call on a
+ * device shares that device's array (each call fully rewrites what it
+ * reads, so nothing carries over between calls): calls that overlap in time
+ * on one device race, so order them on one stream.
+ */
+gla_status gla_forward_noalloc(const void *q, const void *k, const void *v, const void *g,
+                               void *out, int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws,
+                               int64_t d, int64_t frames_per_block, float rope_theta, float eps,
+                               gla_dtype dtype, hipStream_t stream);
+
+/*
  * Diagnostic export of the state and normaliser ("SANA-Video" Section 3.2
  * steps 3-4, Section 3.4 cache): S_out [B, H, nb, d, d] and z_out
  * [B, H, nb, d] as float (device memory), nb = T / frames_per_block (1 when

@@ -24,8 +24,9 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
-SOURCES = ["gla_common.hip", "gla_vector.hip", "gla_mfma.hip", "gla_backward.hip", "gla_backward_mfma.hip", "gla_causal.hip",
-           "gla_causal_mfma.hip",            "gla_api.cpp"]
+SOURCES = ["gla_common.hip", "gla_vector.hip", "gla_mfma.hip", "gla_backward.hip",
+           "gla_backward_mfma.hip", "gla_causal.hip", "gla_causal_mfma.hip", "gla_noalloc.hip",
+           "gla_api.cpp"]
 
 
 def _compile(src: str) -> str:

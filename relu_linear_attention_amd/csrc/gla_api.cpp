@@ -514,7 +514,7 @@ gla_status forward_impl(const void *q, const void *k, const void *v, const void 
                         int64_t F, float theta, float eps, gla_dtype dtype, void *ws,
                         size_t ws_bytes, bool own_ws, hipStream_t stream,
                         const Step *step = nullptr, const Gates *gates = nullptr,
-                        float rms_eps = 0.f) {
+                        float rms_eps = 0.f, bool scratch = false) {
   g_last_error[0] = '\0';
   gla_status st = check_sizes(B, H, T, Hs, Ws, d, F, dtype);
   if (st != GLA_OK) return st;
@@ -534,7 +534,7 @@ gla_status forward_impl(const void *q, const void *k, const void *v, const void 
     st = check_gates(*gates, out, bytes, B * T * Hs * Ws * H, d, dtype, rms_eps);
     if (st != GLA_OK) return st;
   }
-  if (!own_ws && (ws == nullptr || ((uintptr_t)ws & 255) != 0))
+  if (!own_ws && !scratch && (ws == nullptr || ((uintptr_t)ws & 255) != 0))
     return fail(GLA_ERR_INVALID_ARG, "workspace must be a non-null, 256-byte aligned pointer");
   int cus = 0;
   st = device_cus(&cus);
@@ -556,6 +556,18 @@ gla_status forward_impl(const void *q, const void *k, const void *v, const void 
       cache.S_out = step->S_io;
       cache.z_out = step->z_io;
     }
+  }
+  if (scratch) {
+    // the library's static scratch array of this device: no allocation
+    if (P.total_bytes > gla::kNoAllocScratchBytes)
+      return fail(GLA_ERR_UNSUPPORTED,
+                  "this call needs %zu bytes of scratch; gla_forward_noalloc has %zu per device "
+                  "(use gla_forward_ws with a larger workspace)",
+                  P.total_bytes, gla::kNoAllocScratchBytes);
+    void *mem = nullptr;
+    hipError_t e = gla::noalloc_scratch(&mem);
+    if (e != hipSuccess) return hip_fail(e, "scratch address (hipGetSymbolAddress)");
+    return run_plan(P, q, k, v, g, out, mem, stream, apply, cache, gt);
   }
   if (!own_ws) {
     if (ws_bytes < P.total_bytes)
@@ -629,6 +641,14 @@ gla_status gla_forward_ws(const void *q, const void *k, const void *v, const voi
                           void *workspace, size_t workspace_bytes, hipStream_t stream) {
   return forward_impl(q, k, v, g, out, B, H, T, Hs, Ws, d, frames_per_block, rope_theta, eps,
                       dtype, workspace, workspace_bytes, false, stream);
+}
+
+gla_status gla_forward_noalloc(const void *q, const void *k, const void *v, const void *g,
+                               void *out, int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws,
+                               int64_t d, int64_t frames_per_block, float rope_theta, float eps,
+                               gla_dtype dtype, hipStream_t stream) {
+  return forward_impl(q, k, v, g, out, B, H, T, Hs, Ws, d, frames_per_block, rope_theta, eps,
+                      dtype, nullptr, 0, false, stream, nullptr, nullptr, 0.f, true);
 }
 
 gla_status gla_state(const void *k, const void *v, float *S_out, float *z_out, int64_t B,

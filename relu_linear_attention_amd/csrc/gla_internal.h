@@ -72,6 +72,13 @@ __device__ __forceinline__ void add_partials(float4 &run, const float *src, int6
   }
 }
 
+// Size of the static scratch array behind gla_forward_noalloc (one copy per
+// device, held until the process ends).
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+// Device address of the current device's scratch array (looked up once per
+// device).
+hipError_t noalloc_scratch(void **ptr);
+
 // LDS budget of the RoPE table slice kept by the matrix-core kernels
 // (float2 entries).
 constexpr int64_t kStateTabEntries = 6144;  // 48 KiB

@@ -25,7 +25,7 @@ GLA_NUM_STAGES = 6
 # every symbol include/gla.h declares
 EXPORTS = (
     "gla_forward", "gla_block_causal_forward", "gla_workspace_bytes", "gla_forward_ws",
-    "gla_state", "gla_block_step", "gla_gated_forward", "gla_backward",
+    "gla_forward_noalloc", "gla_state", "gla_block_step", "gla_gated_forward", "gla_backward",
     "gla_backward_workspace_bytes", "gla_token_causal_forward", "gla_token_causal_workspace_bytes",
     "gla_status_string", "gla_last_error", "gla_profile_enable",
     "gla_profile_read", "gla_stage_name", "gla_uses_matrix_cores",
@@ -60,6 +60,7 @@ def load():
                                                  ctypes.POINTER(ctypes.c_size_t)]
     lib.gla_forward_ws.argtypes = (tensors5 + sizes6 + [_i64, _f, _f, ctypes.c_int, _vp,
                                                         ctypes.c_size_t, _vp])
+    lib.gla_forward_noalloc.argtypes = tensors5 + sizes6 + [_i64, _f, _f, ctypes.c_int, _vp]
     lib.gla_state.argtypes = [_vp] * 4 + sizes6 + [_i64, _f, ctypes.c_int, _vp]
     lib.gla_block_step.argtypes = (tensors5 + [_vp, _vp] + sizes6 + [_i64, ctypes.c_int, _f, _f,
                                                                     ctypes.c_int, _vp,
@@ -75,7 +76,7 @@ def load():
     lib.gla_token_causal_workspace_bytes.argtypes = sizes6 + [ctypes.c_int,
                                                               ctypes.POINTER(ctypes.c_size_t)]
     for name in ("gla_forward", "gla_block_causal_forward", "gla_workspace_bytes",
-                 "gla_forward_ws", "gla_state", "gla_block_step", "gla_gated_forward",
+                 "gla_forward_ws", "gla_forward_noalloc", "gla_state", "gla_block_step", "gla_gated_forward",
                  "gla_backward", "gla_backward_workspace_bytes", "gla_token_causal_forward",
                  "gla_token_causal_workspace_bytes", "gla_profile_enable",
                  "gla_profile_read"):
@@ -184,6 +185,18 @@ def gla_forward_ws(q, k, v, g, out, grid, workspace, frames_per_block=0, rope_th
                                _ptr(workspace), workspace.numel() * workspace.element_size(),
                                _stream_handle(stream))
     _check(st, "gla_forward_ws")
+
+
+def gla_forward_noalloc(q, k, v, g, out, grid, frames_per_block=0, rope_theta=10000.0, eps=1e-6,
+                        stream=None):
+    """gla_forward_ws without a workspace: the library's static per-device
+    scratch array serves instead, and nothing is allocated."""
+    _check_tensors(q, k, v, g, out)
+    B, H, T, Hs, Ws, d = _sizes(q, grid)
+    st = load().gla_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(out), B, H, T, Hs,
+                                    Ws, d, frames_per_block, rope_theta, eps, _dtype_code(q),
+                                    _stream_handle(stream))
+    _check(st, "gla_forward_noalloc")
 
 
 def gla_state(k, v, S_out, z_out, grid, frames_per_block=0, rope_theta=10000.0, stream=None):
