@@ -256,13 +256,36 @@ gla_status make_plan(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, in
     if (P.Lc > max_tokens || P.Lr > max_tokens) P.mfma = false;
   }
   if (P.mfma) {
+    // Register-resident output stage: four waves per workgroup take hpw
+    // heads of one (batch, block) (four when H allows, so a token's rows of
+    // four heads move together) and 4/hpw tiles of 16 tokens each per item.
+    // One workgroup per compute unit: am workgroups per block share its
+    // items in turn.  A block is cut into super-ranges only when the RoPE
+    // table rows of the whole block would not fit in LDS beside the staging
+    // tiles.
+    P.hpw = H % 4 == 0 ? 4 : (H % 2 == 0 ? 2 : 1);
+    P.ag = B * P.nb * (H / P.hpw);
+    const int64_t item = 16 * (4 / P.hpw);
+    const int64_t items = ceil_div(P.L, item);
+    P.ar = 1;
+    for (;;) {
+      P.air = ceil_div(items, P.ar);
+      if (gla::apply_reg_lds_bytes(P) <= 160 * 1024 || P.air == 1) break;
+      P.ar *= 2;
+    }
+    if (gla::apply_reg_lds_bytes(P) > 160 * 1024) P.mfma = false;
+    const int64_t sranges = P.ag * P.ar;
+    P.am = std::max<int64_t>(1, std::min<int64_t>(P.air, cus / std::max<int64_t>(1, sranges)));
+    if (sranges * P.am > 0x7fffffff) P.mfma = false;
+    // a 16-row tile of one head must be addressable with 32-bit offsets
+    if ((int64_t)16 * H * d * 2 >= ((int64_t)1 << 31)) P.mfma = false;
+  }
+  if (P.mfma) {
     // LDS of the two matrix-core kernels must fit the 160 KiB of a CU
     auto slice = [&](int64_t len) { return spatial_entries + (ceil_div(len, hw) + 1) * pt; };
     const int64_t lds_state = 3 * d * 128 + slice(P.Lc) * 8;
-    const int64_t lds_apply =
-        d * d * 4 + (d / 32) * 64 * 16 + d * 4 + 8 * 16 * (2 * d + 16) + slice(P.Lr) * 8;
-    if (std::max(lds_state, lds_apply) > 160 * 1024) return fail(GLA_ERR_UNSUPPORTED,
-        "internal: LDS plan of %lld bytes exceeds the CU", (long long)std::max(lds_state, lds_apply));
+    if (lds_state > 160 * 1024) return fail(GLA_ERR_UNSUPPORTED,
+        "internal: LDS plan of %lld bytes exceeds the CU", (long long)lds_state);
   }
   // Backward: vector kernels, about four workgroups per compute unit of
   // 16..4096 tokens each.
@@ -480,7 +503,7 @@ gla_status run_plan(const Plan &P, const void *q, const void *k, const void *v, 
   if (st != GLA_OK) return st;
   if (!apply) return GLA_OK;
   return timed_launch(3, stream, "apply kernel", [&] {
-    return P.mfma ? gla::launch_apply_mfma(P, q, g, states, frags, tab, gates.rms_w, out, stream)
+    return P.mfma ? gla::launch_apply_reg(P, q, g, states, frags, tab, gates.rms_w, out, stream)
                   : gla::launch_apply_generic(P, q, g, states, tab, gates.rms_w, out, stream);
   });
 }

@@ -28,6 +28,11 @@ struct Plan {
   int64_t C, Lc;  // state chunks per unit, tokens per chunk
   int64_t R, Lr;  // apply ranges per unit, tokens per range
   int64_t Rb, Lb; // backward ranges per unit, tokens per range
+  // register-resident output stage (matrix cores): workgroups of four waves
+  // own hpw heads of one (batch, block); ag head groups, each block cut into
+  // ar super-ranges of air items (an item = 16 * 4/hpw tokens x hpw heads),
+  // am workgroups per super-range taking its items in turn
+  int64_t hpw, ag, ar, air, am;
   bool bf16;      // element type of q, k, v, g, out
   bool mfma;      // matrix-core kernels (bf16, d = 64 or 128)
   float theta, eps;
@@ -113,9 +118,13 @@ hipError_t launch_apply_generic(const Plan &p, const void *q, const void *g, con
 // Matrix-core kernels (bf16, d = 64 or 128).
 hipError_t launch_state_mfma(const Plan &p, const void *k, const void *v, const void *beta,
                              const float2 *tab, float *partials, hipStream_t stream);
-hipError_t launch_apply_mfma(const Plan &p, const void *q, const void *g, const float *states,
-                             const uint16_t *frags, const float2 *tab, const void *rms_w,
-                             void *out, hipStream_t stream);
+// Register-resident output stage (bf16, d = 64 or 128): frags holds S^T of
+// every unit as bf16 hi and lo matrix-core A fragments,
+// [units][part][d/32][d/16][64 lanes][8]; its LDS bytes for the plan.
+hipError_t launch_apply_reg(const Plan &p, const void *q, const void *g, const float *states,
+                            const uint16_t *frags, const float2 *tab, const void *rms_w,
+                            void *out, hipStream_t stream);
+size_t apply_reg_lds_bytes(const Plan &p);
 
 // Token-causal form.  The state stage writes one partial per chunk of Lc
 // tokens (units = B*H, one block each); the prefix kernel writes, for every

@@ -1,8 +1,7 @@
-// Matrix-core kernels of the operator for bf16 tensors with head size 64 or
-// 128 (gfx950, v_mfma_f32_32x32x16_bf16, fp32 accumulation).
+// State stage of the operator on the matrix cores for bf16 tensors with head
+// size 64 or 128 (gfx950, v_mfma_f32_32x32x16_bf16, fp32 accumulation):
 //
-//   state:  S_c = sum_{n in chunk} RoPE_n(phi(k_n))^T v_n,  z_c = sum phi(k_n)
-//   apply:  o_i = (RoPE_i(phi(q_i)) S) / (phi(q_i) . z + eps) * sigmoid(g_i)
+//   S_c = sum_{n in chunk} RoPE_n(phi(k_n))^T v_n,  z_c = sum phi(k_n)
 //
 // "SANA-Video" notes page, Section 3.2 (phi = ReLU, RoPE after ReLU for the
 // numerator only, un-rotated denominator); "SANA-Video 2.0" Section 2
@@ -14,9 +13,8 @@
 //   B (16 x 32):  lane l holds B[8*(l/32) + j][l % 32]
 //   C (32 x 32):  lane l, value i holds C[8*(i/4) + 4*(l/32) + i%4][l % 32]
 //
-// The contraction of the state is over tokens, so k and v are staged in LDS
-// transposed (feature-major); the contraction of the apply stage is over
-// features, so q is loaded straight from HBM in the B layout.
+// The contraction is over tokens, so k and v are staged in LDS and read
+// back transposed (feature-major).
 
 #include <hip/hip_runtime.h>
 
@@ -26,14 +24,9 @@
 namespace gla {
 namespace {
 
-// Policies of the streams of the two stages.  Measured over whole
-// forward calls at 720p/81f: streaming the k and v reads of the state stage
-// saves about 3% per call; streaming the q and g reads or the out writes of
-// the apply stage (non-temporal, also at system scope) changes nothing
-// measurable, since apply's limit is its operand-layout q loads.
+// k and v are read once: streaming (non-temporal) loads, measured about 3%
+// faster per call at 720p/81f than normal ones.
 constexpr int kStateLoadPolicy = kCacheStream;
-constexpr int kApplyLoadPolicy = kCacheNormal;
-constexpr int kApplyStorePolicy = kCacheNormal;
 
 // ---------------------------------------------------------------- state
 
@@ -269,284 +262,6 @@ __global__ __launch_bounds__(kStateThreads<D>, kStateThreads<D> / 128) void stat
   }
 }
 
-// ---------------------------------------------------------------- apply
-
-// 16x16x32 bf16 matrix-core layout used by the apply stage:
-//   A (16 x 32):  lane l holds A[l % 16][8*(l/16) + j], j = 0..7
-//   B (32 x 16):  lane l holds B[8*(l/16) + j][l % 16]
-//   C (16 x 16):  lane l, value i holds C[4*(l/16) + i][l % 16]
-//
-// One workgroup (8 waves) per (unit, token range); each wave takes 16-token
-// tiles.  LDS holds the unit's S^T as bf16 A fragments in two parts, S ~
-// S_hi + S_lo (written by the reduce stage), the A fragments of the
-// denominator (rows 0, 4, 8, 12 carry z rounded to bf16 and rows 1, 5, 9, 13
-// the bf16 rounding of the remainder, so C values 0 and 1 of every lane sum
-// to phi(q).z), the RoPE table rows of the range, and one staging tile per
-// wave.  Per tile and 32-feature step a lane loads 16 B of its token's q row;
-// ReLU(q) is exact in bf16 and is the B operand of the denominator;
-// RoPE(ReLU(q)) is split into bf16 hi + lo parts, and the numerator
-// accumulates hi*S_hi + lo*S_hi + hi*S_lo in fp32, which carries about 16
-// significant bits of every operand.  The gate g is loaded as whole 256-B
-// rows into the staging tile, read back in the accumulator layout, combined
-// with num / den, written back in place as bf16, and the tile leaves as whole
-// 256-B rows: full-row accesses keep HBM efficient where 8-B pieces per token
-// do not.
-constexpr int kApplyThreads = 512;
-
-
-//
-// kNorm: the RMSNorm of "SANA-Video 2.0" Eq. (1) between num/den and the
-// gate: y = num/den is scaled by 1/sqrt(mean over the D features of y^2 +
-// rms_eps) and by the weight w [D].  A token's D values are spread over the
-// four lanes l % 16 == token (32 each), summed with two lane exchanges.
-template <int D, bool kNorm>
-__global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ g,
-    const float *__restrict__ states, const uint16_t *__restrict__ frags,
-    const float2 *__restrict__ tab, const uint16_t *__restrict__ rms_w,
-    uint16_t *__restrict__ out, MArgs a) {
-  constexpr int KS = D / 32;  // 32-feature contraction steps
-  constexpr int ET = D / 16;  // 16-feature output tiles
-  constexpr int NW = kApplyThreads / 64;
-  extern __shared__ __align__(16) unsigned char lds[];
-  unsigned char *s_sh = lds;             // S hi part, row-major [p][e], units permuted
-  unsigned char *s_sl = lds + D * D * 2;  // S lo part
-  bf16x8 *s_zf = reinterpret_cast<bf16x8 *>(lds + D * D * 4);  // KS fragments x 64 lanes
-  float *s_w = reinterpret_cast<float *>(s_zf + KS * 64);        // RMSNorm weight (D)
-  using St = Stage<D>;
-  unsigned char *s_stage = reinterpret_cast<unsigned char *>(s_w + D);  // NW tiles
-  float2 *s_tab = reinterpret_cast<float2 *>(s_stage + NW * St::kBytes);
-
-  const int64_t wg = blockIdx.x;
-  const int64_t unit = wg / a.R, r = wg % a.R;
-  const int64_t bh = unit / a.nb, blk = unit % a.nb;
-  const int64_t b = bh / a.H, hd = bh % a.H;
-  const int64_t n_begin = blk * a.L + r * a.Lr;
-  const int64_t n_end = min(n_begin + a.Lr, (blk + 1) * a.L);
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform across the wave
-
-  {
-    // S hi then lo, 16-byte units i = (part, row, unit), unit permuted by row
-    const uint4 *src = reinterpret_cast<const uint4 *>(frags + unit * (int64_t)D * D * 2);
-    for (int i = tid; i < D * D * 2 / 8; i += kApplyThreads) {
-      const int u = i % (D / 8), row = (i / (D / 8)) % D, part = i / (D * D / 8);
-      *reinterpret_cast<uint4 *>(lds + part * D * D * 2 + SRow<D>::off(row, u)) = src[i];
-    }
-    const float *zsrc = states + unit * (int64_t)(D * D + D) + D * D;
-    for (int i = tid; i < KS * 64; i += kApplyThreads) {
-      const int ks = i >> 6, l = i & 63, row = l & 15;
-      bf16x8 f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) f[j] = (__bf16)0.f;
-      if ((row & 3) < 2) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float zv = zsrc[32 * ks + 8 * (l >> 4) + j];
-          const __bf16 zh = (__bf16)zv;
-          f[j] = (row & 1) ? (__bf16)(zv - (float)zh) : zh;
-        }
-      }
-      s_zf[i] = f;
-    }
-  }
-  if (kNorm)
-    for (int i = tid; i < D; i += kApplyThreads) s_w[i] = bf16_bits_to_float(rms_w[i]);
-  const TabSlice<D> ts = load_tab_slice<D>(s_tab, tab, a, n_begin, n_end);
-  __syncthreads();
-
-  const int nl = lane & 15, kg = lane >> 4;
-  // transposing-read offsets of the S parts: lane l (s = l%16, group
-  // g = l/16) points at row 8*g + s/4 (+ 32*ks + 4*half), column
-  // 16*et + 4*(s%4); the row's unit permutation depends only on s and g
-  int rd_s[ET];
-#pragma unroll
-  for (int et = 0; et < ET; ++et)
-    rd_s[et] = SRow<D>::off(8 * kg + (nl >> 2), 2 * et + ((nl & 3) >> 1)) + 8 * (nl & 1);
-  // row-wise lane mapping of the staging tile: in pass i lane l covers token
-  // i*kRowsPerPass + l/kLanesPerRow, features 8*(l%kLanesPerRow)..+7
-  const int rl = lane / St::kLanesPerRow, rc = 8 * (lane % St::kLanesPerRow);
-  // buffer resources over this range's rows of q, g and out
-  const int64_t first = ((b * a.N + n_begin) * a.H + hd) * D;
-  const uint32_t row_bytes = (uint32_t)(a.H * D * 2);
-  const uint32_t range_bytes = (uint32_t)(n_end - n_begin - 1) * row_bytes + 2 * D;
-  const __amdgpu_buffer_rsrc_t rq = head_rows_rsrc(q + first, range_bytes);
-  const __amdgpu_buffer_rsrc_t rg = head_rows_rsrc(g + first, range_bytes);
-  const __amdgpu_buffer_rsrc_t ro = head_rows_rsrc(out + first, range_bytes);
-  // loads of one tile: q in the B-operand layout, g as whole rows (rows past
-  // the range read as zeros)
-  auto fetch = [&](int64_t tile, uint4 (&qraw)[KS], uint4 (&grow)[St::kPasses]) {
-    const uint32_t rel = (uint32_t)(tile - n_begin);
-    const uint32_t qoff = (rel + nl) * row_bytes + 2 * 8 * kg;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qraw[ks] = buf_load16<kApplyLoadPolicy>(rq, qoff + 2 * 32 * ks);
-#pragma unroll
-    for (int i = 0; i < St::kPasses; ++i)
-      grow[i] = buf_load16<kApplyLoadPolicy>(rg, (rel + i * St::kRowsPerPass + rl) * row_bytes + 2 * rc);
-  };
-  // everything after the loads of one tile
-  auto process = [&](int64_t tile, const uint4 (&cq)[KS], const uint4 (&cg)[St::kPasses]) {
-      // An offset the compiler cannot see through (always 0) keeps the
-      // loop-invariant S-part reads inside the loop: hoisting all of them
-      // would need 256 registers per lane.  It is a register-only asm, so it
-      // does not make the compiler drain outstanding memory operations.
-      int opaque = 0;
-      asm volatile("" : "+v"(opaque));
-      const unsigned char *sh = s_sh + opaque, *sl = s_sl + opaque;
-      const int64_t n = tile + nl;
-      const bool valid = n < n_end;
-      int t, h, w;
-      token_pos(a, valid ? n : n_end - 1, t, h, w);
-
-      f32x4 acc[ET], accd = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int et = 0; et < ET; ++et) acc[et] = accd;
-
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint32_t qw[4] = {relu_bf16x2(cq[ks].x), relu_bf16x2(cq[ks].y),
-                                relu_bf16x2(cq[ks].z), relu_bf16x2(cq[ks].w)};
-        const bf16x8 bden = __builtin_bit_cast(bf16x8, make_uint4(qw[0], qw[1], qw[2], qw[3]));
-        float x[8];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          x[2 * m] = lo_bf16(qw[m]);
-          x[2 * m + 1] = hi_bf16(qw[m]);
-        }
-        int axis, pia;
-        pair_axis<D>(16 * ks + 4 * kg, axis, pia);
-        float2 c4[4];
-        ts.read(s_tab, ts.lookup(axis, pia).at(t, h, w), c4);
-        rotate4(x, c4);
-        uint32_t hw4[4], lw4[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) split_bf16x2(x[2 * m], x[2 * m + 1], hw4[m], lw4[m]);
-        const bf16x8 bh = __builtin_bit_cast(bf16x8, make_uint4(hw4[0], hw4[1], hw4[2], hw4[3]));
-        const bf16x8 bl = __builtin_bit_cast(bf16x8, make_uint4(lw4[0], lw4[1], lw4[2], lw4[3]));
-        accd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s_zf[ks * 64 + lane], bden, accd, 0, 0, 0);
-        // A = S^T fragments (rows e = 16*et + l%16, columns p = 32*ks +
-        // 8*(l/16) + j), read transposed from the row-major S parts, four
-        // output tiles at a time; the three products of a tile are issued
-        // round-robin over the four tiles so that consecutive matrix-core
-        // instructions do not depend on each other
-#pragma unroll
-        for (int eg = 0; eg < ET; eg += 4) {
-          bf16x8 ah[4], al[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int o0 = rd_s[eg + u] + (32 * ks) * (2 * D);
-            const int o1 = o0 + 4 * (2 * D);
-            const uint2 h0 = lds_read_tr16(sh + o0), h1 = lds_read_tr16(sh + o1);
-            const uint2 l0 = lds_read_tr16(sl + o0), l1 = lds_read_tr16(sl + o1);
-            ah[u] = __builtin_bit_cast(bf16x8, make_uint4(h0.x, h0.y, h1.x, h1.y));
-            al[u] = __builtin_bit_cast(bf16x8, make_uint4(l0.x, l0.y, l1.x, l1.y));
-          }
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            acc[eg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[u], bl, acc[eg + u], 0, 0, 0);
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            acc[eg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[u], bh, acc[eg + u], 0, 0, 0);
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            acc[eg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[u], bh, acc[eg + u], 0, 0, 0);
-        }
-      }
-
-      const float den = accd[0] + accd[1] + a.eps;
-      unsigned char *stage = s_stage + wave * St::kBytes;
-#pragma unroll
-      for (int i = 0; i < St::kPasses; ++i)
-        *reinterpret_cast<uint4 *>(stage + (i * St::kRowsPerPass + rl) * St::kRowBytes + 2 * rc) =
-            cg[i];
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      float scale = 0.f;  // (kNorm) 1 / (den * rms(num / den))
-      if (kNorm) {
-        // sum of num^2 over the token's D features: 32 in this lane, the rest
-        // in lanes l ^ 16, l ^ 32 and l ^ 48, added by two in-register lane
-        // swaps (gfx950 permlane16/32 swap: each returns the pair of values
-        // exchanged between rows, whose sum is this lane's plus its partner's)
-        float ss = 0.f;
-#pragma unroll
-        for (int et = 0; et < ET; ++et)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) ss = __builtin_fmaf(acc[et][i], acc[et][i], ss);
-        const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(ss), __float_as_uint(ss),
-                                                          false, false);
-        ss = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
-        const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss), __float_as_uint(ss),
-                                                          false, false);
-        ss = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
-        // rms(num / den) = sqrt(sum num^2 / (D den^2) + rms_eps)
-        const float inv_den = __builtin_amdgcn_rcpf(den);
-        scale = inv_den * rsqrtf(ss * inv_den * inv_den * (1.f / D) + a.rms_eps);
-      }
-#pragma unroll
-      for (int et = 0; et < ET; ++et) {
-        uint2 *slot = reinterpret_cast<uint2 *>(stage + nl * St::kRowBytes + 2 * (16 * et + 4 * kg));
-        const uint2 gw = *slot;
-        const float gv[4] = {lo_bf16(gw.x), hi_bf16(gw.x), lo_bf16(gw.y), hi_bf16(gw.y)};
-        float o[4];
-        if (kNorm) {
-          const float4 w4 = *reinterpret_cast<const float4 *>(s_w + 16 * et + 4 * kg);
-          const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            // num / den / rms * w * sigmoid(g)
-            const float e = __expf(-gv[i]);
-            o[i] = acc[et][i] * scale * wv[i] * __builtin_amdgcn_rcpf(1.f + e);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            // num / den * sigmoid(g) = num / (den * (1 + exp(-g)))
-            const float e = __expf(-gv[i]);
-            o[i] = acc[et][i] * __builtin_amdgcn_rcpf(__builtin_fmaf(den, e, den));
-          }
-        }
-        *slot = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-      for (int i = 0; i < St::kPasses; ++i) {
-        const int tok = i * St::kRowsPerPass + rl;
-        const uint4 ov = *reinterpret_cast<const uint4 *>(stage + tok * St::kRowBytes + 2 * rc);
-        buf_store16<kApplyStorePolicy>(ro, ((uint32_t)(tile - n_begin) + tok) * row_bytes + 2 * rc, ov);
-      }
-      // the next tile's first staging writes must not overtake these reads
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  };
-
-  // Two tiles of loads stay in flight per wave: buffer A holds tile i while
-  // B receives tile i+1; once tile i is done, A is refilled with tile i+2
-  // before tile i+1 (in B) is processed, and so on.  The refills are
-  // unconditional (tiles past the range read as zeros and are never
-  // processed): with a branch around them the compiler cannot tell which
-  // loads are still outstanding at the top of the loop and waits for all of
-  // them, the next tile's included, which leaves one tile in flight.
-  constexpr int64_t kStep = 16 * NW;
-  uint4 qa[KS], ga[St::kPasses], qb[KS], gb[St::kPasses];
-  int64_t tile = n_begin + 16 * wave;
-  fetch(tile, qa, ga);
-  asm volatile("" ::: "memory");  // the first tile's loads are issued first
-  fetch(tile + kStep, qb, gb);
-  while (tile < n_end) {
-    process(tile, qa, ga);
-    fetch(tile + 2 * kStep, qa, ga);
-    if (tile + kStep < n_end) process(tile + kStep, qb, gb);
-    fetch(tile + 3 * kStep, qb, gb);
-    tile += 2 * kStep;
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // prefetches past the range are still in flight
-}
-
 template <int D, bool kBeta>
 hipError_t state_d(const Plan &p, const void *k, const void *v, const void *beta,
                    const float2 *tab, float *part, hipStream_t stream) {
@@ -561,24 +276,6 @@ hipError_t state_d(const Plan &p, const void *k, const void *v, const void *beta
   return hipGetLastError();
 }
 
-template <int D, bool kNorm>
-hipError_t apply_d(const Plan &p, const void *q, const void *g, const float *states,
-                   const uint16_t *frags, const float2 *tab, const void *rms_w, void *out,
-                   hipStream_t stream) {
-  const size_t lds = (size_t)D * D * 2 * 2 + (size_t)(D / 32) * 64 * 16 + (size_t)D * 4 +
-                     (size_t)(kApplyThreads / 64) * Stage<D>::kBytes +
-                     tab_slice_entries(p, p.Lr) * sizeof(float2);
-  auto kern = apply_mfma_kernel<D, kNorm>;
-  hipError_t e = hipFuncSetAttribute((const void *)kern,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(p.units * p.R)), dim3(kApplyThreads), lds, stream,
-                     (const uint16_t *)q, (const uint16_t *)g, states, frags, tab,
-                     (const uint16_t *)rms_w, (uint16_t *)out,
-                     make_margs(p));
-  return hipGetLastError();
-}
-
 }  // namespace
 
 hipError_t launch_state_mfma(const Plan &p, const void *k, const void *v, const void *beta,
@@ -589,18 +286,6 @@ hipError_t launch_state_mfma(const Plan &p, const void *k, const void *v, const 
   if (p.d == 64)
     return beta ? state_d<64, true>(p, k, v, beta, tab, partials, stream)
                 : state_d<64, false>(p, k, v, beta, tab, partials, stream);
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_apply_mfma(const Plan &p, const void *q, const void *g, const float *states,
-                             const uint16_t *frags, const float2 *tab, const void *rms_w,
-                             void *out, hipStream_t stream) {
-  if (p.d == 128)
-    return rms_w ? apply_d<128, true>(p, q, g, states, frags, tab, rms_w, out, stream)
-                 : apply_d<128, false>(p, q, g, states, frags, tab, rms_w, out, stream);
-  if (p.d == 64)
-    return rms_w ? apply_d<64, true>(p, q, g, states, frags, tab, rms_w, out, stream)
-                 : apply_d<64, false>(p, q, g, states, frags, tab, rms_w, out, stream);
   return hipErrorInvalidValue;
 }
 

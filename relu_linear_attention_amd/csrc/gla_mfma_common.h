@@ -7,10 +7,30 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+#include <utility>
+#include <vector>
+
 #include "gla_internal.h"
 
 namespace gla {
 namespace {
+
+// Raises a kernel's dynamic-LDS limit to a compute unit's 160 KiB, once per
+// (kernel, device) rather than before every launch.
+inline hipError_t lds_limit_once(const void *kern) {
+  static std::mutex mu;
+  static std::vector<std::pair<const void *, int>> done;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(mu);
+  for (const auto &x : done)
+    if (x.first == kern && x.second == dev) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (e == hipSuccess) done.emplace_back(kern, dev);
+  return e;
+}
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -22,6 +42,7 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 struct MArgs {
   int64_t N, H, Hs, Ws;
   int64_t nb, L, C, Lc, R, Lr;
+  int64_t hpw, ag, ar, air, am;  // the register-resident output stage's work layout
   int64_t tab_h_off;  // global entry offset of the h rows (the w rows follow)
   FastDiv div_hw, div_w;  // by Hs*Ws and by Ws (token indices < 2^31)
   float eps;
@@ -349,6 +370,7 @@ inline MArgs make_margs(const Plan &p) {
   MArgs a;
   a.N = p.N; a.H = p.H; a.Hs = p.Hs; a.Ws = p.Ws;
   a.nb = p.nb; a.L = p.L; a.C = p.C; a.Lc = p.Lc; a.R = p.R; a.Lr = p.Lr;
+  a.hpw = p.hpw; a.ag = p.ag; a.ar = p.ar; a.air = p.air; a.am = p.am;
   a.tab_h_off = p.tab_h_off;
   a.div_hw = FastDiv::make((uint32_t)(p.Hs * p.Ws));
   a.div_w = FastDiv::make((uint32_t)p.Ws);
