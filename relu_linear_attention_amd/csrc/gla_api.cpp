@@ -256,16 +256,14 @@ gla_status make_plan(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, in
     if (P.Lc > max_tokens || P.Lr > max_tokens) P.mfma = false;
   }
   if (P.mfma) {
-    // Register-resident output stage: four waves per workgroup take hpw
-    // heads of one (batch, block) (four when H allows, so a token's rows of
-    // four heads move together) and 4/hpw tiles of 16 tokens each per item.
-    // One workgroup per compute unit: am workgroups per block share its
-    // items in turn.  A block is cut into super-ranges only when the RoPE
-    // table rows of the whole block would not fit in LDS beside the staging
-    // tiles.
-    P.hpw = H % 4 == 0 ? 4 : (H % 2 == 0 ? 2 : 1);
-    P.ag = B * P.nb * (H / P.hpw);
-    const int64_t item = 16 * (4 / P.hpw);
+    // Output stage: a workgroup takes one (batch, block, head) unit and items
+    // of kItem tokens (one 16-token tile per wave).  One workgroup per compute
+    // unit: am workgroups per unit share its items in turn.  A block is cut
+    // into super-ranges only when the RoPE table rows of the whole block
+    // would not fit in LDS beside S and the staging tiles.
+    P.hpw = 1;
+    P.ag = B * P.nb * H;
+    const int64_t item = gla::apply_reg_item_tokens();
     const int64_t items = ceil_div(P.L, item);
     P.ar = 1;
     for (;;) {
@@ -277,6 +275,8 @@ gla_status make_plan(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, in
     const int64_t sranges = P.ag * P.ar;
     P.am = std::max<int64_t>(1, std::min<int64_t>(P.air, cus / std::max<int64_t>(1, sranges)));
     if (sranges * P.am > 0x7fffffff) P.mfma = false;
+    // token indices stay below 2^31 up to the prefetches four items past a range
+    if (P.N + 4 * P.am * item + 16 >= ((int64_t)1 << 31)) P.mfma = false;
     // a 16-row tile of one head must be addressable with 32-bit offsets
     if ((int64_t)16 * H * d * 2 >= ((int64_t)1 << 31)) P.mfma = false;
   }

@@ -53,9 +53,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
 // vector; no two threads touch the same output, so the result is the same on
 // every run.
 //
-// frags (optional): S^T in two bf16 parts, S ~ hi + lo (hi = S rounded to
-// bf16, lo = the remainder rounded to bf16), laid out as the A fragments of
-// the output stage's 16x16x32 products: [unit][part][d/32][d/16][64][8].
+// frags (optional): S in two bf16 parts, S ~ hi + lo (hi = S rounded to
+// bf16, lo = the remainder rounded to bf16), each row-major [p][e]; the d*d
+// lo values follow the d*d hi values of a unit.
 // S_in/z_in (optional): the sums carried in from earlier blocks, where the
 // running sums start; S_out/z_out (optional): the final running sums.  Each
 // thread reads its four values of S_in/z_in before it writes the same four
@@ -84,21 +84,18 @@ __global__ __launch_bounds__(kBlock) void reduce_prefix_kernel(
     add_partials(run, partials + unit * C * stride + i4, stride, 0, C);
     *reinterpret_cast<float4 *>(states + unit * stride + i4) = run;
     if (frags != nullptr && i4 < (int64_t)d * d) {
-      // S[p][e] enters the A fragment (ks = p/32, et = e/16) of S^T for the
-      // 16x16x32 product: lane (e % 16) + 16 ((p % 32) / 8), element p % 8
       const float vals[4] = {run.x, run.y, run.z, run.w};
-      const int p = (int)(i4 / d), e0 = (int)(i4 % d);
-      const int KS = d / 32, ET = d / 16, ks = p / 32, j = p % 8;
-      uint16_t *base = frags + unit * (int64_t)d * d * 2;
+      uint16_t hi[4], lo[4];
       for (int r = 0; r < 4; ++r) {
-        const int e = e0 + r;
         const __bf16 h = (__bf16)vals[r];
-        const int ln = (e % 16) + 16 * ((p % 32) / 8);
-        const int64_t o_hi = ((int64_t)(ks * ET + e / 16) * 64 + ln) * 8 + j;
-        const int64_t o_lo = o_hi + (int64_t)KS * ET * 512;
-        base[o_hi] = __builtin_bit_cast(uint16_t, h);
-        base[o_lo] = f32_to_bf16_bits(vals[r] - (float)h);
+        hi[r] = __builtin_bit_cast(uint16_t, h);
+        lo[r] = f32_to_bf16_bits(vals[r] - (float)h);
       }
+      uint16_t *base = frags + unit * (int64_t)d * d * 2 + i4;
+      *reinterpret_cast<uint2 *>(base) =
+          make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
+      *reinterpret_cast<uint2 *>(base + (int64_t)d * d) =
+          make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
     }
   }
   if (S_out != nullptr) {

@@ -28,10 +28,10 @@ struct Plan {
   int64_t C, Lc;  // state chunks per unit, tokens per chunk
   int64_t R, Lr;  // apply ranges per unit, tokens per range
   int64_t Rb, Lb; // backward ranges per unit, tokens per range
-  // register-resident output stage (matrix cores): workgroups of four waves
-  // own hpw heads of one (batch, block); ag head groups, each block cut into
-  // ar super-ranges of air items (an item = 16 * 4/hpw tokens x hpw heads),
-  // am workgroups per super-range taking its items in turn
+  // output stage (matrix cores): a workgroup owns hpw heads of one (batch,
+  // block) (hpw = 1); ag such units, each block cut into ar super-ranges of
+  // air items of 128 tokens, am workgroups per super-range taking its items
+  // in turn
   int64_t hpw, ag, ar, air, am;
   bool bf16;      // element type of q, k, v, g, out
   bool mfma;      // matrix-core kernels (bf16, d = 64 or 128)
@@ -125,6 +125,8 @@ hipError_t launch_apply_reg(const Plan &p, const void *q, const void *g, const f
                             const uint16_t *frags, const float2 *tab, const void *rms_w,
                             void *out, hipStream_t stream);
 size_t apply_reg_lds_bytes(const Plan &p);
+// tokens of one work item of the output stage
+int64_t apply_reg_item_tokens();
 
 // Token-causal form.  The state stage writes one partial per chunk of Lc
 // tokens (units = B*H, one block each); the prefix kernel writes, for every
