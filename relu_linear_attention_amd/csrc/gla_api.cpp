@@ -206,9 +206,9 @@ gla_status make_plan(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, in
   const int64_t tile_s = P.mfma ? gla::kStateTile : 16;
   const int64_t tile_a = P.mfma ? gla::kApplyTile * 8 : 16;
 
-  // State stage: two workgroups resident per compute unit, chunks of at
-  // least 256 tokens.
-  const int64_t C0 = pick_pieces(P.units, P.L, tile_s, 256, 2 * (int64_t)cus);
+  // State stage: one twelve-wave workgroup resident per compute unit at
+  // d = 128 (two six-wave ones at d = 64), chunks of at least 256 tokens.
+  const int64_t C0 = pick_pieces(P.units, P.L, tile_s, 256, (d == 128 ? 1 : 2) * (int64_t)cus);
   int64_t Lc = round_up(ceil_div(P.L, C0), tile_s);
   if (P.mfma) {
     // temporal rows of a chunk: at most ceil(Lc / hw) + 1
@@ -283,7 +283,7 @@ gla_status make_plan(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, in
   if (P.mfma) {
     // LDS of the two matrix-core kernels must fit the 160 KiB of a CU
     auto slice = [&](int64_t len) { return spatial_entries + (ceil_div(len, hw) + 1) * pt; };
-    const int64_t lds_state = 3 * d * 128 + slice(P.Lc) * 8;
+    const int64_t lds_state = 6 * d * 128 + 2 * 64 * 16 + slice(P.Lc) * 8;
     if (lds_state > 160 * 1024) return fail(GLA_ERR_UNSUPPORTED,
         "internal: LDS plan of %lld bytes exceeds the CU", (long long)lds_state);
   }

@@ -116,6 +116,8 @@ hipError_t launch_apply_generic(const Plan &p, const void *q, const void *g, con
                                 hipStream_t stream);
 
 // Matrix-core kernels (bf16, d = 64 or 128).
+// dynamic LDS of the matrix-core state kernel
+size_t state_mfma_lds_bytes(const Plan &p);
 hipError_t launch_state_mfma(const Plan &p, const void *k, const void *v, const void *beta,
                              const float2 *tab, float *partials, hipStream_t stream);
 // Register-resident output stage (bf16, d = 64 or 128): frags holds S^T of

@@ -18,6 +18,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "gla_mfma_common.h"
 
 
@@ -30,24 +32,35 @@ constexpr int kStateLoadPolicy = kCacheStream;
 
 // ---------------------------------------------------------------- state
 
-// Threads per workgroup of the state kernel: d = 128 runs eight waves (two
-// workgroups, 16 waves, per compute unit, in at most 128 registers per
-// lane: the eight waves share one RoPE table slice, and twice the waves hide
-// more of the load latency than four waves with 4 tiles each), d = 64 four.
+// Workgroups of the state kernel: twelve waves at d = 128 (one workgroup per
+// compute unit), six at d = 64 (two per CU).  Two thirds of the waves are
+// producers, one third consumers (below).  Waves w, w + NWV/3 and
+// w + 2 NWV/3 of a workgroup share a SIMD, so every SIMD runs two producers
+// and one consumer: the consumers' matrix-core products overlap the
+// producers' vector work.  One workgroup per CU with several 64-token steps
+// of k and v in flight reads the two tensors faster than two workgroups per
+// CU with one step each (measured at 720p/81f: about 188 against 206 us for
+// the reads alone).
 template <int D>
-constexpr int kStateThreads = D == 128 ? 512 : 256;
+constexpr int kStateThreads = D == 128 ? 768 : 384;
+constexpr int kStatePrefetch = 2;  // 64-token steps of k and v in flight per producer thread
 
 template <int D>
 struct StateCfg {
   static constexpr int NT = kStateThreads<D>;
   static constexpr int NWV = NT / 64;                // waves
+  static constexpr int NCW = NWV / 3;                // consumer waves
+  static constexpr int NPW = NWV - NCW;              // producer waves
   static constexpr int FPT = D / 8;                  // threads per token row (16 B each)
-  static constexpr int TPP = NT / FPT;               // tokens per load pass
-  static constexpr int R = (int)kStateTile / TPP;    // passes per tile
-  static constexpr int TILES = (D / 32) * (D / 32);  // 32x32 output tiles of S
-  static constexpr int TPW = TILES / NWV;            // tiles per wave
+  static constexpr int TPP = NPW * 64 / FPT;         // tokens per load pass
+  static constexpr int R = (int)kStateTile / TPP;    // passes per step
+  static constexpr int TPW = D / 32;                 // tiles per consumer wave (one row of tiles)
   static constexpr int ROW = 2 * D;                  // bytes per token row
   static constexpr int OP_BYTES = (int)kStateTile * ROW;
+  static constexpr int SET_BYTES = 3 * OP_BYTES;     // one set of operand tiles
+  static constexpr int POS_BYTES = (int)kStateTile * 16;  // one step of token positions
+  static_assert(NCW * 32 == D, "consumer wave w owns row w of the 32x32 output tiles");
+  static_assert(R * TPP == (int)kStateTile, "whole passes per step");
   // Operand tiles are row-major [token][feature] with the 16-byte units of a
   // row XOR-permuted by the row index, so that the 16-B row writes and the
   // 8-B transposing reads (4 rows x 64 B per 32 lanes) both spread over all
@@ -61,31 +74,36 @@ struct StateCfg {
   }
 };
 
-// One workgroup per (unit, chunk).  Each 64-token step: the threads load the
-// k and v rows (16 B per thread per row, whole rows per instruction), apply
-// ReLU (accumulating z) and RoPE to k in fp32, and write RoPE(phi(k)) split
-// into bf16 hi + lo parts, and v (exact in bf16), as row-major tiles into
-// LDS.  Each wave then reads its operands transposed (four tokens of one
-// feature per lane and read) and accumulates its share of the 32x32 tiles of
-// S = hi^T v + lo^T v on the matrix cores.  The rows of the next step are in
-// flight in registers meanwhile.
+// One workgroup per (unit, chunk), 64-token steps, one barrier per step
+// ("round" i below).  In round i the producer waves take the k and v rows of
+// step i from registers (16 B per thread per row, whole rows per load
+// instruction), apply ReLU (accumulating z) and RoPE to k in fp32, write
+// RoPE(phi(k)) split into bf16 hi + lo parts, and v (exact in bf16), as
+// row-major tiles into LDS set i % 2, and refill the registers with the rows
+// kStatePrefetch steps ahead.  Meanwhile the consumer waves read the operands
+// of step i - 1 transposed from set (i - 1) % 2 (four tokens of one feature
+// per lane and read) and accumulate S = hi^T v + lo^T v on the matrix cores,
+// each wave one row of 32x32 tiles; consumer wave 0 also writes the grid
+// positions of step i + 1's tokens, as offsets into the RoPE table slice, to
+// LDS (integer divisions the producers would otherwise repeat per feature
+// unit).  Set i % 2 and positions (i + 1) % 2 are complete after barrier i;
+// set (i - 1) % 2, which round i + 1 writes, was consumed before it.
 //
 // kBeta: the write gate ("SANA-Video 2.0" Eq. (1)): beta [B, N, H] scales each
 // token's rotated key before it enters S (z keeps the plain phi(k)).
 template <int D, bool kBeta>
-__global__ __launch_bounds__(kStateThreads<D>, kStateThreads<D> / 128) void state_mfma_kernel(const uint16_t *__restrict__ k,
-                                                            const uint16_t *__restrict__ v,
-                                                            const uint16_t *__restrict__ beta,
-                                                            const float2 *__restrict__ tab,
-                                                            float *__restrict__ partials,
-                                                            MArgs a) {
+__global__ __launch_bounds__(kStateThreads<D>, 3) void state_mfma_kernel(
+    const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const uint16_t *__restrict__ beta, const float2 *__restrict__ tab,
+    float *__restrict__ partials, MArgs a) {
   using Cfg = StateCfg<D>;
-  constexpr int FPT = Cfg::FPT, TPP = Cfg::TPP, R = Cfg::R, ROW = Cfg::ROW;
+  constexpr int FPT = Cfg::FPT, TPP = Cfg::TPP, R = Cfg::R, ROW = Cfg::ROW, TPW = Cfg::TPW;
+  constexpr int P = kStatePrefetch;
   extern __shared__ __align__(16) unsigned char lds[];
-  unsigned char *s_kh = lds;                      // RoPE(phi(k)), bf16 hi part
-  unsigned char *s_kl = lds + Cfg::OP_BYTES;      // bf16 lo part
-  unsigned char *s_v = lds + 2 * Cfg::OP_BYTES;   // v
-  float2 *s_tab = reinterpret_cast<float2 *>(lds + 3 * Cfg::OP_BYTES);
+  // set s: RoPE(phi(k)) hi part, lo part, v at lds + s * SET_BYTES; then the
+  // two position buffers, then the table slice
+  unsigned char *s_pos = lds + 2 * Cfg::SET_BYTES;
+  float2 *s_tab = reinterpret_cast<float2 *>(s_pos + 2 * Cfg::POS_BYTES);
 
   const int64_t wg = blockIdx.x;
   const int64_t unit = wg / a.C, c = wg % a.C;
@@ -93,36 +111,29 @@ __global__ __launch_bounds__(kStateThreads<D>, kStateThreads<D> / 128) void stat
   const int64_t b = bh / a.H, hd = bh % a.H;
   const int64_t n_begin = blk * a.L + c * a.Lc;
   const int64_t n_end = min(n_begin + a.Lc, (blk + 1) * a.L);
+  const int64_t steps = (n_end - n_begin + kStateTile - 1) / kStateTile;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform across the wave
+  const bool producer = wave < Cfg::NPW;
 
-  const int fc = tid % FPT, tg = tid / FPT;
-  // this thread's rows of a tile: tg + TPP*r, 16-byte unit fc
+  // producers: rows tg + TPP*r of a step, 16-byte unit fc
+  const int fc = tid % FPT, tg = (tid / FPT) % TPP;
   const int wr_off = Cfg::off(tg, fc);
 
-  // output tiles of this wave and their transposing-read offsets: lane l
-  // (group g = l/16, s = l%16) points at row 8*(g/2) + s/4 (+ 16*ks +
-  // 4*half), column 32*tile + 16*(g%2) + 4*(s%4)
-  int tile_p[Cfg::TPW], tile_e[Cfg::TPW], rd_p[Cfg::TPW], rd_e[Cfg::TPW];
+  // consumers: output tiles (cw, t), t = 0..TPW-1, and their transposing-read
+  // offsets: lane l (group g = l/16, s = l%16) points at row 8*(g/2) + s/4
+  // (+ 16*ks + 4*half), column 32*tile + 16*(g%2) + 4*(s%4)
+  const int cw = producer ? 0 : wave - Cfg::NPW;
+  int rd_p, rd_e[TPW];
   {
     const int g = lane >> 4, sl = lane & 15;
     const int rrow = 8 * (g >> 1) + (sl >> 2);
+    const int cp = 32 * cw + 16 * (g & 1) + 4 * (sl & 3);
+    rd_p = Cfg::off(rrow, cp >> 3) + ((cp & 7) << 1);
 #pragma unroll
-    for (int t = 0; t < Cfg::TPW; ++t) {
-      if (D == 128 && Cfg::NWV == 8) {
-        tile_p[t] = wave >> 1;
-        tile_e[t] = 2 * (wave & 1) + t;
-      } else if (D == 128) {
-        tile_p[t] = 2 * (wave >> 1) + (t >> 1);
-        tile_e[t] = 2 * (wave & 1) + (t & 1);
-      } else {
-        tile_p[t] = wave >> 1;
-        tile_e[t] = wave & 1;
-      }
-      const int cp = 32 * tile_p[t] + 16 * (g & 1) + 4 * (sl & 3);
-      const int ce = 32 * tile_e[t] + 16 * (g & 1) + 4 * (sl & 3);
-      rd_p[t] = Cfg::off(rrow, cp >> 3) + ((cp & 7) << 1);
+    for (int t = 0; t < TPW; ++t) {
+      const int ce = 32 * t + 16 * (g & 1) + 4 * (sl & 3);
       rd_e[t] = Cfg::off(rrow, ce >> 3) + ((ce & 7) << 1);
     }
   }
@@ -139,136 +150,194 @@ __global__ __launch_bounds__(kStateThreads<D>, kStateThreads<D> / 128) void stat
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t *>(kBeta ? beta + (b * a.N + n_begin) * a.H + hd : k), 0,
       kBeta ? (int)((n_end - n_begin - 1) * a.H * 2 + 2) : 0, 0x00020000);
-  uint4 kr[R], vr[R];
-  uint32_t br[R];
-  auto load_rows = [&](int64_t n0) {
+  // producers: ring of P steps of rows in registers
+  uint4 kr[P][R], vr[P][R];
+  uint32_t br[P][R];
+  auto load_rows = [&](auto js, int64_t n0) {
+    constexpr int j = decltype(js)::value;
     const uint32_t base = (uint32_t)(n0 - n_begin) * row_bytes + my_off;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      kr[r] = buf_load16<kStateLoadPolicy>(rk, base + (uint32_t)(TPP * r) * row_bytes);
-      vr[r] = buf_load16<kStateLoadPolicy>(rv, base + (uint32_t)(TPP * r) * row_bytes);
+      kr[j][r] = buf_load16<kStateLoadPolicy>(rk, base + (uint32_t)(TPP * r) * row_bytes);
+      vr[j][r] = buf_load16<kStateLoadPolicy>(rv, base + (uint32_t)(TPP * r) * row_bytes);
       if (kBeta)
-        br[r] = __builtin_amdgcn_raw_buffer_load_b16(
+        br[j][r] = __builtin_amdgcn_raw_buffer_load_b16(
             rb, (int)(((uint32_t)(n0 - n_begin) + tg + TPP * r) * (uint32_t)a.H * 2), 0, 0);
     }
   };
+  // consumer wave 0: the table offsets of step i's 64 tokens along each axis
+  // (t, h, w rows; the slice's row bases are added by the reader)
+  constexpr int gt = D / 32, gh = 3 * D / 64;  // groups per t row, per h or w row
+  auto write_pos = [&](int64_t i) {
+    int64_t n = n_begin + i * kStateTile + lane;
+    if (n >= n_end) n = n_end - 1;  // rows past the chunk read as zero anyway
+    int t, h, w;
+    token_pos(a, n, t, h, w);
+    *reinterpret_cast<int4 *>(s_pos + (int)(i & 1) * Cfg::POS_BYTES + 16 * lane) =
+        make_int4(t * gt, h * gh, w * gh, 0);
+  };
 
-  // The table slice goes to LDS while the first step's rows are in flight:
+  // The table slice goes to LDS while the first steps' rows are in flight:
   // its loads, then the rows' loads, then its stores (which wait for the
   // older table loads alone).  The compiler-only barriers keep the two groups
   // of loads in that order.
   TabLoad<D> tload;
   tload.issue(tab, a, n_begin, n_end);
   asm volatile("" ::: "memory");
-  load_rows(n_begin);
+  static_assert(P == 2 || P == 3, "the ring holds two or three steps");
+  if (producer) {
+    load_rows(std::integral_constant<int, 0>{}, n_begin);
+    load_rows(std::integral_constant<int, 1>{}, n_begin + kStateTile);
+    if constexpr (P == 3) load_rows(std::integral_constant<int, P - 1>{}, n_begin + 2 * kStateTile);
+  }
   asm volatile("" ::: "memory");
   tload.store(s_tab, tab);
-  const TabSlice<D> ts = tload.ts;
+  if (!producer && cw == 0) write_pos(0);
+  // a producer thread's table group: slice base of its axis and pair group,
+  // plus the token's offset along that axis
   int axis, pia;
   pair_axis<D>(4 * fc, axis, pia);
-  const typename TabSlice<D>::Lookup tl = ts.lookup(axis, pia);
+  const int tab_base = tload.ts.lookup(axis, pia).base;
+  const TabSlice<D> ts = tload.ts;
+  __syncthreads();  // the table slice and the first positions are in LDS
 
-  f32x16 acc[Cfg::TPW];
+  f32x16 acc[TPW];
 #pragma unroll
-  for (int t = 0; t < Cfg::TPW; ++t)
+  for (int t = 0; t < TPW; ++t)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
   float zacc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) zacc[j] = 0.f;
 
-  // Each 64-token step: ReLU/RoPE/split of the rows in (kr, vr) into the LDS
-  // tiles; once they are there, the same registers are refilled with the
-  // next step's rows, which stay in flight during the matrix-core phase.
-  for (int64_t n0 = n_begin; n0 < n_end; n0 += kStateTile) {
-    __syncthreads();  // the previous step's operand reads are done
+  // The two roles run loops of their own with one barrier per round, steps +
+  // 1 rounds each (a barrier counts waves, wherever in the code they wait),
+  // so that neither role's registers stay live in the other's loop.
+  if (producer) {
+    // round i: step i (ring slot i % P) into set i % 2
+    auto round = [&](auto js, int64_t i) {
+      constexpr int j = decltype(js)::value;
+      if (i < steps) {
+        unsigned char *s_kh = lds + (int)(i & 1) * Cfg::SET_BYTES;
+        unsigned char *s_kl = s_kh + Cfg::OP_BYTES;
+        unsigned char *s_v = s_kh + 2 * Cfg::OP_BYTES;
+        const int *pos = reinterpret_cast<const int *>(s_pos + (int)(i & 1) * Cfg::POS_BYTES);
+        const int64_t n0 = n_begin + i * kStateTile;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      int64_t n = n0 + tg + TPP * r;
-      if (n >= n_end) n = n_end - 1;  // position only; the row itself reads as zero
-      int t, h, w;
-      token_pos(a, n, t, h, w);
-      const uint32_t kw[4] = {kr[r].x, kr[r].y, kr[r].z, kr[r].w};
-      float x[8];
+        for (int r = 0; r < R; ++r) {
+          const int grp = tab_base + pos[4 * (tg + TPP * r) + axis];
+          const uint32_t kw[4] = {kr[j][r].x, kr[j][r].y, kr[j][r].z, kr[j][r].w};
+          float x[8];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const uint32_t rl = relu_bf16x2(kw[m]);
-        x[2 * m] = lo_bf16(rl);
-        x[2 * m + 1] = hi_bf16(rl);
+          for (int m = 0; m < 4; ++m) {
+            const uint32_t rl = relu_bf16x2(kw[m]);
+            x[2 * m] = lo_bf16(rl);
+            x[2 * m + 1] = hi_bf16(rl);
+          }
+#pragma unroll
+          for (int q = 0; q < 8; ++q) zacc[q] += x[q];
+          float2 c4[4];
+          ts.read(s_tab, grp, c4);
+          rotate4(x, c4);
+          if (kBeta) {
+            const float bt = bf16_bits_to_float(br[j][r]);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) x[q] *= bt;
+          }
+          uint4 hi, lo;
+          split_bf16x2(x[0], x[1], hi.x, lo.x);
+          split_bf16x2(x[2], x[3], hi.y, lo.y);
+          split_bf16x2(x[4], x[5], hi.z, lo.z);
+          split_bf16x2(x[6], x[7], hi.w, lo.w);
+          const int o = wr_off + r * TPP * ROW;
+          *reinterpret_cast<uint4 *>(s_kh + o) = hi;
+          *reinterpret_cast<uint4 *>(s_kl + o) = lo;
+          *reinterpret_cast<uint4 *>(s_v + o) = vr[j][r];
+        }
+        // unconditional (rows past the chunk read as zeros): a conditional
+        // load here would make the compiler wait for it at the join
+        load_rows(js, n0 + P * kStateTile);
       }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) zacc[j] += x[j];
-      float2 c4[4];
-      ts.read(s_tab, tl.at(t, h, w), c4);
-      rotate4(x, c4);
-      if (kBeta) {
-        const float bt = bf16_bits_to_float(br[r]);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] *= bt;
+      __syncthreads();
+    };
+    for (int64_t i = 0; i <= steps; i += P) {
+      round(std::integral_constant<int, 0>{}, i);
+      if (i + 1 > steps) break;
+      round(std::integral_constant<int, 1>{}, i + 1);
+      if constexpr (P == 3) {
+        if (i + 2 > steps) break;
+        round(std::integral_constant<int, P - 1>{}, i + 2);
       }
-      uint4 hi, lo;
-      split_bf16x2(x[0], x[1], hi.x, lo.x);
-      split_bf16x2(x[2], x[3], hi.y, lo.y);
-      split_bf16x2(x[4], x[5], hi.z, lo.z);
-      split_bf16x2(x[6], x[7], hi.w, lo.w);
-      const int o = wr_off + r * TPP * ROW;
-      *reinterpret_cast<uint4 *>(s_kh + o) = hi;
-      *reinterpret_cast<uint4 *>(s_kl + o) = lo;
-      *reinterpret_cast<uint4 *>(s_v + o) = vr[r];
     }
-    // unconditional (rows past the chunk read as zeros): a conditional load
-    // here would make the compiler wait for it before the matrix-core phase
-    load_rows(n0 + kStateTile);
-    __syncthreads();
+  } else {
+    // round i: positions of step i + 1, products of step i - 1
+    for (int64_t i = 0; i <= steps; ++i) {
+      if (cw == 0 && i + 1 < steps) write_pos(i + 1);
+      if (i >= 1) {
+        const unsigned char *s_kh = lds + (int)((i - 1) & 1) * Cfg::SET_BYTES;
+        const unsigned char *s_kl = s_kh + Cfg::OP_BYTES;
+        const unsigned char *s_v = s_kh + 2 * Cfg::OP_BYTES;
 #pragma unroll
-    for (int ks = 0; ks < (int)kStateTile / 16; ++ks) {
+        for (int ks = 0; ks < (int)kStateTile / 16; ++ks) {
+          const int o0 = (16 * ks) * ROW, o1 = (16 * ks + 4) * ROW;
+          const uint2 h0 = lds_read_tr16(s_kh + rd_p + o0), h1 = lds_read_tr16(s_kh + rd_p + o1);
+          const uint2 l0 = lds_read_tr16(s_kl + rd_p + o0), l1 = lds_read_tr16(s_kl + rd_p + o1);
+          const bf16x8 fa = __builtin_bit_cast(bf16x8, make_uint4(h0.x, h0.y, h1.x, h1.y));
+          const bf16x8 fl = __builtin_bit_cast(bf16x8, make_uint4(l0.x, l0.y, l1.x, l1.y));
+          bf16x8 fb[TPW];
 #pragma unroll
-      for (int t = 0; t < Cfg::TPW; ++t) {
-        const int o0 = (16 * ks) * ROW, o1 = (16 * ks + 4) * ROW;
-        const uint2 h0 = lds_read_tr16(s_kh + rd_p[t] + o0), h1 = lds_read_tr16(s_kh + rd_p[t] + o1);
-        const uint2 l0 = lds_read_tr16(s_kl + rd_p[t] + o0), l1 = lds_read_tr16(s_kl + rd_p[t] + o1);
-        const uint2 v0 = lds_read_tr16(s_v + rd_e[t] + o0), v1 = lds_read_tr16(s_v + rd_e[t] + o1);
-        const bf16x8 fa = __builtin_bit_cast(bf16x8, make_uint4(h0.x, h0.y, h1.x, h1.y));
-        const bf16x8 fl = __builtin_bit_cast(bf16x8, make_uint4(l0.x, l0.y, l1.x, l1.y));
-        const bf16x8 fb = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fl, fb, acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc[t], 0, 0, 0);
+          for (int t = 0; t < TPW; ++t) {
+            const uint2 v0 = lds_read_tr16(s_v + rd_e[t] + o0), v1 = lds_read_tr16(s_v + rd_e[t] + o1);
+            fb[t] = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+          }
+          // the lo products of all tiles, then the hi products: no product
+          // waits for the one just issued
+#pragma unroll
+          for (int t = 0; t < TPW; ++t)
+            acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fl, fb[t], acc[t], 0, 0, 0);
+#pragma unroll
+          for (int t = 0; t < TPW; ++t)
+            acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb[t], acc[t], 0, 0, 0);
+        }
       }
+      __syncthreads();
     }
   }
 
-  // S_c, row-major: lanes 0..31 write 32 consecutive floats of one row
   float *dst = partials + wg * (int64_t)(D * D + D);
+  float *zs = reinterpret_cast<float *>(lds);
+  if (producer) {
+    // z_c: per-thread sums over its tokens, then a fixed-order sum over the
+    // TPP token groups (the operand sets are no longer read)
 #pragma unroll
-  for (int t = 0; t < Cfg::TPW; ++t) {
+    for (int j = 0; j < 8; ++j) zs[tg * D + 8 * fc + j] = zacc[j];
+  } else {
+    // S_c, row-major: lanes 0..31 write 32 consecutive floats of one row
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int p = 32 * tile_p[t] + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-      const int e = 32 * tile_e[t] + (lane & 31);
-      dst[p * D + e] = acc[t][i];
+    for (int t = 0; t < TPW; ++t) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int p = 32 * cw + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        const int e = 32 * t + (lane & 31);
+        dst[p * D + e] = acc[t][i];
+      }
     }
   }
-  // z_c: per-thread sums over its tokens, then a fixed-order sum over the
-  // TPP token groups
-  __syncthreads();
-  float *zs = reinterpret_cast<float *>(lds);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) zs[tg * D + 8 * fc + j] = zacc[j];
   __syncthreads();
   if (tid < D) {
     float s = 0.f;
     for (int gidx = 0; gidx < TPP; ++gidx) s += zs[gidx * D + tid];
     dst[D * D + tid] = s;
   }
+  __builtin_amdgcn_s_waitcnt(0);  // prefetches past the chunk are still in flight
 }
 
 template <int D, bool kBeta>
 hipError_t state_d(const Plan &p, const void *k, const void *v, const void *beta,
                    const float2 *tab, float *part, hipStream_t stream) {
-  const size_t lds = 3 * StateCfg<D>::OP_BYTES + tab_slice_entries(p, p.Lc) * sizeof(float2);
+  const size_t lds = state_mfma_lds_bytes(p);
   auto kern = state_mfma_kernel<D, kBeta>;
-  hipError_t e = hipFuncSetAttribute((const void *)kern,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const hipError_t e = lds_limit_once((const void *)kern);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)(p.units * p.C)), dim3(StateCfg<D>::NT), lds, stream,
                      (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)beta, tab, part,
@@ -277,6 +346,12 @@ hipError_t state_d(const Plan &p, const void *k, const void *v, const void *beta
 }
 
 }  // namespace
+
+size_t state_mfma_lds_bytes(const Plan &p) {
+  const size_t ops = p.d == 128 ? 2 * (StateCfg<128>::SET_BYTES + StateCfg<128>::POS_BYTES)
+                                 : 2 * (StateCfg<64>::SET_BYTES + StateCfg<64>::POS_BYTES);
+  return ops + tab_slice_entries(p, p.Lc) * sizeof(float2);
+}
 
 hipError_t launch_state_mfma(const Plan &p, const void *k, const void *v, const void *beta,
                              const float2 *tab, float *partials, hipStream_t stream) {
