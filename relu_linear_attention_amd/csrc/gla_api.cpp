@@ -11,7 +11,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
 #include <mutex>
+#include <tuple>
 #include <vector>
 
 #include "gla.h"
@@ -443,6 +445,107 @@ gla_status timed_launch(int stage, hipStream_t stream, const char *what, F &&lau
   return GLA_OK;
 }
 
+// ---------------------------------------------------------------- RoPE table cache
+// The (cos, sin) table depends only on (T, Hs, Ws, d, theta, t0).  The first
+// call of a shape on a device computes it, on that call's stream, into
+// library memory that lives until the process ends; later calls read it and
+// skip the table kernel.  A call on another stream before the table kernel
+// has finished waits for it (an event).  The per-call table in the workspace
+// remains for calls that must not allocate (gla_forward_noalloc, which reads
+// a finished cached table but never creates one), for calls made during
+// stream capture while an entry is missing or unfinished (capture must not
+// record the library's one-off work or wait on an event outside the graph),
+// and once kMaxCachedTables shapes are cached.
+struct TabKey {
+  int dev;
+  int64_t T, Hs, Ws, d, t0;
+  uint32_t theta;
+  bool operator<(const TabKey &o) const {
+    return std::tie(dev, T, Hs, Ws, d, t0, theta) <
+           std::tie(o.dev, o.T, o.Hs, o.Ws, o.d, o.t0, o.theta);
+  }
+};
+struct TabEntry {
+  float2 *ptr = nullptr;
+  hipEvent_t done = nullptr;  // recorded after the table kernel
+  bool ready = false;         // the event has completed
+};
+constexpr size_t kMaxCachedTables = 256;
+std::mutex g_tab_mu;
+std::map<TabKey, TabEntry> g_tabs;
+
+// The RoPE table for P on `stream`: the cached one when it exists (creating
+// it when may_create), else computed into the workspace's table ws_tab.
+gla_status rope_table_for(const Plan &P, float2 *ws_tab, hipStream_t stream, bool may_create,
+                          const float2 **tab) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  e = hipStreamIsCapturing(stream, &cap);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+  const bool capturing = cap != hipStreamCaptureStatusNone;
+  uint32_t theta_bits;
+  std::memcpy(&theta_bits, &P.theta, sizeof(theta_bits));
+  const TabKey key{dev, P.T, P.Hs, P.Ws, P.d, P.t0, theta_bits};
+  {
+    std::lock_guard<std::mutex> lk(g_tab_mu);
+    auto it = g_tabs.find(key);
+    if (it != g_tabs.end()) {
+      TabEntry &t = it->second;
+      // (no event query during capture: only a table known to be finished
+      // serves a captured call)
+      if (!t.ready && !capturing) {
+        e = hipEventQuery(t.done);
+        if (e == hipSuccess) {
+          t.ready = true;
+        } else if (e == hipErrorNotReady) {
+          (void)hipGetLastError();  // not an error; keep it from the next launch check
+        } else {
+          return hip_fail(e, "RoPE table event");
+        }
+      }
+      if (t.ready) {
+        *tab = t.ptr;
+        return GLA_OK;
+      }
+      if (!capturing) {
+        e = hipStreamWaitEvent(stream, t.done, 0);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent (RoPE table)");
+        *tab = t.ptr;
+        return GLA_OK;
+      }
+    } else if (may_create && !capturing && g_tabs.size() < kMaxCachedTables) {
+      TabEntry t;
+      e = hipMalloc((void **)&t.ptr, (size_t)P.tab_entries * sizeof(float2));
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&t.done, hipEventDisableTiming);
+      if (e != hipSuccess) {
+        // no cache entry: the per-call table below still works
+        (void)hipGetLastError();
+        if (t.ptr != nullptr) (void)hipFree(t.ptr);
+      } else {
+        gla_status st = timed_launch(0, stream, "rope table kernel",
+                                     [&] { return gla::launch_rope_table(P, t.ptr, stream); });
+        if (st == GLA_OK) {
+          e = hipEventRecord(t.done, stream);
+          if (e != hipSuccess) st = hip_fail(e, "hipEventRecord (RoPE table)");
+        }
+        if (st != GLA_OK) {
+          // the stream may still reach the kernel: keep the memory, drop the entry
+          (void)hipEventDestroy(t.done);
+          return st;
+        }
+        g_tabs.emplace(key, t);
+        *tab = t.ptr;
+        return GLA_OK;
+      }
+    }
+  }
+  *tab = ws_tab;
+  return timed_launch(0, stream, "rope table kernel",
+                      [&] { return gla::launch_rope_table(P, ws_tab, stream); });
+}
+
 // ---------------------------------------------------------------- execution
 // The carried cache of a streaming block step: the reduce stage starts its
 // running sums from (S_in, z_in) and writes the final sums to (S_out, z_out)
@@ -479,18 +582,21 @@ gla_status check_gates(const Gates &gt, const void *out, size_t bytes, int64_t B
 // Enqueues every stage of the operator on `stream`, with workspace `ws`.
 // With `apply == false` only the state is computed (gla_state, cache-only
 // block steps).
+// The table used is returned in *tab_used (for the gradient kernels) when
+// not null; may_create: the call may allocate a cached table.
 gla_status run_plan(const Plan &P, const void *q, const void *k, const void *v, const void *g,
                     void *out, void *ws, hipStream_t stream, bool apply,
-                    const Cache &cache = Cache(), const Gates &gates = Gates()) {
+                    const Cache &cache = Cache(), const Gates &gates = Gates(),
+                    bool may_create = true, const float2 **tab_used = nullptr) {
   char *base = (char *)ws;
-  float2 *tab = (float2 *)(base + P.off_tab);
   float *part = (float *)(base + P.off_part);
   float *states = (float *)(base + P.off_state);
   uint16_t *frags = P.mfma ? (uint16_t *)(base + P.off_frag) : nullptr;
 
-  gla_status st = timed_launch(0, stream, "rope table kernel",
-                               [&] { return gla::launch_rope_table(P, tab, stream); });
+  const float2 *tab = nullptr;
+  gla_status st = rope_table_for(P, (float2 *)(base + P.off_tab), stream, may_create, &tab);
   if (st != GLA_OK) return st;
+  if (tab_used != nullptr) *tab_used = tab;
   st = timed_launch(1, stream, "state kernel", [&] {
     return P.mfma ? gla::launch_state_mfma(P, k, v, gates.beta, tab, part, stream)
                   : gla::launch_state_generic(P, k, v, gates.beta, tab, part, stream);
@@ -512,11 +618,10 @@ gla_status run_plan(const Plan &P, const void *q, const void *k, const void *v, 
 gla_status run_causal(const Plan &P, const void *q, const void *k, const void *v, const void *g,
                       void *out, void *ws, hipStream_t stream) {
   char *base = (char *)ws;
-  float2 *tab = (float2 *)(base + P.off_tab);
   float *part = (float *)(base + P.off_part);
   float *states = (float *)(base + P.off_state);
-  gla_status st = timed_launch(0, stream, "rope table kernel",
-                               [&] { return gla::launch_rope_table(P, tab, stream); });
+  const float2 *tab = nullptr;
+  gla_status st = rope_table_for(P, (float2 *)(base + P.off_tab), stream, true, &tab);
   if (st != GLA_OK) return st;
   st = timed_launch(1, stream, "state kernel", [&] {
     return P.mfma ? gla::launch_state_mfma(P, k, v, nullptr, tab, part, stream)
@@ -590,7 +695,7 @@ gla_status forward_impl(const void *q, const void *k, const void *v, const void 
     void *mem = nullptr;
     hipError_t e = gla::noalloc_scratch(&mem);
     if (e != hipSuccess) return hip_fail(e, "scratch address (hipGetSymbolAddress)");
-    return run_plan(P, q, k, v, g, out, mem, stream, apply, cache, gt);
+    return run_plan(P, q, k, v, g, out, mem, stream, apply, cache, gt, false);
   }
   if (!own_ws) {
     if (ws_bytes < P.total_bytes)
@@ -799,12 +904,13 @@ gla_status gla_backward(const void *q, const void *k, const void *v, const void 
     }
   }
   // the forward state of the call, then the gradient kernels
-  st = run_plan(P, nullptr, k, v, nullptr, nullptr, mem, stream, false);
+  const float2 *tab = nullptr;
+  st = run_plan(P, nullptr, k, v, nullptr, nullptr, mem, stream, false, Cache(), Gates(), true,
+                &tab);
   if (st == GLA_OK) {
     char *base = (char *)mem;
     st = timed_launch(4, stream, "gradient kernels", [&] {
-      return gla::launch_backward(P, q, k, v, g, dout, (const float *)(base + P.off_state),
-                                  (const float2 *)(base + P.off_tab),
+      return gla::launch_backward(P, q, k, v, g, dout, (const float *)(base + P.off_state), tab,
                                   (float *)(base + P.off_bpart), (float *)(base + P.off_grad),
                                   dq, dk, dv, dg, stream);
     });

@@ -414,8 +414,7 @@ hipError_t bwd_d(const Plan &p, const void *q, const void *k, const void *v, con
   const dim3 grid((unsigned)(p.units * p.Rb));
   const size_t lds_q = sizeof(float) * (D * kRow<D> + D + 4 * kTokB * D + 2 * kTokB);
   auto kq = bwd_q_kernel<TIn, D>;
-  hipError_t e = hipFuncSetAttribute((const void *)kq,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_q);
+  hipError_t e = lds_limit_once((const void *)kq);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kq, grid, dim3(kBlock), lds_q, stream, (const TIn *)q, (const TIn *)g,
                      (const TIn *)dout, states, tab, (TIn *)dq, (TIn *)dg, partials, a);
@@ -427,8 +426,7 @@ hipError_t bwd_d(const Plan &p, const void *q, const void *k, const void *v, con
   if (e != hipSuccess) return e;
   const size_t lds_kv = sizeof(float) * (D * kRow<D> + D + 3 * kTokB * D);
   auto kkv = bwd_kv_kernel<TIn, D>;
-  e = hipFuncSetAttribute((const void *)kkv, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)lds_kv);
+  e = lds_limit_once((const void *)kkv);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kkv, grid, dim3(kBlock), lds_kv, stream, (const TIn *)k, (const TIn *)v,
                      grads, tab, (TIn *)dk, (TIn *)dv, a);

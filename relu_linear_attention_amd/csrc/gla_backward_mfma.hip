@@ -637,8 +637,7 @@ hipError_t bwd_q_d(const Plan &p, const void *q, const void *g, const void *dout
                    hipStream_t stream) {
   const size_t lds = BwdQCfg<D>::kFixedLds + (size_t)tab_slice_entries(p, p.Lr) * sizeof(float2);
   auto kern = bwd_q_mfma_kernel<D>;
-  hipError_t e = hipFuncSetAttribute((const void *)kern,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = lds_limit_once((const void *)kern);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)(p.units * p.R)), dim3(kBwdThreads), lds, stream,
                      (const uint16_t *)q, (const uint16_t *)g, (const uint16_t *)dout, states, tab,
@@ -657,8 +656,7 @@ hipError_t bwd_kv_d(const Plan &p, const void *k, const void *v, const float *gr
                     const float2 *tab, void *dk, void *dv, hipStream_t stream) {
   const size_t lds = bwd_kv_lds<D>(p);
   auto kern = bwd_kv_mfma_kernel<D>;
-  hipError_t e = hipFuncSetAttribute((const void *)kern,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = lds_limit_once((const void *)kern);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)(p.units * p.R)), dim3(kBwdThreads), lds, stream,
                      (const uint16_t *)k, (const uint16_t *)v, grads, tab, (uint16_t *)dk,

@@ -299,8 +299,7 @@ hipError_t causal_vec_d(const Plan &p, const void *q, const void *k, const void 
   const size_t lds =
       sizeof(float) * (D * SP + D + 5 * kCTok * SP + 2 * kCTok * (kCTok + 1) + kCTok);
   auto kern = causal_vector_kernel<TIn, D>;
-  hipError_t e = hipFuncSetAttribute((const void *)kern,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = lds_limit_once((const void *)kern);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)(p.units * p.R)), dim3(kBlock), lds, stream,
                      (const TIn *)q, (const TIn *)k, (const TIn *)v, (const TIn *)g, states, tab,

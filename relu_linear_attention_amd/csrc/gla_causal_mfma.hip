@@ -463,8 +463,7 @@ hipError_t causal_d(const Plan &p, const void *q, const void *k, const void *v, 
                     const float *states, const float2 *tab, void *out, hipStream_t stream) {
   const size_t lds = causal_lds<D>(p);
   auto kern = causal_mfma_kernel<D>;
-  hipError_t e = hipFuncSetAttribute((const void *)kern,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = lds_limit_once((const void *)kern);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)(p.units * p.R)), dim3(kCausalThreads), lds, stream,
                      (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v,

@@ -7,6 +7,10 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+#include <utility>
+#include <vector>
+
 #include "gla_internal.h"
 
 namespace gla {
@@ -108,6 +112,20 @@ __global__ __launch_bounds__(kBlock) void reduce_prefix_kernel(
 }
 
 }  // namespace
+
+hipError_t lds_limit_once(const void *kern) {
+  static std::mutex mu;
+  static std::vector<std::pair<const void *, int>> done;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(mu);
+  for (const auto &x : done)
+    if (x.first == kern && x.second == dev) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (e == hipSuccess) done.emplace_back(kern, dev);
+  return e;
+}
 
 hipError_t launch_rope_table(const Plan &p, float2 *tab, hipStream_t stream) {
   int64_t blocks = (p.tab_entries + kBlock - 1) / kBlock;

@@ -116,6 +116,9 @@ hipError_t launch_apply_generic(const Plan &p, const void *q, const void *g, con
                                 hipStream_t stream);
 
 // Matrix-core kernels (bf16, d = 64 or 128).
+// Raises a kernel's dynamic-LDS limit to a compute unit's 160 KiB, once per
+// (kernel, device) rather than before every launch; thread-safe.
+hipError_t lds_limit_once(const void *kern);
 // dynamic LDS of the matrix-core state kernel
 size_t state_mfma_lds_bytes(const Plan &p);
 hipError_t launch_state_mfma(const Plan &p, const void *k, const void *v, const void *beta,

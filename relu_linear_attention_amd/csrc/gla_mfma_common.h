@@ -16,22 +16,6 @@
 namespace gla {
 namespace {
 
-// Raises a kernel's dynamic-LDS limit to a compute unit's 160 KiB, once per
-// (kernel, device) rather than before every launch.
-inline hipError_t lds_limit_once(const void *kern) {
-  static std::mutex mu;
-  static std::vector<std::pair<const void *, int>> done;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  std::lock_guard<std::mutex> lk(mu);
-  for (const auto &x : done)
-    if (x.first == kern && x.second == dev) return hipSuccess;
-  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-  if (e == hipSuccess) done.emplace_back(kern, dev);
-  return e;
-}
-
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));

@@ -268,8 +268,7 @@ hipError_t apply_d(const Plan &p, const void *q, const void *g, const float *sta
                    const float2 *tab, const void *rms_w, void *out, hipStream_t stream) {
   const size_t lds = sizeof(float) * (D * D + D + 2 * kTok * D + kTok);
   auto kern = apply_vector_kernel<TIn, D>;
-  hipError_t e = hipFuncSetAttribute((const void *)kern,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = lds_limit_once((const void *)kern);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)(p.units * p.R)), dim3(kBlock), lds, stream,
                      (const TIn *)q, (const TIn *)g, states, tab, (const TIn *)rms_w, (TIn *)out,

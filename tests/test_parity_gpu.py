@@ -193,7 +193,11 @@ def test_stage_timing_records_every_launch():
         gla.gla_forward(dev["q"], dev["k"], dev["v"], dev["g"], out, (3, 5, 7))
     rec = gla.gla_profile_read()
     gla.gla_profile_enable(False)
-    # one launch per forward stage and call; a forward call runs no gradient kernels
+    # one launch per forward stage and call, except the RoPE table, which is
+    # computed once per shape and then read from the library's cache (this
+    # grid may already be cached by an earlier test); a forward call runs no
+    # gradient kernels
     assert all(rec[s][0] == 3 and rec[s][1] > 0
-               for s in ("rope_table", "state_partials", "reduce_prefix", "apply")), rec
+               for s in ("state_partials", "reduce_prefix", "apply")), rec
+    assert rec["rope_table"][0] <= 1, rec
     assert rec["backward"][0] == 0 and rec["causal_apply"][0] == 0, rec
