@@ -2,11 +2,13 @@
 configuration the benchmark times.
 
 480p/81f, 720p/81f and the block-causal 720p layer are compared element by
-element over every output; the 720p/60 s layer (2.67e9 elements per tensor)
-is compared on sampled heads and tokens, the oracle's state being built from
-all 867,600 tokens of those heads.  Inputs are drawn on the device
-(relu_linear_attention_amd.inputs.device_inputs) and read back for the
-oracle.
+element over every output; the 720p/60 s layer (3.55e9 elements per tensor)
+over every output of four of its 24 heads (all 867,600 tokens; the heads
+are independent, so the oracle runs on those heads alone).  Inputs are drawn
+on the device (relu_linear_attention_amd.inputs.device_inputs) and read back
+for the oracle.  Besides the elementwise bound, the relative L2 error of the
+whole output must stay within REL_L2: rounding the output to bf16 alone
+gives about 2^-9 / sqrt(3) = 1.1e-3.
 """
 import numpy as np
 import pytest
@@ -18,6 +20,8 @@ from tests.gpu_util import TOL, have_gpu
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow,
               pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
+
+REL_L2 = 3e-3
 
 
 def _forward(w, x):
@@ -68,6 +72,7 @@ def test_full_size_parity(name):
     worst, worst_abs, l2 = _chunked_errors(got, ref)
     print(f"  max rel err {worst:.3e}  max abs err {worst_abs:.3e}  rel l2 {l2:.3e}", flush=True)
     assert worst <= TOL[w.dtype]
+    assert l2 <= REL_L2
 
 
 def test_block_causal_last_block_equals_noncausal_full_size():
@@ -88,23 +93,23 @@ def test_block_causal_last_block_equals_noncausal_full_size():
     assert float((bc[:, :n0].float() - nc[:, :n0].float()).abs().max()) > 1e-4
 
 
-def test_long_video_sampled_parity():
+def test_long_video_parity_four_heads():
     import torch
 
     w = WORKLOADS["720p_60s"]
-    print(f"workload {w.name}: N={w.N} H={w.H}", flush=True)
+    heads = [0, 7, 16, 23]
+    print(f"workload {w.name}: N={w.N} H={w.H}, heads {heads}, every token", flush=True)
     x = device_inputs_for(w)
     out = _forward(w, x)
-    heads = [0, 17]
-    rng = np.random.default_rng(0)
-    tokens = np.unique(np.concatenate([
-        rng.integers(0, w.N, 3000), [0, 1, w.N - 1, w.N // 2],
-        np.arange(0, w.N, w.Hs * w.Ws * 16)]))  # every 16th frame start
-    hs = {n: t[:, :, heads].float().cpu().numpy() for n, t in x.items()}
-    S, z = oracle.state(hs["k"], hs["v"], w.grid, 0, w.theta)
-    ref = oracle.apply(hs["q"], hs["g"], S, z, w.grid, 0, w.theta, w.eps, tokens=tokens)
-    tok = torch.from_numpy(tokens).cuda()
-    got = out[:, tok][:, :, heads].float().cpu().numpy()
-    err = float(np.max(np.abs(got - ref) / (np.abs(ref) + 1e-3)))
-    print(f"  sampled {tokens.size} tokens x {len(heads)} heads: max rel err {err:.3e}", flush=True)
-    assert err <= TOL["bf16"]
+    idx = torch.tensor(heads, device="cuda")
+    hs = {n: t.index_select(2, idx).float().cpu().numpy() for n, t in x.items()}
+    got = out.index_select(2, idx).float().cpu().numpy()
+    del x, out
+    grid = (w.T, w.Hs, w.Ws)
+    S, z = oracle.state(hs["k"], hs["v"], grid, 0, w.theta)
+    ref = oracle.apply(hs["q"], hs["g"], S, z, grid, 0, w.theta, w.eps)
+    worst, worst_abs, l2 = _chunked_errors(got, ref)
+    print(f"  {w.N} tokens x {len(heads)} heads: max rel err {worst:.3e}  "
+          f"max abs err {worst_abs:.3e}  rel l2 {l2:.3e}", flush=True)
+    assert worst <= TOL["bf16"]
+    assert l2 <= REL_L2
