@@ -284,8 +284,8 @@ gla_status make_plan(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, in
   }
   if (P.mfma) {
     // LDS of the two matrix-core kernels must fit the 160 KiB of a CU
-    auto slice = [&](int64_t len) { return spatial_entries + (ceil_div(len, hw) + 1) * pt; };
-    const int64_t lds_state = 6 * d * 128 + 2 * 64 * 16 + slice(P.Lc) * 8;
+    // (+ 64 bytes for the state kernel's static LDS)
+    const int64_t lds_state = (int64_t)gla::state_mfma_lds_bytes(P) + 64;
     if (lds_state > 160 * 1024) return fail(GLA_ERR_UNSUPPORTED,
         "internal: LDS plan of %lld bytes exceeds the CU", (long long)lds_state);
   }
@@ -546,6 +546,56 @@ gla_status rope_table_for(const Plan &P, float2 *ws_tab, hipStream_t stream, boo
                       [&] { return gla::launch_rope_table(P, ws_tab, stream); });
 }
 
+// ---------------------------------------------------------------- reduce counters
+// The counters of the reduce folded into the state kernel, one set per
+// (device, stream): calls on one stream run in order, so a set is never used
+// by two kernels at once.  A set is allocated on a stream's first call and
+// zeroed stream-ordered on that stream; the last workgroup of each unit puts
+// its counter back to zero, so the set stays zeroed between kernels.  Calls
+// during stream capture, calls that must not allocate, calls with more than
+// kMaxCounterUnits units and calls beyond kMaxCounterSets streams run the
+// separate reduce kernel instead (bitwise the same sums).  (A stream that is
+// destroyed while its last call still runs and whose handle a new stream
+// reuses at once would share the set with it; the library cannot see that.)
+constexpr int64_t kMaxCounterUnits = (int64_t)1 << 16;
+constexpr size_t kMaxCounterSets = 64;
+std::mutex g_cnt_mu;
+std::map<std::pair<int, hipStream_t>, unsigned *> g_cnts;
+
+// The counter set of `stream` (nullptr when the fold is not available).
+gla_status reduce_counters(hipStream_t stream, bool may_alloc, unsigned **cnt) {
+  *cnt = nullptr;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(stream, &cap);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+  if (cap != hipStreamCaptureStatusNone) return GLA_OK;
+  int dev = 0;
+  e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lk(g_cnt_mu);
+  auto it = g_cnts.find({dev, stream});
+  if (it != g_cnts.end()) {
+    *cnt = it->second;
+    return GLA_OK;
+  }
+  if (!may_alloc || g_cnts.size() >= kMaxCounterSets) return GLA_OK;
+  unsigned *p = nullptr;
+  const size_t bytes = (size_t)kMaxCounterUnits * sizeof(unsigned);
+  e = hipMalloc((void **)&p, bytes);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // no set: the separate reduce kernel still works
+    return GLA_OK;
+  }
+  e = hipMemsetAsync(p, 0, bytes, stream);
+  if (e != hipSuccess) {
+    (void)hipFree(p);
+    return hip_fail(e, "hipMemsetAsync (reduce counters)");
+  }
+  g_cnts.emplace(std::make_pair(dev, stream), p);
+  *cnt = p;
+  return GLA_OK;
+}
+
 // ---------------------------------------------------------------- execution
 // The carried cache of a streaming block step: the reduce stage starts its
 // running sums from (S_in, z_in) and writes the final sums to (S_out, z_out)
@@ -583,26 +633,41 @@ gla_status check_gates(const Gates &gt, const void *out, size_t bytes, int64_t B
 // With `apply == false` only the state is computed (gla_state, cache-only
 // block steps).
 // The table used is returned in *tab_used (for the gradient kernels) when
-// not null; may_create: the call may allocate a cached table.
+// not null; may_alloc: the call may allocate the library's cached table and
+// reduce counters.  With one temporal block on the matrix-core path the
+// reduce runs in the state kernel's last workgroups (two launches per call).
 gla_status run_plan(const Plan &P, const void *q, const void *k, const void *v, const void *g,
                     void *out, void *ws, hipStream_t stream, bool apply,
                     const Cache &cache = Cache(), const Gates &gates = Gates(),
-                    bool may_create = true, const float2 **tab_used = nullptr) {
+                    bool may_alloc = true, const float2 **tab_used = nullptr) {
   char *base = (char *)ws;
   float *part = (float *)(base + P.off_part);
   float *states = (float *)(base + P.off_state);
   uint16_t *frags = P.mfma ? (uint16_t *)(base + P.off_frag) : nullptr;
 
   const float2 *tab = nullptr;
-  gla_status st = rope_table_for(P, (float2 *)(base + P.off_tab), stream, may_create, &tab);
+  gla_status st = rope_table_for(P, (float2 *)(base + P.off_tab), stream, may_alloc, &tab);
   if (st != GLA_OK) return st;
   if (tab_used != nullptr) *tab_used = tab;
+  gla::FusedReduce fz;
+  // (the last workgroup addresses a unit's C partials with 32-bit offsets)
+  if (P.mfma && P.nb == 1 && P.units <= kMaxCounterUnits &&
+      P.C * gla::kPartialStride(P.d) * 4 < ((int64_t)1 << 31)) {
+    st = reduce_counters(stream, may_alloc, &fz.cnt);
+    if (st != GLA_OK) return st;
+    fz.states = states;
+    fz.frags = apply ? frags : nullptr;
+    fz.S_in = cache.S_in;
+    fz.z_in = cache.z_in;
+    fz.S_out = cache.S_out;
+    fz.z_out = cache.z_out;
+  }
   st = timed_launch(1, stream, "state kernel", [&] {
-    return P.mfma ? gla::launch_state_mfma(P, k, v, gates.beta, tab, part, stream)
+    return P.mfma ? gla::launch_state_mfma(P, k, v, gates.beta, tab, part, fz, stream)
                   : gla::launch_state_generic(P, k, v, gates.beta, tab, part, stream);
   });
   if (st != GLA_OK) return st;
-  st = timed_launch(2, stream, "reduce kernel", [&] {
+  if (fz.cnt == nullptr) st = timed_launch(2, stream, "reduce kernel", [&] {
     return gla::launch_reduce(P, part, states, apply ? frags : nullptr, cache.S_in, cache.z_in,
                               cache.S_out, cache.z_out, stream);
   });
@@ -624,7 +689,8 @@ gla_status run_causal(const Plan &P, const void *q, const void *k, const void *v
   gla_status st = rope_table_for(P, (float2 *)(base + P.off_tab), stream, true, &tab);
   if (st != GLA_OK) return st;
   st = timed_launch(1, stream, "state kernel", [&] {
-    return P.mfma ? gla::launch_state_mfma(P, k, v, nullptr, tab, part, stream)
+    return P.mfma ? gla::launch_state_mfma(P, k, v, nullptr, tab, part, gla::FusedReduce(),
+                                           stream)
                   : gla::launch_state_generic(P, k, v, nullptr, tab, part, stream);
   });
   if (st != GLA_OK) return st;

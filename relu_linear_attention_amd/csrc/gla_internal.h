@@ -56,14 +56,21 @@ constexpr int64_t kPartialStride(int64_t d) { return d * d + d; }
 // loads in flight: the reduce kernels are latency-bound with one partial per
 // round trip.  Indices past c1 - 1 are clamped (their values are loaded and
 // dropped), so every load is unconditional.
+// `load` reads the four floats at a pointer (PlainLoad4: an ordinary load).
+struct PlainLoad4 {
+  __device__ __forceinline__ float4 operator()(const float *p) const {
+    return *reinterpret_cast<const float4 *>(p);
+  }
+};
+template <class Load = PlainLoad4>
 __device__ __forceinline__ void add_partials(float4 &run, const float *src, int64_t stride,
-                                             int64_t c0, int64_t c1) {
+                                             int64_t c0, int64_t c1, Load load = Load()) {
   for (int64_t c = c0; c < c1; c += 8) {
     float4 x[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int64_t cj = c + j < c1 ? c + j : c1 - 1;
-      x[j] = *reinterpret_cast<const float4 *>(src + cj * stride);
+      x[j] = load(src + cj * stride);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -74,6 +81,74 @@ __device__ __forceinline__ void add_partials(float4 &run, const float *src, int6
         run.w += x[j].w;
       }
     }
+  }
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  __bf16 h = (__bf16)x;  // round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// The element i4 of the carried cache (S rows then z) of (batch, head) bh.
+__device__ __forceinline__ float *cache_ptr(float *S, float *z, int64_t bh, int64_t i4, int d) {
+  const int64_t dd = (int64_t)d * d;
+  return i4 < dd ? S + bh * dd + i4 : z + bh * d + (i4 - dd);
+}
+
+// Sum of the C chunk partials of every block unit of (batch, head) bh, in
+// chunk order, followed by the inclusive prefix over its nb temporal blocks,
+// in block order, for the four consecutive floats i4..i4+3 of the d*d + d
+// state vector (d % 4 == 0, so they never straddle S and z).  Every output
+// value is owned by one caller, so the result is the same on every run; the
+// separate reduce kernel and the state kernel's last workgroup both run
+// this, so their results agree bit for bit.
+//
+// states: [unit][d*d + d] running sums (unit = bh * nb + block).
+// frags (optional): S in two bf16 parts, S ~ hi + lo (hi = S rounded to
+// bf16, lo = the remainder rounded to bf16), each row-major [p][e]; the d*d
+// lo values follow the d*d hi values of a unit.
+// S_in/z_in (optional): the sums carried in from earlier blocks, where the
+// running sums start; S_out/z_out (optional): the final running sums.  The
+// four values of S_in/z_in are read before the same four of S_out/z_out are
+// written, so the two may be the same arrays (an in-place update).
+template <class Load = PlainLoad4>
+__device__ __forceinline__ void reduce_prefix_values(const float *partials, float *states,
+                                                     uint16_t *frags, const float *S_in,
+                                                     const float *z_in, float *S_out,
+                                                     float *z_out, int64_t bh, int64_t nb,
+                                                     int64_t C, int d, int64_t i4,
+                                                     Load load = Load()) {
+  const int64_t stride = (int64_t)d * d + d;
+  float4 run = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (S_in != nullptr) {
+    const float *c = cache_ptr(const_cast<float *>(S_in), const_cast<float *>(z_in), bh, i4, d);
+    run = make_float4(c[0], c[1], c[2], c[3]);
+  }
+  for (int64_t blk = 0; blk < nb; ++blk) {
+    const int64_t unit = bh * nb + blk;
+    add_partials(run, partials + unit * C * stride + i4, stride, 0, C, load);
+    *reinterpret_cast<float4 *>(states + unit * stride + i4) = run;
+    if (frags != nullptr && i4 < (int64_t)d * d) {
+      const float vals[4] = {run.x, run.y, run.z, run.w};
+      uint16_t hi[4], lo[4];
+      for (int r = 0; r < 4; ++r) {
+        const __bf16 h = (__bf16)vals[r];
+        hi[r] = __builtin_bit_cast(uint16_t, h);
+        lo[r] = f32_to_bf16_bits(vals[r] - (float)h);
+      }
+      uint16_t *base = frags + unit * (int64_t)d * d * 2 + i4;
+      *reinterpret_cast<uint2 *>(base) =
+          make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
+      *reinterpret_cast<uint2 *>(base + (int64_t)d * d) =
+          make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
+    }
+  }
+  if (S_out != nullptr) {
+    float *c = cache_ptr(S_out, z_out, bh, i4, d);
+    c[0] = run.x;
+    c[1] = run.y;
+    c[2] = run.z;
+    c[3] = run.w;
   }
 }
 
@@ -116,13 +191,28 @@ hipError_t launch_apply_generic(const Plan &p, const void *q, const void *g, con
                                 hipStream_t stream);
 
 // Matrix-core kernels (bf16, d = 64 or 128).
-// Raises a kernel's dynamic-LDS limit to a compute unit's 160 KiB, once per
-// (kernel, device) rather than before every launch; thread-safe.
+// Raises a kernel's dynamic-LDS limit to a compute unit's 160 KiB less the
+// kernel's static LDS, once per (kernel, device) rather than before every
+// launch; thread-safe.
 hipError_t lds_limit_once(const void *kern);
 // dynamic LDS of the matrix-core state kernel
 size_t state_mfma_lds_bytes(const Plan &p);
+// The reduce folded into the state kernel (one temporal block, nb == 1):
+// each workgroup counts itself done on cnt[unit] (an agent-scope atomic),
+// and the last of a unit's C workgroups runs reduce_prefix_values for the
+// unit and puts cnt[unit] back to 0.  cnt must hold zeros when the kernel
+// starts, and no other kernel may use it meanwhile.  cnt == nullptr: the
+// partials are left for the separate reduce kernel.
+struct FusedReduce {
+  unsigned *cnt = nullptr;
+  float *states = nullptr;
+  uint16_t *frags = nullptr;
+  const float *S_in = nullptr, *z_in = nullptr;
+  float *S_out = nullptr, *z_out = nullptr;
+};
 hipError_t launch_state_mfma(const Plan &p, const void *k, const void *v, const void *beta,
-                             const float2 *tab, float *partials, hipStream_t stream);
+                             const float2 *tab, float *partials, const FusedReduce &fuse,
+                             hipStream_t stream);
 // Register-resident output stage (bf16, d = 64 or 128): frags holds S^T of
 // every unit as bf16 hi and lo matrix-core A fragments,
 // [units][part][d/32][d/16][64 lanes][8]; its LDS bytes for the plan.

@@ -30,6 +30,21 @@ namespace {
 // faster per call at 720p/81f than normal ones.
 constexpr int kStateLoadPolicy = kCacheStream;
 
+// 16-byte loads of chunk partials at device scope (the SC1 cache-policy
+// bit): coherent with the device-scope stores other workgroups made, from
+// any XCD.  `base` is where the resource starts.
+constexpr int kCacheDevice = 16;
+struct DeviceLoad4 {
+  __amdgpu_buffer_rsrc_t r;
+  const float *base;
+  __device__ __forceinline__ float4 operator()(const float *p) const {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)((p - base) * 4), 0,
+                                                          kCacheDevice);
+    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                       __uint_as_float(v.w));
+  }
+};
+
 // ---------------------------------------------------------------- state
 
 // Workgroups of the state kernel: twelve waves at d = 128 (one workgroup per
@@ -95,7 +110,7 @@ template <int D, bool kBeta>
 __global__ __launch_bounds__(kStateThreads<D>, 3) void state_mfma_kernel(
     const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const uint16_t *__restrict__ beta, const float2 *__restrict__ tab,
-    float *__restrict__ partials, MArgs a) {
+    float *__restrict__ partials, MArgs a, FusedReduce fz) {
   using Cfg = StateCfg<D>;
   constexpr int FPT = Cfg::FPT, TPP = Cfg::TPP, R = Cfg::R, ROW = Cfg::ROW, TPW = Cfg::TPW;
   constexpr int P = kStatePrefetch;
@@ -304,6 +319,9 @@ __global__ __launch_bounds__(kStateThreads<D>, 3) void state_mfma_kernel(
     }
   }
 
+  // The partials are written with device-scope stores (through to memory,
+  // past this XCD's L2), so that the unit's last workgroup, on any XCD, reads
+  // them with device-scope loads and no whole-cache fence.
   float *dst = partials + wg * (int64_t)(D * D + D);
   float *zs = reinterpret_cast<float *>(lds);
   if (producer) {
@@ -319,7 +337,7 @@ __global__ __launch_bounds__(kStateThreads<D>, 3) void state_mfma_kernel(
       for (int i = 0; i < 16; ++i) {
         const int p = 32 * cw + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
         const int e = 32 * t + (lane & 31);
-        dst[p * D + e] = acc[t][i];
+        __hip_atomic_store(dst + p * D + e, acc[t][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
@@ -327,21 +345,48 @@ __global__ __launch_bounds__(kStateThreads<D>, 3) void state_mfma_kernel(
   if (tid < D) {
     float s = 0.f;
     for (int gidx = 0; gidx < TPP; ++gidx) s += zs[gidx * D + tid];
-    dst[D * D + tid] = s;
+    __hip_atomic_store(dst + D * D + tid, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (fz.cnt != nullptr) {
+    // The unit's last workgroup to finish sums its C partials (the reduce
+    // stage, folded in).  Each thread waits until its device-scope stores
+    // are complete, then one thread counts the workgroup done; the count
+    // only picks which workgroup sums, never the order of the sums.
+    __shared__ unsigned s_last;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+      const unsigned before = __hip_atomic_fetch_add(fz.cnt + unit, 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+      s_last = before == (unsigned)(a.C - 1) ? 1u : 0u;
+    }
+    __syncthreads();
+    if (s_last != 0u) {
+      const int64_t stride = (int64_t)D * D + D;
+      const DeviceLoad4 load{head_rows_rsrc(reinterpret_cast<const uint16_t *>(
+                                 partials + unit * a.C * stride),
+                             (uint32_t)(a.C * stride * 4)),
+                             partials + unit * a.C * stride};
+      for (int64_t i4 = 4 * tid; i4 < stride; i4 += 4 * Cfg::NT)
+        reduce_prefix_values(partials, fz.states, fz.frags, fz.S_in, fz.z_in, fz.S_out, fz.z_out,
+                             unit, 1, a.C, D, i4, load);
+      if (tid == 0)
+        __hip_atomic_store(fz.cnt + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);  // prefetches past the chunk are still in flight
 }
 
 template <int D, bool kBeta>
 hipError_t state_d(const Plan &p, const void *k, const void *v, const void *beta,
-                   const float2 *tab, float *part, hipStream_t stream) {
+                   const float2 *tab, float *part, const FusedReduce &fz, hipStream_t stream) {
   const size_t lds = state_mfma_lds_bytes(p);
   auto kern = state_mfma_kernel<D, kBeta>;
   const hipError_t e = lds_limit_once((const void *)kern);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)(p.units * p.C)), dim3(StateCfg<D>::NT), lds, stream,
                      (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)beta, tab, part,
-                     make_margs(p));
+                     make_margs(p), fz);
   return hipGetLastError();
 }
 
@@ -354,13 +399,15 @@ size_t state_mfma_lds_bytes(const Plan &p) {
 }
 
 hipError_t launch_state_mfma(const Plan &p, const void *k, const void *v, const void *beta,
-                             const float2 *tab, float *partials, hipStream_t stream) {
+                             const float2 *tab, float *partials, const FusedReduce &fuse,
+                             hipStream_t stream) {
+  if (fuse.cnt != nullptr && p.nb != 1) return hipErrorInvalidValue;
   if (p.d == 128)
-    return beta ? state_d<128, true>(p, k, v, beta, tab, partials, stream)
-                : state_d<128, false>(p, k, v, beta, tab, partials, stream);
+    return beta ? state_d<128, true>(p, k, v, beta, tab, partials, fuse, stream)
+                : state_d<128, false>(p, k, v, beta, tab, partials, fuse, stream);
   if (p.d == 64)
-    return beta ? state_d<64, true>(p, k, v, beta, tab, partials, stream)
-                : state_d<64, false>(p, k, v, beta, tab, partials, stream);
+    return beta ? state_d<64, true>(p, k, v, beta, tab, partials, fuse, stream)
+                : state_d<64, false>(p, k, v, beta, tab, partials, fuse, stream);
   return hipErrorInvalidValue;
 }
 
