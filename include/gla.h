@@ -43,10 +43,26 @@
  * Streams.  All work is enqueued on `stream` (NULL = the null stream) with
  *   no host synchronisation; GLA_OK means "enqueued".  Errors raised by a
  *   kernel at run time surface at the caller's next synchronisation.
- * Errors.  Arguments are validated on the host before any HIP call; a
- *   failing call enqueues nothing.  gla_last_error() returns a description
- *   of the last failure on the calling thread.  No C++ exception crosses
- *   this interface.
+ * Errors.  Arguments are validated on the host before any HIP call, and
+ *   the dynamic-LDS attributes of all the library's kernels are set on a
+ *   device before the library's first launch there: a call that returns
+ *   GLA_ERR_INVALID_ARG, GLA_ERR_UNSUPPORTED or GLA_ERR_ALLOC has enqueued
+ *   nothing.  GLA_ERR_HIP means that the HIP runtime refused a call or a
+ *   launch; when it refuses a later launch of a call, earlier kernels of
+ *   that call may already be enqueued, and the call's outputs (for
+ *   gla_block_step with update also the cache) are then unspecified.
+ *   gla_last_error() returns a description of the last failure on the
+ *   calling thread.  No C++ exception crosses this interface.
+ * Library memory.  On each device the library keeps, until the process
+ *   ends: the RoPE (cos, sin) table of every (T, Hs, Ws, d, rope_theta,
+ *   t_offset) it has met, up to 256 of them (T*d/8 + 3*(Hs + Ws)*d/16
+ *   entries of 8 bytes each, computed on the calling stream by a shape's
+ *   first call), and a set of 256 KiB of counters for each stream it has run
+ *   on, up to 64 streams (zeroed on that stream by its first call).  Any
+ *   entry point may allocate these at first use; gla_forward_noalloc and
+ *   calls made during stream capture never do (they compute the table into
+ *   their workspace and run the reduce as a kernel of its own, with bitwise
+ *   the same results).
  * Determinism.  For identical inputs, shapes and device, results are
  *   bitwise identical run to run (fixed-order reductions, no float atomics).
  */
@@ -110,8 +126,9 @@ gla_status gla_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t Hs, int6
 /*
  * Either operator with a caller-owned workspace (device memory, at least
  * gla_workspace_bytes() bytes, 256-byte aligned); frames_per_block = 0 is
- * the non-causal operator.  Allocates nothing.  Calls that share a
- * workspace must be ordered on one stream.
+ * the non-causal operator.  Allocates no per-call memory (only the library
+ * memory described above, at first use).  Calls that share a workspace must
+ * be ordered on one stream.
  */
 gla_status gla_forward_ws(const void *q, const void *k, const void *v, const void *g, void *out,
                           int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, int64_t d,
@@ -193,7 +210,7 @@ gla_status gla_gated_forward(const void *q, const void *k, const void *v, const 
  * GLA_ERR_INVALID_ARG.  The cache may not overlap any tensor.
  * workspace: NULL (taken stream-ordered on `stream`, like gla_forward) or
  * at least gla_workspace_bytes(B, H, Tb, Hs, Ws, d, 0, dtype) bytes of
- * device memory, 256-byte aligned (then nothing is allocated).
+ * device memory, 256-byte aligned (then no per-call memory is allocated).
  */
 gla_status gla_block_step(const void *q, const void *k, const void *v, const void *g, void *out,
                           float *S_io, float *z_io, int64_t B, int64_t H, int64_t Tb, int64_t Hs,
@@ -242,7 +259,7 @@ gla_status gla_backward_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t
  * the decomposition beyond rounding.
  * workspace: NULL (taken stream-ordered on `stream`) or at least
  * gla_token_causal_workspace_bytes() bytes of device memory, 256-byte
- * aligned (then nothing is allocated).
+ * aligned (then no per-call memory is allocated).
  */
 gla_status gla_token_causal_forward(const void *q, const void *k, const void *v, const void *g,
                                     void *out, int64_t B, int64_t H, int64_t T, int64_t Hs,

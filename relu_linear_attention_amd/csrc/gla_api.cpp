@@ -66,6 +66,15 @@ gla_status device_cus(int *cus) {
     int n = 0;
     e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(multiprocessor count)");
+    // every kernel's dynamic-LDS limit, before the first launch on this
+    // device: no later call can then fail on an attribute mid-plan
+    for (auto set : {gla::state_mfma_lds_limits, gla::apply_reg_lds_limits,
+                     gla::causal_mfma_lds_limits, gla::backward_mfma_lds_limits,
+                     gla::vector_lds_limits, gla::causal_vector_lds_limits,
+                     gla::backward_vector_lds_limits}) {
+      e = set();
+      if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute (dynamic LDS limit)");
+    }
     g_cu_count[dev] = n > 0 ? n : 1;
   }
   *cus = g_cu_count[dev];

@@ -351,6 +351,13 @@ size_t apply_reg_lds_bytes(const Plan &p) {
 
 int64_t apply_reg_item_tokens() { return kItem; }
 
+hipError_t apply_reg_lds_limits() {
+  return lds_limits({(const void *)apply_reg_kernel<128, false>,
+                     (const void *)apply_reg_kernel<128, true>,
+                     (const void *)apply_reg_kernel<64, false>,
+                     (const void *)apply_reg_kernel<64, true>});
+}
+
 hipError_t launch_apply_reg(const Plan &p, const void *q, const void *g, const float *states,
                             const uint16_t *frags, const float2 *tab, const void *rms_w,
                             void *out, hipStream_t stream) {

@@ -456,6 +456,23 @@ hipError_t bwd_t(const Plan &p, const void *q, const void *k, const void *v, con
 
 }  // namespace
 
+template <typename TIn>
+hipError_t backward_vector_limits() {
+  return lds_limits({(const void *)bwd_q_kernel<TIn, 16>,  (const void *)bwd_kv_kernel<TIn, 16>,
+                     (const void *)bwd_q_kernel<TIn, 32>,  (const void *)bwd_kv_kernel<TIn, 32>,
+                     (const void *)bwd_q_kernel<TIn, 48>,  (const void *)bwd_kv_kernel<TIn, 48>,
+                     (const void *)bwd_q_kernel<TIn, 64>,  (const void *)bwd_kv_kernel<TIn, 64>,
+                     (const void *)bwd_q_kernel<TIn, 80>,  (const void *)bwd_kv_kernel<TIn, 80>,
+                     (const void *)bwd_q_kernel<TIn, 96>,  (const void *)bwd_kv_kernel<TIn, 96>,
+                     (const void *)bwd_q_kernel<TIn, 112>, (const void *)bwd_kv_kernel<TIn, 112>,
+                     (const void *)bwd_q_kernel<TIn, 128>, (const void *)bwd_kv_kernel<TIn, 128>});
+}
+
+hipError_t backward_vector_lds_limits() {
+  const hipError_t e = backward_vector_limits<uint16_t>();
+  return e != hipSuccess ? e : backward_vector_limits<float>();
+}
+
 hipError_t launch_backward(const Plan &p, const void *q, const void *k, const void *v,
                            const void *g, const void *dout, const float *states,
                            const float2 *tab, float *partials, float *grads, void *dq, void *dk,

@@ -672,6 +672,11 @@ size_t bwd_q_mfma_lds_bytes(const Plan &p) {
   return 0;
 }
 
+hipError_t backward_mfma_lds_limits() {
+  return lds_limits({(const void *)bwd_q_mfma_kernel<128>, (const void *)bwd_q_mfma_kernel<64>,
+                     (const void *)bwd_kv_mfma_kernel<128>, (const void *)bwd_kv_mfma_kernel<64>});
+}
+
 hipError_t launch_bwd_q_mfma(const Plan &p, const void *q, const void *g, const void *dout,
                              const float *states, const float2 *tab, void *dq, void *dg,
                              float *partials, hipStream_t stream) {

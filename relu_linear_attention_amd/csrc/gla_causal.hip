@@ -329,6 +329,23 @@ hipError_t causal_vec_t(const Plan &p, const void *q, const void *k, const void 
 
 }  // namespace
 
+template <typename TIn>
+hipError_t causal_vector_limits() {
+  return lds_limits({(const void *)causal_vector_kernel<TIn, 16>,
+                     (const void *)causal_vector_kernel<TIn, 32>,
+                     (const void *)causal_vector_kernel<TIn, 48>,
+                     (const void *)causal_vector_kernel<TIn, 64>,
+                     (const void *)causal_vector_kernel<TIn, 80>,
+                     (const void *)causal_vector_kernel<TIn, 96>,
+                     (const void *)causal_vector_kernel<TIn, 112>,
+                     (const void *)causal_vector_kernel<TIn, 128>});
+}
+
+hipError_t causal_vector_lds_limits() {
+  const hipError_t e = causal_vector_limits<uint16_t>();
+  return e != hipSuccess ? e : causal_vector_limits<float>();
+}
+
 hipError_t launch_range_prefix(const Plan &p, const float *partials, float *states,
                                hipStream_t stream) {
   const int64_t stride = kPartialStride(p.d);

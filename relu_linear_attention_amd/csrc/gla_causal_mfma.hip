@@ -479,6 +479,10 @@ size_t causal_mfma_lds_bytes(const Plan &p) {
   return 0;
 }
 
+hipError_t causal_mfma_lds_limits() {
+  return lds_limits({(const void *)causal_mfma_kernel<128>, (const void *)causal_mfma_kernel<64>});
+}
+
 hipError_t launch_causal_mfma(const Plan &p, const void *q, const void *k, const void *v,
                               const void *g, const float *states, const float2 *tab, void *out,
                               hipStream_t stream) {

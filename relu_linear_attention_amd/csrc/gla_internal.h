@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 namespace gla {
 
 // Work decomposition of one call, computed on the host.
@@ -195,6 +197,24 @@ hipError_t launch_apply_generic(const Plan &p, const void *q, const void *g, con
 // kernel's static LDS, once per (kernel, device) rather than before every
 // launch; thread-safe.
 hipError_t lds_limit_once(const void *kern);
+// lds_limit_once for each kernel of a list (stops at the first failure).
+inline hipError_t lds_limits(std::initializer_list<const void *> kerns) {
+  for (const void *k : kerns) {
+    const hipError_t e = lds_limit_once(k);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+// The limits of every kernel of one translation unit; the library sets them
+// all once per device, before its first launch there, so that no call fails
+// on an attribute after it has enqueued work.
+hipError_t apply_reg_lds_limits();
+hipError_t state_mfma_lds_limits();
+hipError_t causal_mfma_lds_limits();
+hipError_t backward_mfma_lds_limits();
+hipError_t vector_lds_limits();
+hipError_t causal_vector_lds_limits();
+hipError_t backward_vector_lds_limits();
 // dynamic LDS of the matrix-core state kernel
 size_t state_mfma_lds_bytes(const Plan &p);
 // The reduce folded into the state kernel (one temporal block, nb == 1):
@@ -260,8 +280,11 @@ hipError_t launch_bwd_kv_mfma(const Plan &p, const void *k, const void *v, const
                               const float2 *tab, void *dk, void *dv, hipStream_t stream);
 
 // Division by a fixed divisor d >= 1 for dividends 0 <= n < 2^31, by a
-// multiply-high and a shift: with s = ceil(log2 d) and
-// m = floor(2^32 (2^s - d) / d) + 1, n / d = (mulhi(n, m) + n) >> s.
+// multiply-high and a shift: the division by invariant integers using
+// multiplication of Granlund and Montgomery (PLDI 1994), in its N+1-bit
+// multiplier form.  With s = ceil(log2 d) and m = floor(2^32 (2^s - d) / d)
+// + 1, n / d = (mulhi(n, m) + n) >> s (the sum stays below 2^32 because
+// n < 2^31).
 struct FastDiv {
   uint32_t d, m, s;
   static FastDiv make(uint32_t d) {

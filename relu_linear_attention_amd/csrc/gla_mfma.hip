@@ -392,6 +392,13 @@ hipError_t state_d(const Plan &p, const void *k, const void *v, const void *beta
 
 }  // namespace
 
+hipError_t state_mfma_lds_limits() {
+  return lds_limits({(const void *)state_mfma_kernel<128, false>,
+                     (const void *)state_mfma_kernel<128, true>,
+                     (const void *)state_mfma_kernel<64, false>,
+                     (const void *)state_mfma_kernel<64, true>});
+}
+
 size_t state_mfma_lds_bytes(const Plan &p) {
   const size_t ops = p.d == 128 ? 2 * (StateCfg<128>::SET_BYTES + StateCfg<128>::POS_BYTES)
                                  : 2 * (StateCfg<64>::SET_BYTES + StateCfg<64>::POS_BYTES);

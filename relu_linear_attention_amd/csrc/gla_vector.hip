@@ -310,6 +310,23 @@ hipError_t apply_t(const Plan &p, const void *q, const void *g, const float *st,
 
 }  // namespace
 
+template <typename TIn>
+hipError_t apply_vector_limits() {
+  return lds_limits({(const void *)apply_vector_kernel<TIn, 16>,
+                     (const void *)apply_vector_kernel<TIn, 32>,
+                     (const void *)apply_vector_kernel<TIn, 48>,
+                     (const void *)apply_vector_kernel<TIn, 64>,
+                     (const void *)apply_vector_kernel<TIn, 80>,
+                     (const void *)apply_vector_kernel<TIn, 96>,
+                     (const void *)apply_vector_kernel<TIn, 112>,
+                     (const void *)apply_vector_kernel<TIn, 128>});
+}
+
+hipError_t vector_lds_limits() {
+  const hipError_t e = apply_vector_limits<uint16_t>();
+  return e != hipSuccess ? e : apply_vector_limits<float>();
+}
+
 hipError_t launch_state_generic(const Plan &p, const void *k, const void *v, const void *beta,
                                 const float2 *tab, float *partials, hipStream_t stream) {
   return p.bf16 ? state_t<uint16_t>(p, k, v, beta, tab, partials, stream)

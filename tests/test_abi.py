@@ -220,3 +220,22 @@ def test_profile_read_without_records(lib):
                         "causal_apply"}
     assert all(v == (0, 0.0) for v in rec.values())
     gla.gla_profile_enable(False)
+
+
+def _device_count() -> int:
+    try:
+        import torch
+
+        return torch.cuda.device_count()  # does not initialise the GPU
+    except Exception:
+        return 0
+
+
+@pytest.mark.skipif(_device_count() > 0, reason="a GPU is visible: the call would launch kernels")
+def test_valid_call_without_a_device_is_a_hip_error(lib):
+    # arguments that pass every host check; the first HIP call (the device
+    # query) fails, which is GLA_ERR_HIP naming that call
+    p = [ctypes.c_void_p(FAKE * i) for i in (1, 3, 5, 7, 9)]
+    assert lib.gla_forward(*p, 1, 2, 2, 4, 4, 32, 1e4, 1e-6, 0, None) == 4
+    assert "hipGetDevice" in gla.gla_last_error()
+    assert gla.status_string(4) == "HIP runtime error"
