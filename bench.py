@@ -1,8 +1,10 @@
 """Throughput of the gated ReLU linear-attention token mixer on one MI355X.
 
-One step = one call of the whole operator (RoPE table, state partials,
-reduce/prefix, apply) over one batch of synthetic inputs already resident in
-HBM, through the C ABI (gla_forward_ws with a pre-allocated workspace).
+One step = one call of the whole operator over one batch of synthetic inputs
+already resident in HBM, through the C ABI (gla_forward_ws with a
+pre-allocated workspace): the state kernel (chunk partials, with the reduce
+folded into each unit's last workgroup) and the apply kernel; the RoPE table
+comes from the library's per-shape cache after the first call.
 
     python bench.py [--steps K] [--warmup W] [--workload 720p_81f]
 
@@ -27,6 +29,7 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
 PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector, published
+PEAK_BF16_MFMA_FLOPS = 2.5e15  # MI355X dense bf16 matrix cores, published
 DEFAULT_WORKLOAD = "720p_81f"
 CSRC = os.path.join(ROOT, "relu_linear_attention_amd", "csrc")
 
@@ -67,6 +70,52 @@ def measured_traffic(workload: str):
     return {k: (fk * scale_f + wk * scale_w) * 1024.0 for k, (fk, wk) in kernels.items()}
 
 
+def measured_counters(workload: str):
+    """Normalised matrix-core busy fraction per kernel from the committed
+    rocprofv3 counter summary (lines "mfma_busy <kernel> <fraction>"), or {}
+    when there is none or the kernels have changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"counters_{workload}.txt")
+    if not os.path.exists(path):
+        return {}
+    digest, busy = None, {}
+    with open(path) as f:
+        for line in f:
+            parts = line.split()
+            if not parts or parts[0].startswith("#"):
+                continue
+            if parts[0] == "source_digest":
+                digest = parts[1]
+            elif parts[0] == "mfma_busy":
+                busy[parts[1]] = float(parts[2])
+    return busy if digest == source_digest() else {}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def per_call_ms(call, n: int, stream) -> list:
+    """n calls, each between its own pair of events on `stream` (the events
+    sit between calls, outside any kernel): per-call durations in ms."""
+    import torch
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(n):
+        call()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
+
+
 def cpu_baseline(w, dev_inputs):
     """The fp64 oracle, as it stands, on one full forward of the workload."""
     import oracle
@@ -81,6 +130,7 @@ def cpu_baseline(w, dev_inputs):
         "value": w.B * w.N / dt,
         "unit": "tokens/s",
         "cores": oracle.num_threads(),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"one full fp64 forward of the {w.name} layer ({w.B}x{w.N} tokens, "
                    f"{w.H} heads, d={w.d}) on the host, inputs copied from HBM; "
@@ -440,15 +490,17 @@ def main(argv=None) -> int:
         gla.gla_forward_ws(q, k, v, g, out, w.grid, ws, w.frames_per_block, w.theta, w.eps,
                            stream=stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    # the W untimed warm-up calls, each between its own events (its duration
+    # is reported, not counted: the first calls of a process run slower)
+    warm_ms = per_call_ms(step, args.warmup, stream) if args.warmup else []
 
     # timed region: K steps between events on `stream`; then K more steps with
     # every kernel bracketed by HIP events on `stream` for the per-kernel
-    # durations (the roofline of the dominant kernel)
+    # durations (the roofline of the dominant kernel); then K more, each
+    # between its own events, for the per-call median, min and max
     ms_per_step, wall, _ = timed_calls(step, args.steps, stream, profile=False)
     _, _, stages = timed_calls(step, args.steps, stream, profile=True)
+    calls_ms = sorted(per_call_ms(step, args.steps, stream))
     tokens = w.B * w.N
     elem = w.B * w.N * w.H * w.d * w.elem_bytes
     algo_bytes = {"state_partials": 2 * elem, "apply": 3 * elem}
@@ -461,6 +513,19 @@ def main(argv=None) -> int:
     kernel_names = {"state_partials": "state_mfma_kernel" if mfma else "state_vector_kernel",
                     "apply": "apply_mfma_kernel" if mfma else "apply_vector_kernel"}
     traffic = measured_traffic(w.name).get(kernel_names[dominant])
+    # matrix-core work issued per launch (flops of the bf16 products as
+    # issued, hi/lo splits included): state 2 products of d x d per token and
+    # head, apply 3 plus the 16-row normaliser product per 32 features
+    hd = w.B * w.N * w.H
+    mfma_flops = {"state_partials": 2 * 2 * hd * w.d * w.d,
+                  "apply": 3 * 2 * hd * w.d * w.d + 2 * 16 * hd * w.d}
+    busy = measured_counters(w.name)
+    mfma_util = {}
+    for st, kname in kernel_names.items():
+        if mfma and stage_ms.get(st):
+            mfma_util[kname] = {
+                "issued_flops_frac": mfma_flops[st] / (stage_ms[st] * 1e-3) / PEAK_BF16_MFMA_FLOPS,
+                "busy_counter": busy.get(kname)}
 
     result = {
         "metric": "GLA fwd tokens/s at 720p/81f (32 heads, d=128, bf16) + % of HBM roofline",
@@ -488,7 +553,16 @@ def main(argv=None) -> int:
             "frac": achieved / PEAK_HBM_GBPS,
             "traffic": traffic,
             "algorithmic_bytes_per_launch": algo_bytes[dominant],
+            "mfma_busy": busy.get(kernel_names[dominant]),
+            "mfma_busy_note": ("SQ_VALU_MFMA_BUSY_CYCLES / (4 SIMDs x CUs x GRBM_GUI_ACTIVE / 8 "
+                               "XCDs): the fraction of the kernel's cycles its SIMDs spent in "
+                               "matrix-core instructions, from the committed counter summary"),
         },
+        "mfma_utilisation": mfma_util,
+        "per_call_ms": {"median": calls_ms[len(calls_ms) // 2], "min": calls_ms[0],
+                        "max": calls_ms[-1], "n": len(calls_ms),
+                        "note": "one event pair per call, after the timed pass"},
+        "warmup_calls_ms": warm_ms,
         "stages_ms": stage_ms,
         "same_bytes_reference": same_bytes_reference(x, args.steps, min(args.warmup, 20)),
         "path": {

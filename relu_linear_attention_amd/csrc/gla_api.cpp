@@ -68,7 +68,7 @@ gla_status device_cus(int *cus) {
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(multiprocessor count)");
     // every kernel's dynamic-LDS limit, before the first launch on this
     // device: no later call can then fail on an attribute mid-plan
-    for (auto set : {gla::state_mfma_lds_limits, gla::apply_reg_lds_limits,
+    for (auto set : {gla::state_mfma_lds_limits, gla::apply_mfma_lds_limits,
                      gla::causal_mfma_lds_limits, gla::backward_mfma_lds_limits,
                      gla::vector_lds_limits, gla::causal_vector_lds_limits,
                      gla::backward_vector_lds_limits}) {
@@ -274,15 +274,15 @@ gla_status make_plan(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, in
     // would not fit in LDS beside S and the staging tiles.
     P.hpw = 1;
     P.ag = B * P.nb * H;
-    const int64_t item = gla::apply_reg_item_tokens();
+    const int64_t item = gla::apply_mfma_item_tokens();
     const int64_t items = ceil_div(P.L, item);
     P.ar = 1;
     for (;;) {
       P.air = ceil_div(items, P.ar);
-      if (gla::apply_reg_lds_bytes(P) <= 160 * 1024 || P.air == 1) break;
+      if (gla::apply_mfma_lds_bytes(P) <= 160 * 1024 || P.air == 1) break;
       P.ar *= 2;
     }
-    if (gla::apply_reg_lds_bytes(P) > 160 * 1024) P.mfma = false;
+    if (gla::apply_mfma_lds_bytes(P) > 160 * 1024) P.mfma = false;
     const int64_t sranges = P.ag * P.ar;
     P.am = std::max<int64_t>(1, std::min<int64_t>(P.air, cus / std::max<int64_t>(1, sranges)));
     if (sranges * P.am > 0x7fffffff) P.mfma = false;
@@ -683,7 +683,7 @@ gla_status run_plan(const Plan &P, const void *q, const void *k, const void *v, 
   if (st != GLA_OK) return st;
   if (!apply) return GLA_OK;
   return timed_launch(3, stream, "apply kernel", [&] {
-    return P.mfma ? gla::launch_apply_reg(P, q, g, states, frags, tab, gates.rms_w, out, stream)
+    return P.mfma ? gla::launch_apply_mfma(P, q, g, states, frags, tab, gates.rms_w, out, stream)
                   : gla::launch_apply_generic(P, q, g, states, tab, gates.rms_w, out, stream);
   });
 }

@@ -68,7 +68,7 @@ constexpr int64_t kItem = 16 * (kApplyThreads / 64);  // tokens of an item: a ti
 // rms_eps) and by the weight w [D].  A token's D values are spread over the
 // four lanes l % 16 == token (32 each), summed with two lane exchanges.
 template <int D, bool kNorm>
-__global__ __launch_bounds__(kApplyThreads) void apply_reg_kernel(
+__global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ g,
     const float *__restrict__ states, const uint16_t *__restrict__ frags,
     const float2 *__restrict__ tab, const uint16_t *__restrict__ rms_w,
@@ -324,11 +324,11 @@ __global__ __launch_bounds__(kApplyThreads) void apply_reg_kernel(
 }
 
 template <int D, bool kNorm>
-hipError_t apply_reg_d(const Plan &p, const void *q, const void *g, const float *states,
+hipError_t apply_mfma_d(const Plan &p, const void *q, const void *g, const float *states,
                        const uint16_t *frags, const float2 *tab, const void *rms_w, void *out,
                        hipStream_t stream) {
-  const size_t lds = apply_reg_lds_bytes(p);
-  auto kern = apply_reg_kernel<D, kNorm>;
+  const size_t lds = apply_mfma_lds_bytes(p);
+  auto kern = apply_mfma_kernel<D, kNorm>;
   const hipError_t attr = lds_limit_once((const void *)kern);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(kern, dim3((unsigned)(p.ag * p.ar * p.am)), dim3(kApplyThreads), lds,
@@ -339,7 +339,7 @@ hipError_t apply_reg_d(const Plan &p, const void *q, const void *g, const float 
 
 }  // namespace
 
-size_t apply_reg_lds_bytes(const Plan &p) {
+size_t apply_mfma_lds_bytes(const Plan &p) {
   const int64_t d = p.d;
   const int64_t hw = p.Hs * p.Ws;
   const int64_t sr_tokens = p.air * kItem;
@@ -349,24 +349,24 @@ size_t apply_reg_lds_bytes(const Plan &p) {
                   (kApplyThreads / 64) * (16 * (2 * d + 16)) + entries * 8);
 }
 
-int64_t apply_reg_item_tokens() { return kItem; }
+int64_t apply_mfma_item_tokens() { return kItem; }
 
-hipError_t apply_reg_lds_limits() {
-  return lds_limits({(const void *)apply_reg_kernel<128, false>,
-                     (const void *)apply_reg_kernel<128, true>,
-                     (const void *)apply_reg_kernel<64, false>,
-                     (const void *)apply_reg_kernel<64, true>});
+hipError_t apply_mfma_lds_limits() {
+  return lds_limits({(const void *)apply_mfma_kernel<128, false>,
+                     (const void *)apply_mfma_kernel<128, true>,
+                     (const void *)apply_mfma_kernel<64, false>,
+                     (const void *)apply_mfma_kernel<64, true>});
 }
 
-hipError_t launch_apply_reg(const Plan &p, const void *q, const void *g, const float *states,
+hipError_t launch_apply_mfma(const Plan &p, const void *q, const void *g, const float *states,
                             const uint16_t *frags, const float2 *tab, const void *rms_w,
                             void *out, hipStream_t stream) {
   if (p.d == 128)
-    return rms_w ? apply_reg_d<128, true>(p, q, g, states, frags, tab, rms_w, out, stream)
-                 : apply_reg_d<128, false>(p, q, g, states, frags, tab, rms_w, out, stream);
+    return rms_w ? apply_mfma_d<128, true>(p, q, g, states, frags, tab, rms_w, out, stream)
+                 : apply_mfma_d<128, false>(p, q, g, states, frags, tab, rms_w, out, stream);
   if (p.d == 64)
-    return rms_w ? apply_reg_d<64, true>(p, q, g, states, frags, tab, rms_w, out, stream)
-                 : apply_reg_d<64, false>(p, q, g, states, frags, tab, rms_w, out, stream);
+    return rms_w ? apply_mfma_d<64, true>(p, q, g, states, frags, tab, rms_w, out, stream)
+                 : apply_mfma_d<64, false>(p, q, g, states, frags, tab, rms_w, out, stream);
   return hipErrorInvalidValue;
 }
 

@@ -208,7 +208,7 @@ inline hipError_t lds_limits(std::initializer_list<const void *> kerns) {
 // The limits of every kernel of one translation unit; the library sets them
 // all once per device, before its first launch there, so that no call fails
 // on an attribute after it has enqueued work.
-hipError_t apply_reg_lds_limits();
+hipError_t apply_mfma_lds_limits();
 hipError_t state_mfma_lds_limits();
 hipError_t causal_mfma_lds_limits();
 hipError_t backward_mfma_lds_limits();
@@ -236,12 +236,12 @@ hipError_t launch_state_mfma(const Plan &p, const void *k, const void *v, const 
 // Register-resident output stage (bf16, d = 64 or 128): frags holds S^T of
 // every unit as bf16 hi and lo matrix-core A fragments,
 // [units][part][d/32][d/16][64 lanes][8]; its LDS bytes for the plan.
-hipError_t launch_apply_reg(const Plan &p, const void *q, const void *g, const float *states,
+hipError_t launch_apply_mfma(const Plan &p, const void *q, const void *g, const float *states,
                             const uint16_t *frags, const float2 *tab, const void *rms_w,
                             void *out, hipStream_t stream);
-size_t apply_reg_lds_bytes(const Plan &p);
+size_t apply_mfma_lds_bytes(const Plan &p);
 // tokens of one work item of the output stage
-int64_t apply_reg_item_tokens();
+int64_t apply_mfma_item_tokens();
 
 // Token-causal form.  The state stage writes one partial per chunk of Lc
 // tokens (units = B*H, one block each); the prefix kernel writes, for every
