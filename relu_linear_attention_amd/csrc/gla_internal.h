@@ -233,9 +233,9 @@ struct FusedReduce {
 hipError_t launch_state_mfma(const Plan &p, const void *k, const void *v, const void *beta,
                              const float2 *tab, float *partials, const FusedReduce &fuse,
                              hipStream_t stream);
-// Register-resident output stage (bf16, d = 64 or 128): frags holds S^T of
-// every unit as bf16 hi and lo matrix-core A fragments,
-// [units][part][d/32][d/16][64 lanes][8]; its LDS bytes for the plan.
+// Output stage on the matrix cores (bf16, d = 64 or 128): frags holds S of
+// every unit as bf16 hi and lo parts, [units][part][d][d] row-major (written
+// by the reduce); its LDS bytes for the plan.
 hipError_t launch_apply_mfma(const Plan &p, const void *q, const void *g, const float *states,
                             const uint16_t *frags, const float2 *tab, const void *rms_w,
                             void *out, hipStream_t stream);

@@ -26,7 +26,7 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 struct MArgs {
   int64_t N, H, Hs, Ws;
   int64_t nb, L, C, Lc, R, Lr;
-  int64_t hpw, ag, ar, air, am;  // the register-resident output stage's work layout
+  int64_t hpw, ag, ar, air, am;  // the output stage's work layout (Plan)
   int64_t tab_h_off;  // global entry offset of the h rows (the w rows follow)
   FastDiv div_hw, div_w;  // by Hs*Ws and by Ws (token indices < 2^31)
   float eps;
