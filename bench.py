@@ -317,9 +317,11 @@ def backward_leg(w, x, steps: int, warmup: int):
                                      else gla.GLA_F32) == 1
     grad_ms = stage_ms["backward"]
     if mfma:
-        # the gradient kernels stream nine tensor passes (q, g, dout, k, v read;
-        # dq, dg, dk, dv written) against their matrix-core products
-        names = ("bwd_q_mfma_kernel", "bwd_reduce_kernel", "bwd_kv_mfma_kernel")
+        # the gradient kernels' algorithmic bytes are nine tensor passes (q, g,
+        # dout, k, v read; dq, dg, dk, dv written); the state pass reads q, g
+        # and dout a second time, which the measured traffic shows
+        names = ("bwd_token_mfma_kernel", "bwd_dstate_mfma_kernel", "bwd_reduce_kernel",
+                 "bwd_kv_mfma_kernel")
         measured = measured_traffic(w.name)
         roof = {"bound": "hbm", "kernel": " + ".join(names),
                 "achieved": nbytes / (grad_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
@@ -328,7 +330,8 @@ def backward_leg(w, x, steps: int, warmup: int):
                             else None),
                 "algorithmic_bytes_per_launch": nbytes}
         roof["frac"] = roof["achieved"] / PEAK_HBM_GBPS
-        kernels = "matrix-core gradient kernels (query side, block sums, key/value side)"
+        kernels = ("matrix-core gradient kernels (query side: token pass and state pass; block "
+                   "sums; key/value side)")
     else:
         # fp32 FMA work on the vector units: per token-head, five d x d products
         # (num, S dnum and the dS outer product on the query side; G v and

@@ -70,6 +70,7 @@ gla_status device_cus(int *cus) {
     // device: no later call can then fail on an attribute mid-plan
     for (auto set : {gla::state_mfma_lds_limits, gla::apply_mfma_lds_limits,
                      gla::causal_mfma_lds_limits, gla::backward_mfma_lds_limits,
+                     gla::backward_query_lds_limits,
                      gla::vector_lds_limits, gla::causal_vector_lds_limits,
                      gla::backward_vector_lds_limits}) {
       e = set();
@@ -323,11 +324,13 @@ gla_status make_plan(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, in
   P.total_bytes = off;
   P.off_bpart = off;
   // (the vector gradient kernels write Rb range partials per unit, the
-  // matrix-core ones R)
-  off = align256(off + (size_t)P.units * std::max(P.Rb, P.R) * gla::kPartialStride(d) *
+  // matrix-core ones C chunk partials)
+  off = align256(off + (size_t)P.units * std::max(P.Rb, P.C) * gla::kPartialStride(d) *
                            sizeof(float));
   P.off_grad = off;
   off = align256(off + (size_t)P.units * gla::kPartialStride(d) * sizeof(float));
+  P.off_dd = off;
+  if (P.mfma) off = align256(off + (size_t)(B * H * P.N) * 2 * sizeof(float));
   P.bwd_total_bytes = off;
   *p = P;
   return GLA_OK;
@@ -393,7 +396,7 @@ gla_status make_causal_plan(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t
   off = align256(off + (size_t)P.units * P.R * gla::kPartialStride(d) * sizeof(float));
   P.off_frag = off;
   P.total_bytes = off;
-  P.off_bpart = P.off_grad = P.bwd_total_bytes = off;
+  P.off_bpart = P.off_grad = P.off_dd = P.bwd_total_bytes = off;
   *p = P;
   return GLA_OK;
 }
@@ -987,6 +990,7 @@ gla_status gla_backward(const void *q, const void *k, const void *v, const void 
     st = timed_launch(4, stream, "gradient kernels", [&] {
       return gla::launch_backward(P, q, k, v, g, dout, (const float *)(base + P.off_state), tab,
                                   (float *)(base + P.off_bpart), (float *)(base + P.off_grad),
+                                  (float2 *)(base + P.off_dd),
                                   dq, dk, dv, dg, stream);
     });
   }

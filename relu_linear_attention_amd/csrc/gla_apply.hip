@@ -17,27 +17,6 @@
 namespace gla {
 namespace {
 
-// Buffer resource over the rows [n, n + 16) of one head that lie inside
-// [.., n_end): rows past n_end (and whole tiles past it) read as zeros and
-// are not written.  `base` points at feature 0 of row n.  Every input is
-// uniform across the wave; the values pass through readfirstlane so that the
-// compiler keeps the descriptor in scalar registers (a descriptor it
-// believes divergent costs a loop around every access).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t *base, int64_t n,
-                                                            int64_t n_end, uint32_t row_bytes,
-                                                            int D) {
-  const int64_t left = n_end - n;
-  const uint32_t rows = left <= 0 ? 0u : (left >= 16 ? 16u : (uint32_t)left);
-  const uint32_t bytes = __builtin_amdgcn_readfirstlane(
-      rows == 0 ? 0u : (rows - 1) * row_bytes + 2u * (uint32_t)D);
-  const uint64_t addr = (uint64_t)(uintptr_t)base;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
-  const uint16_t *p = (const uint16_t *)(uintptr_t)(((uint64_t)hi << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(p), 0, (int)bytes,
-                                           0x00020000);
-}
-
 // 16x16x32 bf16 matrix-core layout used by the apply stage:
 //   A (16 x 32):  lane l holds A[l % 16][8*(l/16) + j], j = 0..7
 //   B (32 x 16):  lane l holds B[8*(l/16) + j][l % 16]

@@ -396,16 +396,21 @@ BwdArgs make_bargs(const Plan &p) {
 template <typename TIn, int D>
 hipError_t bwd_d(const Plan &p, const void *q, const void *k, const void *v, const void *g,
                  const void *dout, const float *states, const float2 *tab, float *partials,
-                 float *grads, void *dq, void *dk, void *dv, void *dg, hipStream_t stream) {
+                 float *grads, float2 *dd, void *dq, void *dk, void *dv, void *dg,
+                 hipStream_t stream) {
   const int64_t stride = kPartialStride(p.d), per_block = (int64_t)kBlock * 4;
   const dim3 rgrid((unsigned)(p.B * p.H), (unsigned)((stride + per_block - 1) / per_block));
   if (p.mfma && (D == 64 || D == 128) && sizeof(TIn) == 2 &&
-      bwd_q_mfma_lds_bytes(p) <= 160 * 1024) {
-    // matrix-core kernels over the apply stage's ranges (R x Lr)
-    hipError_t e = launch_bwd_q_mfma(p, q, g, dout, states, tab, dq, dg, partials, stream);
+      bwd_query_lds_bytes(p) <= 160 * 1024 && (p.Lr % 128) == 0) {
+    // matrix-core kernels: the token pass over the output stage's ranges
+    // (R x Lr), the state pass over the state stage's chunks (C x Lc), the
+    // block sums over the chunks, then the key/value side
+    hipError_t e = launch_bwd_token_mfma(p, q, g, dout, states, tab, dq, dg, dd, stream);
+    if (e != hipSuccess) return e;
+    e = launch_bwd_dstate_mfma(p, q, g, dout, dd, tab, partials, stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_reduce_kernel, rgrid, dim3(kBlock), 0, stream, partials, grads, p.nb,
-                       p.R, (int)p.d);
+                       p.C, (int)p.d);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_bwd_kv_mfma(p, k, v, grads, tab, dk, dv, stream);
@@ -436,10 +441,11 @@ hipError_t bwd_d(const Plan &p, const void *q, const void *k, const void *v, con
 template <typename TIn>
 hipError_t bwd_t(const Plan &p, const void *q, const void *k, const void *v, const void *g,
                  const void *dout, const float *states, const float2 *tab, float *partials,
-                 float *grads, void *dq, void *dk, void *dv, void *dg, hipStream_t s) {
+                 float *grads, float2 *dd, void *dq, void *dk, void *dv, void *dg, hipStream_t s) {
 #define GLA_BWD_CASE(DD)                                                                        \
   case DD:                                                                                      \
-    return bwd_d<TIn, DD>(p, q, k, v, g, dout, states, tab, partials, grads, dq, dk, dv, dg, s);
+    return bwd_d<TIn, DD>(p, q, k, v, g, dout, states, tab, partials, grads, dd, dq, dk, dv, dg, \
+                          s);
   switch (p.d) {
     GLA_BWD_CASE(16)
     GLA_BWD_CASE(32)
@@ -475,12 +481,12 @@ hipError_t backward_vector_lds_limits() {
 
 hipError_t launch_backward(const Plan &p, const void *q, const void *k, const void *v,
                            const void *g, const void *dout, const float *states,
-                           const float2 *tab, float *partials, float *grads, void *dq, void *dk,
-                           void *dv, void *dg, hipStream_t stream) {
-  return p.bf16 ? bwd_t<uint16_t>(p, q, k, v, g, dout, states, tab, partials, grads, dq, dk, dv,
-                                  dg, stream)
-                : bwd_t<float>(p, q, k, v, g, dout, states, tab, partials, grads, dq, dk, dv, dg,
-                               stream);
+                           const float2 *tab, float *partials, float *grads, float2 *dd,
+                           void *dq, void *dk, void *dv, void *dg, hipStream_t stream) {
+  return p.bf16 ? bwd_t<uint16_t>(p, q, k, v, g, dout, states, tab, partials, grads, dd, dq, dk,
+                                  dv, dg, stream)
+                : bwd_t<float>(p, q, k, v, g, dout, states, tab, partials, grads, dd, dq, dk, dv,
+                               dg, stream);
 }
 
 }  // namespace gla

@@ -44,8 +44,10 @@ struct Plan {
   // workspace layout, byte offsets
   size_t off_tab, off_part, off_state, off_frag, total_bytes;
   // the backward call's extra sections (after total_bytes): the per-range
-  // dS, dz partials and the suffix-summed gradients of the block states
-  size_t off_bpart, off_grad, bwd_total_bytes;
+  // (or, on the matrix cores, per-chunk) dS, dz partials, the suffix-summed
+  // gradients of the block states, and (matrix cores) each token's
+  // (den, dden), float2 [B*H][N]
+  size_t off_bpart, off_grad, off_dd, bwd_total_bytes;
 };
 
 constexpr int kBlock = 256;          // threads per workgroup for every kernel
@@ -212,6 +214,7 @@ hipError_t apply_mfma_lds_limits();
 hipError_t state_mfma_lds_limits();
 hipError_t causal_mfma_lds_limits();
 hipError_t backward_mfma_lds_limits();
+hipError_t backward_query_lds_limits();
 hipError_t vector_lds_limits();
 hipError_t causal_vector_lds_limits();
 hipError_t backward_vector_lds_limits();
@@ -259,23 +262,27 @@ hipError_t launch_causal_generic(const Plan &p, const void *q, const void *k, co
                                  const void *g, const float *states, const float2 *tab, void *out,
                                  hipStream_t stream);
 
-// Gradients (vector kernels): with the forward states of the call in
-// `states`, writes dq, dk, dv, dg; `partials` holds units*Rb and `grads`
-// units state vectors of d*d + d floats.
+// Gradients: with the forward states of the call in `states`, writes dq,
+// dk, dv, dg; `partials` holds units * max(Rb, C) and `grads` units state
+// vectors of d*d + d floats; `dd` (matrix-core path) B*H*N float2.
 hipError_t launch_backward(const Plan &p, const void *q, const void *k, const void *v,
                            const void *g, const void *dout, const float *states,
-                           const float2 *tab, float *partials, float *grads, void *dq, void *dk,
-                           void *dv, void *dg, hipStream_t stream);
+                           const float2 *tab, float *partials, float *grads, float2 *dd,
+                           void *dq, void *dk, void *dv, void *dg, hipStream_t stream);
 
+// Query side of the gradients on the matrix cores (bf16, d = 64 or 128), in
+// two passes: the token pass writes dq, dg and each token's (den, dden)
+// (ranges R x Lr, Lr a multiple of 128); the state pass re-reads q, g, dout
+// and writes the per-chunk dS, dz partials ([units][C][d*d + d]).
+hipError_t launch_bwd_token_mfma(const Plan &p, const void *q, const void *g, const void *dout,
+                                 const float *states, const float2 *tab, void *dq, void *dg,
+                                 float2 *dd, hipStream_t stream);
+hipError_t launch_bwd_dstate_mfma(const Plan &p, const void *q, const void *g, const void *dout,
+                                  const float2 *dd, const float2 *tab, float *partials,
+                                  hipStream_t stream);
+size_t bwd_query_lds_bytes(const Plan &p);
 // Matrix-core kernel of the key/value side of the gradients (bf16, d = 64 or
 // 128): dk, dv from G, Gz (`grads`, [units][d*d + d]); ranges R x Lr.
-// Matrix-core kernel of the query side of the gradients (bf16, d = 64 or
-// 128): dq, dg and the per-range dS, dz partials ([units][R][d*d + d]) from
-// the forward states; ranges R x Lr (Lr a multiple of 64).
-hipError_t launch_bwd_q_mfma(const Plan &p, const void *q, const void *g, const void *dout,
-                             const float *states, const float2 *tab, void *dq, void *dg,
-                             float *partials, hipStream_t stream);
-size_t bwd_q_mfma_lds_bytes(const Plan &p);
 hipError_t launch_bwd_kv_mfma(const Plan &p, const void *k, const void *v, const float *grads,
                               const float2 *tab, void *dk, void *dv, hipStream_t stream);
 

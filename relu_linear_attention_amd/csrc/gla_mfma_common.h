@@ -61,6 +61,27 @@ __device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t o
   __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, Policy);
 }
 
+// Buffer resource over the rows [n, n + 16) of one head that lie inside
+// [.., n_end): rows past n_end (and whole tiles past it) read as zeros and
+// are not written.  `base` points at feature 0 of row n.  Every input is
+// uniform across the wave; the values pass through readfirstlane so that the
+// compiler keeps the descriptor in scalar registers (a descriptor it
+// believes divergent costs a loop around every access).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t *base, int64_t n,
+                                                            int64_t n_end, uint32_t row_bytes,
+                                                            int D) {
+  const int64_t left = n_end - n;
+  const uint32_t rows = left <= 0 ? 0u : (left >= 16 ? 16u : (uint32_t)left);
+  const uint32_t bytes = __builtin_amdgcn_readfirstlane(
+      rows == 0 ? 0u : (rows - 1) * row_bytes + 2u * (uint32_t)D);
+  const uint64_t addr = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+  const uint16_t *p = (const uint16_t *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(p), 0, (int)bytes,
+                                           0x00020000);
+}
+
 // 8-byte buffer accesses (four bf16 of one token row)
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -108,6 +129,14 @@ __device__ __forceinline__ uint32_t relu_bf16x2(uint32_t x) {
   s16x2 v = __builtin_bit_cast(s16x2, x);
   s16x2 zero = {0, 0};
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(v, zero));
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+// 0xffff in each 16-bit half of x that is nonzero, else 0: for a packed
+// ReLU(x) pair, the mask of the elements with x > 0
+__device__ __forceinline__ uint32_t nonzero_mask16(uint32_t x) {
+  const u16x2 nz = __builtin_elementwise_min(__builtin_bit_cast(u16x2, x), u16x2{1, 1});
+  return __builtin_bit_cast(uint32_t, u16x2{0, 0} - nz);
 }
 
 __device__ __forceinline__ float lo_bf16(uint32_t x) { return __uint_as_float(x << 16); }
@@ -237,6 +266,33 @@ __device__ TabSlice<D> load_tab_slice(float2 *s_tab, const float2 *__restrict__ 
   tl.issue(tab, a, n_begin, n_end);
   tl.store(s_tab, tab);
   return tl.ts;
+}
+
+// The gradient of a rotated operand, in the B-operand layout of the
+// feature: lane (token, kg) holds features 32 ks + 8 kg + 4 half + i in
+// value i of a[half] (half = 0, 1), the pairs' (cos, sin) entries in cs[0..3].
+// Returns RoPE^T(a) + add, zero where the packed ReLU words relu[0..3] are
+// zero, as eight packed bf16.
+__device__ __forceinline__ uint4 rope_t_add_mask(const f32x4 &a0, const f32x4 &a1,
+                                                 const float2 (&cs)[4], const float (&add)[8],
+                                                 const uint32_t (&relu)[4]) {
+  float o[8];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const f32x4 d4 = half ? a1 : a0;
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+      const float2 c = cs[2 * half + pr];
+      const float d0 = d4[2 * pr], d1 = d4[2 * pr + 1];
+      const int j = 4 * half + 2 * pr;
+      o[j] = d0 * c.x + __builtin_fmaf(d1, c.y, add[j]);
+      o[j + 1] = d1 * c.x - __builtin_fmaf(d0, c.y, -add[j + 1]);
+    }
+  }
+  uint32_t w[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) w[m] = pack_bf16x2(o[2 * m], o[2 * m + 1]) & nonzero_mask16(relu[m]);
+  return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 // Rotate four adjacent pairs x[0..7] by the (cos, sin) entries cs[0..3].
