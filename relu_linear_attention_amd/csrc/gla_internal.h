@@ -99,6 +99,31 @@ __device__ __forceinline__ float *cache_ptr(float *S, float *z, int64_t bh, int6
   return i4 < dd ? S + bh * dd + i4 : z + bh * d + (i4 - dd);
 }
 
+// The running sums `run` of floats i4..i4+3 of unit `unit`'s state (d*d + d
+// floats: S rows, then z): written to `states` and, for S and when `frags` is
+// given, as bf16 hi + lo parts (hi = the value rounded to bf16, lo = the
+// remainder rounded to bf16; the d*d lo values follow the d*d hi values of a
+// unit, each row-major [p][e]).
+__device__ __forceinline__ void store_state4(const float4 &run, float *states, uint16_t *frags,
+                                             int64_t unit, int d, int64_t i4) {
+  const int64_t stride = (int64_t)d * d + d;
+  *reinterpret_cast<float4 *>(states + unit * stride + i4) = run;
+  if (frags != nullptr && i4 < (int64_t)d * d) {
+    const float vals[4] = {run.x, run.y, run.z, run.w};
+    uint16_t hi[4], lo[4];
+    for (int r = 0; r < 4; ++r) {
+      const __bf16 h = (__bf16)vals[r];
+      hi[r] = __builtin_bit_cast(uint16_t, h);
+      lo[r] = f32_to_bf16_bits(vals[r] - (float)h);
+    }
+    uint16_t *base = frags + unit * (int64_t)d * d * 2 + i4;
+    *reinterpret_cast<uint2 *>(base) =
+        make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
+    *reinterpret_cast<uint2 *>(base + (int64_t)d * d) =
+        make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
+  }
+}
+
 // Sum of the C chunk partials of every block unit of (batch, head) bh, in
 // chunk order, followed by the inclusive prefix over its nb temporal blocks,
 // in block order, for the four consecutive floats i4..i4+3 of the d*d + d
@@ -131,21 +156,7 @@ __device__ __forceinline__ void reduce_prefix_values(const float *partials, floa
   for (int64_t blk = 0; blk < nb; ++blk) {
     const int64_t unit = bh * nb + blk;
     add_partials(run, partials + unit * C * stride + i4, stride, 0, C, load);
-    *reinterpret_cast<float4 *>(states + unit * stride + i4) = run;
-    if (frags != nullptr && i4 < (int64_t)d * d) {
-      const float vals[4] = {run.x, run.y, run.z, run.w};
-      uint16_t hi[4], lo[4];
-      for (int r = 0; r < 4; ++r) {
-        const __bf16 h = (__bf16)vals[r];
-        hi[r] = __builtin_bit_cast(uint16_t, h);
-        lo[r] = f32_to_bf16_bits(vals[r] - (float)h);
-      }
-      uint16_t *base = frags + unit * (int64_t)d * d * 2 + i4;
-      *reinterpret_cast<uint2 *>(base) =
-          make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
-      *reinterpret_cast<uint2 *>(base + (int64_t)d * d) =
-          make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
-    }
+    store_state4(run, states, frags, unit, d, i4);
   }
   if (S_out != nullptr) {
     float *c = cache_ptr(S_out, z_out, bh, i4, d);

@@ -45,6 +45,73 @@ struct DeviceLoad4 {
   }
 };
 
+// The reduce of one unit (one temporal block) by the NT threads of its last
+// state workgroup: thread t owns the four-float slots i4 = 4 (t + k NT),
+// k = 0..K-1, of the d*d + d state vector.  The loads of all its slots are
+// interleaved, kBatch partials of every slot in flight at once, while each
+// float still adds the C partials in chunk order from its start value (the
+// carried cache or 0), so the sums are bitwise those of reduce_prefix_values
+// (one slot after another, with C / 8 round trips each, this left the other
+// compute units idle for about a dozen memory latencies at the end of a
+// small call).
+template <int D, int NT>
+__device__ __forceinline__ void fused_reduce_unit(const FusedReduce &fz, const float *partials,
+                                                  int64_t unit, int64_t C) {
+  constexpr int64_t stride = (int64_t)D * D + D;
+  constexpr int K = (int)((stride + 4 * NT - 1) / (4 * NT));
+  constexpr int kBatch = 4;
+  const float *base = partials + unit * C * stride;
+  const DeviceLoad4 load{head_rows_rsrc(reinterpret_cast<const uint16_t *>(base),
+                                        (uint32_t)(C * stride * 4)),
+                         base};
+  const int tid = threadIdx.x;
+  float4 run[K];
+  int i4[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    i4[k] = 4 * (tid + k * NT);
+    run[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (fz.S_in != nullptr && i4[k] < stride) {
+      const float *c = cache_ptr(const_cast<float *>(fz.S_in), const_cast<float *>(fz.z_in),
+                                 unit, i4[k], D);
+      run[k] = make_float4(c[0], c[1], c[2], c[3]);
+    }
+  }
+  for (int64_t c0 = 0; c0 < C; c0 += kBatch) {
+    float4 x[kBatch][K];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int64_t cj = c0 + j < C ? c0 + j : C - 1;  // clamped: loaded, not added
+#pragma unroll
+      for (int k = 0; k < K; ++k) x[j][k] = load(base + cj * stride + (i4[k] < stride ? i4[k] : 0));
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (c0 + j < C) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          run[k].x += x[j][k].x;
+          run[k].y += x[j][k].y;
+          run[k].z += x[j][k].z;
+          run[k].w += x[j][k].w;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    if (i4[k] >= stride) continue;
+    store_state4(run[k], fz.states, fz.frags, unit, D, i4[k]);
+    if (fz.S_out != nullptr) {
+      float *c = cache_ptr(fz.S_out, fz.z_out, unit, i4[k], D);
+      c[0] = run[k].x;
+      c[1] = run[k].y;
+      c[2] = run[k].z;
+      c[3] = run[k].w;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- state
 
 // Workgroups of the state kernel: twelve waves at d = 128 (one workgroup per
@@ -362,14 +429,7 @@ __global__ __launch_bounds__(kStateThreads<D>, 3) void state_mfma_kernel(
     }
     __syncthreads();
     if (s_last != 0u) {
-      const int64_t stride = (int64_t)D * D + D;
-      const DeviceLoad4 load{head_rows_rsrc(reinterpret_cast<const uint16_t *>(
-                                 partials + unit * a.C * stride),
-                             (uint32_t)(a.C * stride * 4)),
-                             partials + unit * a.C * stride};
-      for (int64_t i4 = 4 * tid; i4 < stride; i4 += 4 * Cfg::NT)
-        reduce_prefix_values(partials, fz.states, fz.frags, fz.S_in, fz.z_in, fz.S_out, fz.z_out,
-                             unit, 1, a.C, D, i4, load);
+      fused_reduce_unit<D, Cfg::NT>(fz, partials, unit, a.C);
       if (tid == 0)
         __hip_atomic_store(fz.cnt + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
