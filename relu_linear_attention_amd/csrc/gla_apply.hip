@@ -127,87 +127,113 @@ __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
   const uint16_t *q_head = q + (b * a.N * a.H + hd) * D;
   const uint16_t *g_head = g + (b * a.N * a.H + hd) * D;
   uint16_t *o_head = out + (b * a.N * a.H + hd) * D;
-  // loads of one tile: q in the B-operand layout, g as whole rows
-  auto fetch = [&](int64_t tile, uint4 (&qraw)[KS], uint4 (&grow)[St::kPasses]) {
+  // loads of one 16-token block: q in the B-operand layout, g as whole rows
+  auto fetch_q = [&](int64_t tile, uint4 (&qraw)[KS]) {
     const __amdgpu_buffer_rsrc_t rq = tile_rsrc(q_head + tile * a.H * D, tile, n_end, row_bytes, D);
-    const __amdgpu_buffer_rsrc_t rg = tile_rsrc(g_head + tile * a.H * D, tile, n_end, row_bytes, D);
     const uint32_t qoff = (uint32_t)nl * row_bytes + 2 * 8 * kg;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qraw[ks] = buf_load16<kCacheStream>(rq, qoff + 2 * 32 * ks);
+  };
+  auto fetch_g = [&](int64_t tile, uint4 (&grow)[St::kPasses]) {
+    const __amdgpu_buffer_rsrc_t rg = tile_rsrc(g_head + tile * a.H * D, tile, n_end, row_bytes, D);
 #pragma unroll
     for (int i = 0; i < St::kPasses; ++i)
       grow[i] = buf_load16<kCacheStream>(rg, (uint32_t)(i * St::kRowsPerPass + rl) * row_bytes + 2 * rc);
   };
-  // everything after the loads of one tile
-  auto process = [&](int64_t tile, const uint4 (&cq)[KS], const uint4 (&cg)[St::kPasses]) {
-      // An offset the compiler cannot see through (always 0) keeps the
-      // loop-invariant S-part reads inside the loop: hoisting all of them
-      // would need 256 registers per lane.  It is a register-only asm, so it
-      // does not make the compiler drain outstanding memory operations.
-      int opaque = 0;
-      asm volatile("" : "+v"(opaque));
-      const unsigned char *sh = s_sh + opaque, *sl = s_sl + opaque;
-      const int64_t n = tile + nl;
-      const bool valid = n < n_end;
-      int t, h, w;
-      token_pos(a, valid ? n : n_end - 1, t, h, w);
 
-      f32x4 acc[ET], accd = {0.f, 0.f, 0.f, 0.f};
+  // RoPE(ReLU(q)) of one block's k-step ks as bf16 hi + lo B operands, and
+  // ReLU(q) itself (exact in bf16) for the denominator
+  auto q_operands = [&](const uint4 &cq, int ks, int t, int h, int w, bf16x8 &bh, bf16x8 &bl,
+                        bf16x8 &bden) {
+    const uint32_t qw[4] = {relu_bf16x2(cq.x), relu_bf16x2(cq.y), relu_bf16x2(cq.z),
+                            relu_bf16x2(cq.w)};
+    bden = __builtin_bit_cast(bf16x8, make_uint4(qw[0], qw[1], qw[2], qw[3]));
+    float x[8];
 #pragma unroll
-      for (int et = 0; et < ET; ++et) acc[et] = accd;
+    for (int m = 0; m < 4; ++m) {
+      x[2 * m] = lo_bf16(qw[m]);
+      x[2 * m + 1] = hi_bf16(qw[m]);
+    }
+    int axis, pia;
+    pair_axis<D>(16 * ks + 4 * kg, axis, pia);
+    float2 c4[4];
+    ts.read(s_tab, ts.lookup(axis, pia).at(t, h, w), c4);
+    rotate4(x, c4);
+    uint32_t hw4[4], lw4[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) split_bf16x2(x[2 * m], x[2 * m + 1], hw4[m], lw4[m]);
+    bh = __builtin_bit_cast(bf16x8, make_uint4(hw4[0], hw4[1], hw4[2], hw4[3]));
+    bl = __builtin_bit_cast(bf16x8, make_uint4(lw4[0], lw4[1], lw4[2], lw4[3]));
+  };
 
+  // num and den of two 16-token blocks (A, B) that share every S fragment
+  // read: per k-step, each pair of S^T fragments (hi, lo) of an output tile
+  // feeds six products, three per block
+  auto products = [&](int64_t tA, int64_t tB, const uint4 (&cqA)[KS], const uint4 (&cqB)[KS],
+                      f32x4 (&accA)[ET], f32x4 (&accB)[ET], float &denA, float &denB) {
+    // An offset the compiler cannot see through (always 0) keeps the
+    // loop-invariant S-part reads inside the loop: hoisting all of them
+    // would need 256 registers per lane.  It is a register-only asm, so it
+    // does not make the compiler drain outstanding memory operations.
+    int opaque = 0;
+    asm volatile("" : "+v"(opaque));
+    const unsigned char *sh = s_sh + opaque, *sl = s_sl + opaque;
+    int pA[3], pB[3];
+    {
+      const int64_t nA = tA + nl, nB = tB + nl;
+      token_pos(a, nA < n_end ? nA : n_end - 1, pA[0], pA[1], pA[2]);
+      token_pos(a, nB < n_end ? nB : n_end - 1, pB[0], pB[1], pB[2]);
+    }
+    f32x4 adA = {0.f, 0.f, 0.f, 0.f}, adB = adA;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint32_t qw[4] = {relu_bf16x2(cq[ks].x), relu_bf16x2(cq[ks].y),
-                                relu_bf16x2(cq[ks].z), relu_bf16x2(cq[ks].w)};
-        const bf16x8 bden = __builtin_bit_cast(bf16x8, make_uint4(qw[0], qw[1], qw[2], qw[3]));
-        float x[8];
+    for (int et = 0; et < ET; ++et) accA[et] = accB[et] = adA;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          x[2 * m] = lo_bf16(qw[m]);
-          x[2 * m + 1] = hi_bf16(qw[m]);
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 bhA, blA, bdA, bhB, blB, bdB;
+      q_operands(cqA[ks], ks, pA[0], pA[1], pA[2], bhA, blA, bdA);
+      q_operands(cqB[ks], ks, pB[0], pB[1], pB[2], bhB, blB, bdB);
+      adA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s_zf[ks * 64 + lane], bdA, adA, 0, 0, 0);
+      adB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s_zf[ks * 64 + lane], bdB, adB, 0, 0, 0);
+      // A = S^T fragments (rows e = 16*et + l%16, columns p = 32*ks +
+      // 8*(l/16) + j), read transposed from the row-major S parts, two
+      // output tiles at a time; the products are issued so that consecutive
+      // matrix-core instructions do not depend on each other
+#pragma unroll
+      for (int eg = 0; eg < ET; eg += 2) {
+        bf16x8 ah[2], al[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int o0 = rd_s[eg + u] + (32 * ks) * (2 * D);
+          const int o1 = o0 + 4 * (2 * D);
+          const uint2 h0 = lds_read_tr16(sh + o0), h1 = lds_read_tr16(sh + o1);
+          const uint2 l0 = lds_read_tr16(sl + o0), l1 = lds_read_tr16(sl + o1);
+          ah[u] = __builtin_bit_cast(bf16x8, make_uint4(h0.x, h0.y, h1.x, h1.y));
+          al[u] = __builtin_bit_cast(bf16x8, make_uint4(l0.x, l0.y, l1.x, l1.y));
         }
-        int axis, pia;
-        pair_axis<D>(16 * ks + 4 * kg, axis, pia);
-        float2 c4[4];
-        ts.read(s_tab, ts.lookup(axis, pia).at(t, h, w), c4);
-        rotate4(x, c4);
-        uint32_t hw4[4], lw4[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) split_bf16x2(x[2 * m], x[2 * m + 1], hw4[m], lw4[m]);
-        const bf16x8 bh = __builtin_bit_cast(bf16x8, make_uint4(hw4[0], hw4[1], hw4[2], hw4[3]));
-        const bf16x8 bl = __builtin_bit_cast(bf16x8, make_uint4(lw4[0], lw4[1], lw4[2], lw4[3]));
-        accd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s_zf[ks * 64 + lane], bden, accd, 0, 0, 0);
-        // A = S^T fragments (rows e = 16*et + l%16, columns p = 32*ks +
-        // 8*(l/16) + j), read transposed from the row-major S parts, four
-        // output tiles at a time; the three products of a tile are issued
-        // round-robin over the four tiles so that consecutive matrix-core
-        // instructions do not depend on each other
+        for (int u = 0; u < 2; ++u) {
+          accA[eg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[u], blA, accA[eg + u], 0, 0, 0);
+          accB[eg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[u], blB, accB[eg + u], 0, 0, 0);
+        }
 #pragma unroll
-        for (int eg = 0; eg < ET; eg += 4) {
-          bf16x8 ah[4], al[4];
+        for (int u = 0; u < 2; ++u) {
+          accA[eg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[u], bhA, accA[eg + u], 0, 0, 0);
+          accB[eg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[u], bhB, accB[eg + u], 0, 0, 0);
+        }
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int o0 = rd_s[eg + u] + (32 * ks) * (2 * D);
-            const int o1 = o0 + 4 * (2 * D);
-            const uint2 h0 = lds_read_tr16(sh + o0), h1 = lds_read_tr16(sh + o1);
-            const uint2 l0 = lds_read_tr16(sl + o0), l1 = lds_read_tr16(sl + o1);
-            ah[u] = __builtin_bit_cast(bf16x8, make_uint4(h0.x, h0.y, h1.x, h1.y));
-            al[u] = __builtin_bit_cast(bf16x8, make_uint4(l0.x, l0.y, l1.x, l1.y));
-          }
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            acc[eg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[u], bl, acc[eg + u], 0, 0, 0);
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            acc[eg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[u], bh, acc[eg + u], 0, 0, 0);
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            acc[eg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[u], bh, acc[eg + u], 0, 0, 0);
+        for (int u = 0; u < 2; ++u) {
+          accA[eg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[u], bhA, accA[eg + u], 0, 0, 0);
+          accB[eg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[u], bhB, accB[eg + u], 0, 0, 0);
         }
       }
+    }
+    denA = adA[0] + adA[1] + a.eps;
+    denB = adB[0] + adB[1] + a.eps;
+  };
 
-      const float den = accd[0] + accd[1] + a.eps;
+  // the gate, the divide and the store of one 16-token block
+  auto finish = [&](int64_t tile, const f32x4 (&acc)[ET], float den,
+                    const uint4 (&cg)[St::kPasses]) {
       unsigned char *stage = s_stage + wave * St::kBytes;
 #pragma unroll
       for (int i = 0; i < St::kPasses; ++i)
@@ -272,31 +298,45 @@ __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
         const uint4 ov = *reinterpret_cast<const uint4 *>(stage + tok * St::kRowBytes + 2 * rc);
         buf_store16<kCacheStream>(ro, (uint32_t)tok * row_bytes + 2 * rc, ov);
       }
-      // the next tile's first staging writes must not overtake these reads
+      // the next block's first staging writes must not overtake these reads
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  // Items slot, slot + m, ... of this super-range; the wave's tile of item
-  // i starts at token n_begin + i kItem + 16 wave.  Two tiles of loads stay in
-  // flight per wave: buffer A holds tile i while B receives tile i + 1; once
-  // tile i is done, A is refilled with tile i + 2 before tile i + 1 (in B) is
-  // processed, and so on.  The refills are unconditional (tiles past the
-  // range read as zeros and are never processed): with a branch around them
-  // the compiler cannot tell which loads are still outstanding at the top of
-  // the loop and waits for all of them, which leaves one tile in flight.
+  // The workgroup takes the items slot, slot + m, ... of its super-range; a
+  // wave takes the 16-token block 16 wave of two consecutive ones (A, B) at
+  // a time.  q of the next pair is in flight during the current pair's
+  // products and gate; g of a block is refilled right after its gate and
+  // arrives during the next pair's products.  Refills are unconditional
+  // (blocks past the range read as zeros and their stores are dropped):
+  // with a branch around them the compiler waits for every outstanding load
+  // at the join.
   const int64_t kStep = kItem * a.am;
-  uint4 qa[KS], ga[St::kPasses], qb[KS], gb[St::kPasses];
+  uint4 q0[KS], q1[KS], q2[KS], q3[KS], gA[St::kPasses], gB[St::kPasses];
   int64_t tile = n_begin + slot * kItem + 16 * wave;
-  fetch(tile, qa, ga);
-  asm volatile("" ::: "memory");  // the first tile's loads are issued first
-  fetch(tile + kStep, qb, gb);
+  fetch_q(tile, q0);
+  fetch_q(tile + kStep, q1);
+  fetch_g(tile, gA);
+  fetch_g(tile + kStep, gB);
+  asm volatile("" ::: "memory");  // the first pair's loads are issued first
+  auto pair = [&](int64_t t0, const uint4 (&qa)[KS], const uint4 (&qb)[KS], uint4 (&na)[KS],
+                  uint4 (&nb)[KS]) {
+    fetch_q(t0 + 2 * kStep, na);
+    fetch_q(t0 + 3 * kStep, nb);
+    f32x4 accA[ET], accB[ET];
+    float denA, denB;
+    products(t0, t0 + kStep, qa, qb, accA, accB, denA, denB);
+    finish(t0, accA, denA, gA);
+    fetch_g(t0 + 2 * kStep, gA);
+    finish(t0 + kStep, accB, denB, gB);
+    fetch_g(t0 + 3 * kStep, gB);
+  };
   while (tile < n_end) {
-    process(tile, qa, ga);
-    fetch(tile + 2 * kStep, qa, ga);
-    if (tile + kStep < n_end) process(tile + kStep, qb, gb);
-    fetch(tile + 3 * kStep, qb, gb);
+    pair(tile, q0, q1, q2, q3);
+    tile += 2 * kStep;
+    if (tile >= n_end) break;
+    pair(tile, q2, q3, q0, q1);
     tile += 2 * kStep;
   }
   __builtin_amdgcn_s_waitcnt(0);  // prefetches past the range are still in flight
