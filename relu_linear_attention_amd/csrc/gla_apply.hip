@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "gla_mfma_common.h"
 
@@ -46,7 +47,9 @@ constexpr int64_t kItem = 16 * (kApplyThreads / 64);  // tokens of an item: a ti
 // gate: y = num/den is scaled by 1/sqrt(mean over the D features of y^2 +
 // rms_eps) and by the weight w [D].  A token's D values are spread over the
 // four lanes l % 16 == token (32 each), summed with two lane exchanges.
-template <int D, bool kNorm>
+//
+// kPair: a wave takes two 16-token blocks at a time (below); otherwise one.
+template <int D, bool kNorm, bool kPair>
 __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ g,
     const float *__restrict__ states, const uint16_t *__restrict__ frags,
@@ -168,9 +171,11 @@ __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
 
   // num and den of two 16-token blocks (A, B) that share every S fragment
   // read: per k-step, each pair of S^T fragments (hi, lo) of an output tile
-  // feeds six products, three per block
-  auto products = [&](int64_t tA, int64_t tB, const uint4 (&cqA)[KS], const uint4 (&cqB)[KS],
-                      f32x4 (&accA)[ET], f32x4 (&accB)[ET], float &denA, float &denB) {
+  // feeds six products, three per block (nb2 false: block A alone)
+  auto products = [&](auto nb2, int64_t tA, int64_t tB, const uint4 (&cqA)[KS],
+                      const uint4 (&cqB)[KS], f32x4 (&accA)[ET], f32x4 (&accB)[ET], float &denA,
+                      float &denB) {
+    constexpr bool kTwo = decltype(nb2)::value;
     // An offset the compiler cannot see through (always 0) keeps the
     // loop-invariant S-part reads inside the loop: hoisting all of them
     // would need 256 registers per lane.  It is a register-only asm, so it
@@ -182,7 +187,7 @@ __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
     {
       const int64_t nA = tA + nl, nB = tB + nl;
       token_pos(a, nA < n_end ? nA : n_end - 1, pA[0], pA[1], pA[2]);
-      token_pos(a, nB < n_end ? nB : n_end - 1, pB[0], pB[1], pB[2]);
+      if (kTwo) token_pos(a, nB < n_end ? nB : n_end - 1, pB[0], pB[1], pB[2]);
     }
     f32x4 adA = {0.f, 0.f, 0.f, 0.f}, adB = adA;
 #pragma unroll
@@ -191,9 +196,9 @@ __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
     for (int ks = 0; ks < KS; ++ks) {
       bf16x8 bhA, blA, bdA, bhB, blB, bdB;
       q_operands(cqA[ks], ks, pA[0], pA[1], pA[2], bhA, blA, bdA);
-      q_operands(cqB[ks], ks, pB[0], pB[1], pB[2], bhB, blB, bdB);
+      if (kTwo) q_operands(cqB[ks], ks, pB[0], pB[1], pB[2], bhB, blB, bdB);
       adA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s_zf[ks * 64 + lane], bdA, adA, 0, 0, 0);
-      adB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s_zf[ks * 64 + lane], bdB, adB, 0, 0, 0);
+      if (kTwo) adB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s_zf[ks * 64 + lane], bdB, adB, 0, 0, 0);
       // A = S^T fragments (rows e = 16*et + l%16, columns p = 32*ks +
       // 8*(l/16) + j), read transposed from the row-major S parts, two
       // output tiles at a time; the products are issued so that consecutive
@@ -213,22 +218,25 @@ __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           accA[eg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[u], blA, accA[eg + u], 0, 0, 0);
-          accB[eg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[u], blB, accB[eg + u], 0, 0, 0);
+          if (kTwo)
+            accB[eg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[u], blB, accB[eg + u], 0, 0, 0);
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           accA[eg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[u], bhA, accA[eg + u], 0, 0, 0);
-          accB[eg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[u], bhB, accB[eg + u], 0, 0, 0);
+          if (kTwo)
+            accB[eg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[u], bhB, accB[eg + u], 0, 0, 0);
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           accA[eg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[u], bhA, accA[eg + u], 0, 0, 0);
-          accB[eg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[u], bhB, accB[eg + u], 0, 0, 0);
+          if (kTwo)
+            accB[eg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[u], bhB, accB[eg + u], 0, 0, 0);
         }
       }
     }
     denA = adA[0] + adA[1] + a.eps;
-    denB = adB[0] + adB[1] + a.eps;
+    denB = kTwo ? adB[0] + adB[1] + a.eps : 0.f;
   };
 
   // the gate, the divide and the store of one 16-token block
@@ -304,50 +312,80 @@ __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  // The workgroup takes the items slot, slot + m, ... of its super-range; a
-  // wave takes the 16-token block 16 wave of two consecutive ones (A, B) at
-  // a time.  q of the next pair is in flight during the current pair's
-  // products and gate; g of a block is refilled right after its gate and
-  // arrives during the next pair's products.  Refills are unconditional
-  // (blocks past the range read as zeros and their stores are dropped):
-  // with a branch around them the compiler waits for every outstanding load
-  // at the join.
   const int64_t kStep = kItem * a.am;
-  uint4 q0[KS], q1[KS], q2[KS], q3[KS], gA[St::kPasses], gB[St::kPasses];
   int64_t tile = n_begin + slot * kItem + 16 * wave;
-  fetch_q(tile, q0);
-  fetch_q(tile + kStep, q1);
-  fetch_g(tile, gA);
-  fetch_g(tile + kStep, gB);
-  asm volatile("" ::: "memory");  // the first pair's loads are issued first
-  auto pair = [&](int64_t t0, const uint4 (&qa)[KS], const uint4 (&qb)[KS], uint4 (&na)[KS],
-                  uint4 (&nb)[KS]) {
-    fetch_q(t0 + 2 * kStep, na);
-    fetch_q(t0 + 3 * kStep, nb);
-    f32x4 accA[ET], accB[ET];
-    float denA, denB;
-    products(t0, t0 + kStep, qa, qb, accA, accB, denA, denB);
-    finish(t0, accA, denA, gA);
-    fetch_g(t0 + 2 * kStep, gA);
-    finish(t0 + kStep, accB, denB, gB);
-    fetch_g(t0 + 3 * kStep, gB);
-  };
-  while (tile < n_end) {
-    pair(tile, q0, q1, q2, q3);
-    tile += 2 * kStep;
-    if (tile >= n_end) break;
-    pair(tile, q2, q3, q0, q1);
-    tile += 2 * kStep;
+  if constexpr (kPair) {
+    // The workgroup takes the items slot, slot + m, ... of its super-range; a
+    // wave takes the 16-token block 16 wave of two consecutive ones (A, B) at
+    // a time.  q of the next pair is in flight during the current pair's
+    // products and gates; g of a block is refilled right after its gate and
+    // arrives during the next pair's products.  Refills are unconditional
+    // (blocks past the range read as zeros and their stores are dropped):
+    // with a branch around them the compiler waits for every outstanding
+    // load at the join.  With an odd item count the last pair's second block
+    // lies past the range; the plan takes pairs only where that block is
+    // off the critical path or a small share of it.
+    uint4 q0[KS], q1[KS], q2[KS], q3[KS], gA[St::kPasses], gB[St::kPasses];
+    fetch_q(tile, q0);
+    fetch_q(tile + kStep, q1);
+    fetch_g(tile, gA);
+    fetch_g(tile + kStep, gB);
+    asm volatile("" ::: "memory");  // the first pair's loads are issued first
+    auto pair = [&](int64_t t0, const uint4 (&qa)[KS], const uint4 (&qb)[KS], uint4 (&na)[KS],
+                    uint4 (&nb)[KS]) {
+      fetch_q(t0 + 2 * kStep, na);
+      fetch_q(t0 + 3 * kStep, nb);
+      f32x4 accA[ET], accB[ET];
+      float denA, denB;
+      products(std::true_type{}, t0, t0 + kStep, qa, qb, accA, accB, denA, denB);
+      finish(t0, accA, denA, gA);
+      fetch_g(t0 + 2 * kStep, gA);
+      finish(t0 + kStep, accB, denB, gB);
+      fetch_g(t0 + 3 * kStep, gB);
+    };
+    while (tile < n_end) {
+      pair(tile, q0, q1, q2, q3);
+      tile += 2 * kStep;
+      if (tile >= n_end) break;
+      pair(tile, q2, q3, q0, q1);
+      tile += 2 * kStep;
+    }
+  } else {
+    // One block at a time, two in flight: buffer A holds block i while B
+    // receives block i + 1; once block i is done, A is refilled with block
+    // i + 2 before block i + 1 (in B) is processed, and so on (refills
+    // unconditional, as above).
+    uint4 qa[KS], ga[St::kPasses], qb[KS], gb[St::kPasses];
+    auto single = [&](int64_t t0, const uint4 (&cq)[KS], const uint4 (&cg)[St::kPasses]) {
+      f32x4 acc[ET], unused[ET];
+      float den, unused_den;
+      products(std::false_type{}, t0, t0, cq, cq, acc, unused, den, unused_den);
+      finish(t0, acc, den, cg);
+    };
+    fetch_q(tile, qa);
+    fetch_g(tile, ga);
+    asm volatile("" ::: "memory");  // the first block's loads are issued first
+    fetch_q(tile + kStep, qb);
+    fetch_g(tile + kStep, gb);
+    while (tile < n_end) {
+      single(tile, qa, ga);
+      fetch_q(tile + 2 * kStep, qa);
+      fetch_g(tile + 2 * kStep, ga);
+      if (tile + kStep < n_end) single(tile + kStep, qb, gb);
+      fetch_q(tile + 3 * kStep, qb);
+      fetch_g(tile + 3 * kStep, gb);
+      tile += 2 * kStep;
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);  // prefetches past the range are still in flight
 }
 
-template <int D, bool kNorm>
+template <int D, bool kNorm, bool kPair>
 hipError_t apply_mfma_d(const Plan &p, const void *q, const void *g, const float *states,
                        const uint16_t *frags, const float2 *tab, const void *rms_w, void *out,
                        hipStream_t stream) {
   const size_t lds = apply_mfma_lds_bytes(p);
-  auto kern = apply_mfma_kernel<D, kNorm>;
+  auto kern = apply_mfma_kernel<D, kNorm, kPair>;
   const hipError_t attr = lds_limit_once((const void *)kern);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(kern, dim3((unsigned)(p.ag * p.ar * p.am)), dim3(kApplyThreads), lds,
@@ -371,21 +409,31 @@ size_t apply_mfma_lds_bytes(const Plan &p) {
 int64_t apply_mfma_item_tokens() { return kItem; }
 
 hipError_t apply_mfma_lds_limits() {
-  return lds_limits({(const void *)apply_mfma_kernel<128, false>,
-                     (const void *)apply_mfma_kernel<128, true>,
-                     (const void *)apply_mfma_kernel<64, false>,
-                     (const void *)apply_mfma_kernel<64, true>});
+  return lds_limits({(const void *)apply_mfma_kernel<128, false, false>,
+                     (const void *)apply_mfma_kernel<128, true, false>,
+                     (const void *)apply_mfma_kernel<64, false, false>,
+                     (const void *)apply_mfma_kernel<64, true, false>,
+                     (const void *)apply_mfma_kernel<128, false, true>,
+                     (const void *)apply_mfma_kernel<128, true, true>,
+                     (const void *)apply_mfma_kernel<64, false, true>,
+                     (const void *)apply_mfma_kernel<64, true, true>});
 }
 
 hipError_t launch_apply_mfma(const Plan &p, const void *q, const void *g, const float *states,
                             const uint16_t *frags, const float2 *tab, const void *rms_w,
                             void *out, hipStream_t stream) {
-  if (p.d == 128)
-    return rms_w ? apply_mfma_d<128, true>(p, q, g, states, frags, tab, rms_w, out, stream)
-                 : apply_mfma_d<128, false>(p, q, g, states, frags, tab, rms_w, out, stream);
-  if (p.d == 64)
-    return rms_w ? apply_mfma_d<64, true>(p, q, g, states, frags, tab, rms_w, out, stream)
-                 : apply_mfma_d<64, false>(p, q, g, states, frags, tab, rms_w, out, stream);
+#define GLA_APPLY_CASE(DD, NORM)                                                                \
+  return p.apair ? apply_mfma_d<DD, NORM, true>(p, q, g, states, frags, tab, rms_w, out, stream)  \
+                 : apply_mfma_d<DD, NORM, false>(p, q, g, states, frags, tab, rms_w, out, stream);
+  if (p.d == 128) {
+    if (rms_w) GLA_APPLY_CASE(128, true)
+    GLA_APPLY_CASE(128, false)
+  }
+  if (p.d == 64) {
+    if (rms_w) GLA_APPLY_CASE(64, true)
+    GLA_APPLY_CASE(64, false)
+  }
+#undef GLA_APPLY_CASE
   return hipErrorInvalidValue;
 }
 

@@ -35,6 +35,7 @@ struct Plan {
   // air items of 128 tokens, am workgroups per super-range taking its items
   // in turn
   int64_t hpw, ag, ar, air, am;
+  bool apair;     // output stage: two 16-token blocks per wave at a time
   bool bf16;      // element type of q, k, v, g, out
   bool mfma;      // matrix-core kernels (bf16, d = 64 or 128)
   float theta, eps;
