@@ -30,14 +30,16 @@ constexpr int kTokThreads = 512;  // 8 waves, a 16-token tile each
 
 // One workgroup (8 waves) per (unit, token range).  LDS: S hi and lo parts
 // (row-major [p][e], SRow layout), the z fragments of the denominator
-// product (as in the output stage), z in fp32, and the RoPE table slice of
-// the range.  Per 16-token tile a wave
+// product (as in the output stage), z in fp32, a staging tile per wave, and
+// the RoPE table slice of the range.  Per 16-token tile a wave
 //   1. loads q in the B-operand layout of v_mfma_f32_16x16x32_bf16 (lane l:
-//      token l % 16, features 32 ks + 8 (l / 16) + 0..7) and g, dout in the
+//      token l % 16, features 32 ks + 8 (l / 16) + 0..7), and g and dout as
+//      whole rows, which pass through a per-wave staging tile into the
 //      accumulator layout (features 16 et + 4 (l / 16) + 0..3);
 //   2. forms x = RoPE(ReLU(q)) hi + lo and num = x S (3 products per tile of
 //      S^T fragments), den = ReLU(q) . z + eps on the matrix cores;
-//   3. computes y, s, dg (stored), dnum (split into hi + lo) and the sum
+//   3. computes y, s, dg (stored as whole rows through the staging tile),
+//      dnum (split into hi + lo) and the sum
 //      dout s . y over the token's features (its four lanes);
 //   4. moves dnum into the B-operand layout with two in-register lane swaps
 //      per register (lane (token, kg) then holds features 32 ks + 8 kg +
@@ -61,7 +63,9 @@ __global__ __launch_bounds__(kTokThreads) void bwd_token_mfma_kernel(
   unsigned char *s_sl = lds + D * D * 2;  // S lo
   bf16x8 *s_zf = reinterpret_cast<bf16x8 *>(lds + D * D * 4);  // KS fragments x 64 lanes
   float *s_z = reinterpret_cast<float *>(s_zf + KS * 64);       // z (D)
-  float2 *s_tab = reinterpret_cast<float2 *>(s_z + D);
+  using St = Stage<D>;
+  unsigned char *s_stage = reinterpret_cast<unsigned char *>(s_z + D);  // NW staging tiles
+  float2 *s_tab = reinterpret_cast<float2 *>(s_stage + NW * St::kBytes);
 
   const int64_t wg = blockIdx.x;
   const int64_t unit = wg / a.R, r = wg % a.R;
@@ -129,23 +133,50 @@ __global__ __launch_bounds__(kTokThreads) void bwd_token_mfma_kernel(
   uint16_t *dq_head = dq + head0, *dg_head = dg + head0;
   float2 *dd_head = dd + bh * a.N;
 
-  auto fetch = [&](int64_t tile, uint4 (&qr)[KS], uint2 (&gr)[ET], uint2 (&dr)[ET]) {
+  // row-wise lane mapping of the staging tile: in pass i lane l covers token
+  // i*kRowsPerPass + l/kLanesPerRow, features 8*(l%kLanesPerRow)..+7
+  const int rl = lane / St::kLanesPerRow, rc = 8 * (lane % St::kLanesPerRow);
+  // loads of one tile: q in the B-operand layout, g and dout as whole rows
+  // (they pass through the staging tile into the accumulator layout)
+  auto fetch = [&](int64_t tile, uint4 (&qr)[KS], uint4 (&gr)[St::kPasses],
+                   uint4 (&dr)[St::kPasses]) {
     const __amdgpu_buffer_rsrc_t rq = tile_rsrc(q_head + tile * a.H * D, tile, n_end, row_bytes, D);
     const __amdgpu_buffer_rsrc_t rg = tile_rsrc(g_head + tile * a.H * D, tile, n_end, row_bytes, D);
     const __amdgpu_buffer_rsrc_t rd = tile_rsrc(d_head + tile * a.H * D, tile, n_end, row_bytes, D);
     const uint32_t qoff = (uint32_t)nl * row_bytes + 16 * kg;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qr[ks] = buf_load16<kCacheNormal>(rq, qoff + 64 * ks);
-    const uint32_t coff = (uint32_t)nl * row_bytes + 8 * kg;
 #pragma unroll
-    for (int et = 0; et < ET; ++et) {
-      gr[et] = buf_load8(rg, coff + 32 * et);
-      dr[et] = buf_load8(rd, coff + 32 * et);
+    for (int i = 0; i < St::kPasses; ++i) {
+      const uint32_t o = (uint32_t)(i * St::kRowsPerPass + rl) * row_bytes + 2 * rc;
+      gr[i] = buf_load16<kCacheNormal>(rg, o);
+      dr[i] = buf_load16<kCacheNormal>(rd, o);
     }
   };
+  // a tile's rows (in row-wise registers) into the staging tile and back in
+  // the accumulator layout: value et holds features 16 et + 4 kg + 0..3 of
+  // token nl
+  unsigned char *stage = s_stage + wave * St::kBytes;
+  auto staged = [&](const uint4 (&rows)[St::kPasses], uint2 (&acc_layout)[ET]) {
+#pragma unroll
+    for (int i = 0; i < St::kPasses; ++i)
+      *reinterpret_cast<uint4 *>(stage + (i * St::kRowsPerPass + rl) * St::kRowBytes + 2 * rc) =
+          rows[i];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int et = 0; et < ET; ++et)
+      acc_layout[et] =
+          *reinterpret_cast<const uint2 *>(stage + nl * St::kRowBytes + 2 * (16 * et + 4 * kg));
+    // the next writes into the tile must not overtake these reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
 
-  auto process = [&](int64_t tile, const uint4 (&cq)[KS], const uint2 (&cg)[ET],
-                     const uint2 (&cd)[ET]) {
+  auto process = [&](int64_t tile, const uint4 (&cq)[KS], const uint4 (&gr)[St::kPasses],
+                     const uint4 (&dr)[St::kPasses]) {
     // (an offset the compiler cannot see through keeps the loop-invariant
     // S reads inside the loop, as in the output stage)
     int opaque = 0;
@@ -216,7 +247,9 @@ __global__ __launch_bounds__(kTokThreads) void bwd_token_mfma_kernel(
     const float den = accd[0] + accd[1] + a.eps;
     const float inv_den = __builtin_amdgcn_rcpf(den);
     const __amdgpu_buffer_rsrc_t rdg = tile_rsrc(dg_head + tile * a.H * D, tile, n_end, row_bytes, D);
-    const uint32_t coff = (uint32_t)nl * row_bytes + 8 * kg;
+    uint2 cg[ET], cd[ET], dgw[ET];
+    staged(gr, cg);
+    staged(dr, cd);
     // dnum hi / lo, packed pairs: X from tile 2 ks (features 32 ks + 4 kg +
     // 0..3), Y from tile 2 ks + 1 (32 ks + 16 + 4 kg + 0..3)
     uint32_t xh[KS][2], yh[KS][2], xl[KS][2], yl[KS][2];
@@ -227,19 +260,19 @@ __global__ __launch_bounds__(kTokThreads) void bwd_token_mfma_kernel(
                            hi_bf16(cg[et].y)};
       const float dv[4] = {lo_bf16(cd[et].x), hi_bf16(cd[et].x), lo_bf16(cd[et].y),
                            hi_bf16(cd[et].y)};
+      // with s' = s / den: dnum = dout s', dout s . y = dnum num, and
+      // dg = dout y s (1 - s) = (dnum num)(e s), since 1 - s = e s
       float dgo[4], dn[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float y = acc[et][i] * inv_den;
         const float e = __expf(-gv[i]);
         const float sg = __builtin_amdgcn_rcpf(1.f + e);
-        const float dy = dv[i] * sg;
-        dgo[i] = dy * y * (e * sg);  // 1 - s = e s
-        dn[i] = dy * inv_den;
-        dyy = __builtin_fmaf(dy, y, dyy);
+        dn[i] = dv[i] * (sg * inv_den);
+        const float t = dn[i] * acc[et][i];
+        dyy += t;
+        dgo[i] = t * (e * sg);
       }
-      buf_store8(rdg, coff + 32 * et,
-                 make_uint2(pack_bf16x2(dgo[0], dgo[1]), pack_bf16x2(dgo[2], dgo[3])));
+      dgw[et] = make_uint2(pack_bf16x2(dgo[0], dgo[1]), pack_bf16x2(dgo[2], dgo[3]));
       const int ks = et >> 1;
       if (et & 1) {
         split_bf16x2(dn[0], dn[1], yh[ks][0], yl[ks][0]);
@@ -249,6 +282,7 @@ __global__ __launch_bounds__(kTokThreads) void bwd_token_mfma_kernel(
         split_bf16x2(dn[2], dn[3], xh[ks][1], xl[ks][1]);
       }
     }
+    store_tile_rows<D>(stage, dgw, rdg, 0, row_bytes);
     // Transpose across the token's four lanes (rows of 16 lanes, row = kg):
     // row r needs X of rows 2r, 2r + 1 (r < 2) or Y of rows 2r - 4, 2r - 3.
     // A 32-lane swap of (X, Y) gives X' = (X0, X1, Y0, Y1), Y' = (X2, X3, Y2,
@@ -338,7 +372,7 @@ __global__ __launch_bounds__(kTokThreads) void bwd_token_mfma_kernel(
   // zeros and are never processed).
   const int64_t kStep = 16 * NW;
   uint4 qa[KS], qb[KS];
-  uint2 ga[ET], da[ET], gb[ET], db[ET];
+  uint4 ga[St::kPasses], da[St::kPasses], gb[St::kPasses], db[St::kPasses];
   int64_t tile = n_begin + 16 * wave;
   fetch(tile, qa, ga, da);
   asm volatile("" ::: "memory");
@@ -638,6 +672,7 @@ __global__ __launch_bounds__(kDsThreads<D>, 3) void bwd_dstate_mfma_kernel(
 template <int D>
 size_t token_lds(const Plan &p) {
   return (size_t)D * D * 4 + (size_t)(D / 32) * 64 * 16 + (size_t)D * 4 +
+         (size_t)(kTokThreads / 64) * Stage<D>::kBytes +
          (size_t)tab_slice_entries(p, p.Lr) * sizeof(float2);
 }
 template <int D>

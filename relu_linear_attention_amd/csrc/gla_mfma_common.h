@@ -131,12 +131,13 @@ __device__ __forceinline__ uint32_t relu_bf16x2(uint32_t x) {
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(v, zero));
 }
 
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-// 0xffff in each 16-bit half of x that is nonzero, else 0: for a packed
-// ReLU(x) pair, the mask of the elements with x > 0
+// 0xffff in each 16-bit half of x that is nonzero, else 0, for x a packed
+// pair of ReLU results (each half in 0..0x7f80): the mask of the elements
+// with x > 0.  A nonzero half h has -h in 0x8080..0xffff, so the arithmetic
+// shift of -h by 15 gives 0xffff, and 0 gives 0 (two packed 16-bit ops).
 __device__ __forceinline__ uint32_t nonzero_mask16(uint32_t x) {
-  const u16x2 nz = __builtin_elementwise_min(__builtin_bit_cast(u16x2, x), u16x2{1, 1});
-  return __builtin_bit_cast(uint32_t, u16x2{0, 0} - nz);
+  const s16x2 neg = s16x2{0, 0} - __builtin_bit_cast(s16x2, x);
+  return __builtin_bit_cast(uint32_t, neg >> s16x2{15, 15});
 }
 
 __device__ __forceinline__ float lo_bf16(uint32_t x) { return __uint_as_float(x << 16); }
