@@ -83,16 +83,40 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_kernel(
   const __amdgpu_buffer_rsrc_t rdk = head_rows_rsrc(dk + first, range_bytes);
   const __amdgpu_buffer_rsrc_t rdv = head_rows_rsrc(dv + first, range_bytes);
 
-  auto fetch = [&](int64_t tile, uint4 (&kb)[KS], uint4 (&vb)[KS]) {
-    const uint32_t off = ((uint32_t)(tile - n_begin) + nl) * row_bytes + 16 * kg;
+  using St = Stage<D>;
+  // k and v come in as whole rows (pass i, lane l: token i*kRowsPerPass +
+  // l/kLanesPerRow, features 8*(l%kLanesPerRow)..+7) and reach the operand
+  // layout (token nl, features 32*ks + 8*kg..+7) through the staging tile;
+  // dk leaves the same way
+  const int rl = lane / St::kLanesPerRow, rc = 8 * (lane % St::kLanesPerRow);
+  auto fetch = [&](int64_t tile, uint4 (&kr)[St::kPasses], uint4 (&vr)[St::kPasses]) {
+    const uint32_t base = (uint32_t)(tile - n_begin) * row_bytes + 2 * rc;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      kb[ks] = buf_load16<kCacheNormal>(rk, off + 64 * ks);
-      vb[ks] = buf_load16<kCacheNormal>(rv, off + 64 * ks);
+    for (int i = 0; i < St::kPasses; ++i) {
+      const uint32_t off = base + (uint32_t)(i * St::kRowsPerPass + rl) * row_bytes;
+      kr[i] = buf_load16<kCacheNormal>(rk, off);
+      vr[i] = buf_load16<kCacheNormal>(rv, off);
     }
   };
+  auto wave_sync = []() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  // rows -> staging tile -> operand layout (the tile is free again on return)
+  auto to_operand = [&](unsigned char *stage, const uint4 (&rows)[St::kPasses], uint4 (&ops)[KS]) {
+#pragma unroll
+    for (int i = 0; i < St::kPasses; ++i)
+      *reinterpret_cast<uint4 *>(stage + (i * St::kRowsPerPass + rl) * St::kRowBytes + 2 * rc) =
+          rows[i];
+    wave_sync();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      ops[ks] = *reinterpret_cast<const uint4 *>(stage + nl * St::kRowBytes + 2 * (32 * ks + 8 * kg));
+    wave_sync();
+  };
 
-  auto process = [&](int64_t tile, const uint4 (&kb)[KS], const uint4 (&vb)[KS]) {
+  auto process = [&](int64_t tile, const uint4 (&kr)[St::kPasses], const uint4 (&vr)[St::kPasses]) {
     // loop-invariant LDS offsets kept inside the loop (as in the apply stage)
     int opaque = 0;
     asm volatile("" : "+v"(opaque));
@@ -102,6 +126,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_kernel(
     token_pos(a, n < n_end ? n : n_end - 1, t, h, w);
     const uint32_t row0 = (uint32_t)(tile - n_begin) * row_bytes;
     unsigned char *stage = s_stage + wave * Stage<D>::kBytes;
+    uint4 kb[KS];
+    to_operand(stage, kr, kb);
     uint32_t kw[KS][4];  // ReLU(k), packed bf16, in the B-operand layout
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -171,6 +197,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_kernel(
     // nl % 4, so that lane (token, kg) receives features 32 ks' + 8 kg + 0..7,
     // the features it loaded of k (the mask and the pairs stay in the lane)
     {
+      uint4 vb[KS];
+      to_operand(stage, vr, vb);
       f32x4 acc[ET];
 #pragma unroll
       for (int pt = 0; pt < ET; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -188,7 +216,6 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_kernel(
         }
       }
       mfma_drain();
-      const uint32_t koff = row0 + (uint32_t)nl * row_bytes + 16 * kg;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         int axis, pia;
@@ -198,15 +225,24 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_kernel(
         const float4 z0 = *reinterpret_cast<const float4 *>(s_gz + 32 * ks + 8 * kg);
         const float4 z1 = *reinterpret_cast<const float4 *>(s_gz + 32 * ks + 8 * kg + 4);
         const float gz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
-        buf_store16<kCacheNormal>(rdk, koff + 64 * ks,
-                                  rope_t_add_mask(acc[2 * ks], acc[2 * ks + 1], c4, gz, kw[ks]));
+        *reinterpret_cast<uint4 *>(stage + nl * St::kRowBytes + 2 * (32 * ks + 8 * kg)) =
+            rope_t_add_mask(acc[2 * ks], acc[2 * ks + 1], c4, gz, kw[ks]);
       }
+      wave_sync();
+#pragma unroll
+      for (int i = 0; i < St::kPasses; ++i) {
+        const int tok = i * St::kRowsPerPass + rl;
+        buf_store16<kCacheNormal>(
+            rdk, row0 + (uint32_t)tok * row_bytes + 2 * rc,
+            *reinterpret_cast<const uint4 *>(stage + tok * St::kRowBytes + 2 * rc));
+      }
+      wave_sync();
     }
   };
 
   // two tiles of loads in flight per wave (as in the apply stage)
   constexpr int64_t kStep = 16 * NW;
-  uint4 ka[KS], va[KS], kb2[KS], vb2[KS];
+  uint4 ka[St::kPasses], va[St::kPasses], kb2[St::kPasses], vb2[St::kPasses];
   int64_t tile = n_begin + 16 * wave;
   fetch(tile, ka, va);
   asm volatile("" ::: "memory");  // the first tile's loads are issued first
