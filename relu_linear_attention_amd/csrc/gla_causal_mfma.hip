@@ -24,7 +24,9 @@
 //              phi(q) and RoPE(phi(q)) hi, lo in registers.
 //   outputs    wave w: query tile qt(w), output features of half eh(w):
 //              den, the intra-step scores against key tiles 0..qt (masked
-//              on the diagonal tile), num, the gate and the store.
+//              on the diagonal tile) and num; after a barrier, the gate and
+//              the store as whole half rows through the wave's piece of the
+//              phi(k) tile.
 //   state      S^T += v^T RoPE(phi(k)) (32x32 tiles, two per wave at
 //              d = 128), published as bf16 hi + lo; z += the step's sums.
 
@@ -157,8 +159,19 @@ __global__ __launch_bounds__(kCausalThreads) void causal_mfma_kernel(
   pair_axis<D>(4 * fc, axis, pia);
   const typename TabSlice<D>::Lookup tl = ts.lookup(axis, pia);
 
+  // The gate comes in, and the output leaves, as whole half rows (the D/2
+  // features of half eh of the wave's 16 tokens): pass i, lane l covers
+  // token 16 qt + i*HRP + l/HU, 16-byte unit l%HU of the half row.  They
+  // reach the accumulator layout through the wave's piece of the phi(k) tile
+  // (free from the end of a step's outputs to the next step's prologue), 16
+  // half rows of D bytes whose 16-byte units are XOR-permuted by hswz(row):
+  // the 32 lanes of an 8-byte fragment access then fall on distinct banks.
+  constexpr int HU = D / 16;      // 16-byte units of a half row
+  constexpr int HRP = 64 / HU;    // half rows per pass
+  constexpr int HP = 16 / HRP;    // passes
+  auto hswz = [](int row) { return (row / (256 / D)) & (HU - 1); };
   uint4 kr[RP], vr[RP], qraw[KS];
-  uint2 graw[ETW];
+  uint4 grow[HP];
   auto load_kvq = [&](int64_t n0) {
     const uint32_t rel = (uint32_t)(n0 - n_begin);
 #pragma unroll
@@ -173,11 +186,28 @@ __global__ __launch_bounds__(kCausalThreads) void causal_mfma_kernel(
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qraw[ks] = buf_load16<kCacheNormal>(rq, qoff + 64 * ks);
   };
-  // the gate in the accumulator layout: token nl, features 16*et + 4*kg..+3
+  const int hr = lane / HU, hc = lane % HU;  // whole-row mapping
   auto load_g = [&](int64_t n0) {
-    const uint32_t goff = ((uint32_t)(n0 - n_begin) + 16 * qt + nl) * row_bytes + 8 * kg;
+    const uint32_t goff =
+        ((uint32_t)(n0 - n_begin) + 16 * qt + hr) * row_bytes + eh * D + 16 * hc;
 #pragma unroll
-    for (int u = 0; u < ETW; ++u) graw[u] = buf_load8(rg, goff + 32 * (eh * ETW + u));
+    for (int i = 0; i < HP; ++i) grow[i] = buf_load16<kCacheStream>(rg, goff + i * HRP * row_bytes);
+  };
+  unsigned char *hs = s_kp + wave * (16 * D);  // this wave's half-row tile
+  int hrow[HP], hfrag[ETW];
+#pragma unroll
+  for (int i = 0; i < HP; ++i) {
+    const int row = i * HRP + hr;
+    hrow[i] = row * D + 16 * (hc ^ hswz(row));
+  }
+  // accumulator layout: token nl, features 16*u + 4*kg..+3 of the half
+#pragma unroll
+  for (int u = 0; u < ETW; ++u)
+    hfrag[u] = nl * D + 16 * ((2 * u + (kg >> 1)) ^ hswz(nl)) + 8 * (kg & 1);
+  auto wave_sync = []() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
   // LDS offsets of the read patterns of a step.  The row swizzles of both
@@ -400,14 +430,21 @@ __global__ __launch_bounds__(kCausalThreads) void causal_mfma_kernel(
 
     mfma_drain();
 
-    // den over the token's four lanes (fixed order), the gate and the store
+    // den over the token's four lanes (fixed order)
     dpart += __shfl_xor(dpart, 16);
     dpart += __shfl_xor(dpart, 32);
     const float den = dpart + a.eps;
-    const uint32_t ooff = ((uint32_t)(n0 - n_begin) + 16 * qt + nl) * row_bytes + 8 * kg;
+    __syncthreads();  // every wave is done with the step's tiles
+
+    // the gate and the store through the wave's half-row tile: g rows in,
+    // g fragments out, output fragments in (each lane on its own places),
+    // output rows out
+#pragma unroll
+    for (int i = 0; i < HP; ++i) *reinterpret_cast<uint4 *>(hs + hrow[i]) = grow[i];
+    wave_sync();
 #pragma unroll
     for (int u = 0; u < ETW; ++u) {
-      const uint2 gw = graw[u];
+      const uint2 gw = *reinterpret_cast<const uint2 *>(hs + hfrag[u]);
       const float gv[4] = {lo_bf16(gw.x), hi_bf16(gw.x), lo_bf16(gw.y), hi_bf16(gw.y)};
       float o[4];
 #pragma unroll
@@ -416,11 +453,19 @@ __global__ __launch_bounds__(kCausalThreads) void causal_mfma_kernel(
         const float e = __expf(-gv[i]);
         o[i] = acc[u][i] * __builtin_amdgcn_rcpf(__builtin_fmaf(den, e, den));
       }
-      buf_store8(ro, ooff + 32 * (eh * ETW + u),
-                 make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])));
+      *reinterpret_cast<uint2 *>(hs + hfrag[u]) =
+          make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+    }
+    wave_sync();
+    {
+      const uint32_t ooff =
+          ((uint32_t)(n0 - n_begin) + 16 * qt + hr) * row_bytes + eh * D + 16 * hc;
+#pragma unroll
+      for (int i = 0; i < HP; ++i)
+        buf_store16<kCacheStream>(ro, ooff + i * HRP * row_bytes,
+                                  *reinterpret_cast<const uint4 *>(hs + hrow[i]));
     }
     load_g(n0 + STEP);
-    __syncthreads();
 
     // ---------------- state: S^T += v^T RoPE(phi(k)) over the step's keys
     if (s_owner) {
