@@ -343,10 +343,46 @@ def backward_leg(w, x, steps: int, warmup: int):
                 "frac": tflops / PEAK_FP32_VALU_TFLOPS, "traffic": None,
                 "algorithmic_flops_per_launch": flops}
         kernels = "vector (fp32 VALU) gradient kernels"
+    # The training pair: the forward keeps its reduced state (gla_forward_train)
+    # and the gradients take it (gla_backward_saved), as an autograd step
+    # would, so the state stage is not run twice.  Timed alone and as whole
+    # steps (forward + gradients).
+    dt = gla.GLA_BF16 if w.dtype == "bf16" else gla.GLA_F32
+    saved = torch.empty(gla.gla_saved_state_bytes(w.B, w.H, w.T, w.Hs, w.Ws, w.d,
+                                                  w.frames_per_block) // 4,
+                        dtype=torch.float32, device="cuda")
+    out = torch.empty_like(x["q"])
+    fws = torch.empty(gla.gla_workspace_bytes(w.B, w.H, w.T, w.Hs, w.Ws, w.d, w.frames_per_block,
+                                              dt), dtype=torch.uint8, device="cuda")
+
+    def fwd_train():
+        gla.gla_forward_train(x["q"], x["k"], x["v"], x["g"], out, saved, w.grid,
+                              w.frames_per_block, w.theta, w.eps, workspace=fws, stream=stream)
+
+    def bwd_saved():
+        gla.gla_backward_saved(x["q"], x["k"], x["v"], x["g"], dout, *grads, saved, w.grid,
+                               w.frames_per_block, w.theta, w.eps, workspace=ws, stream=stream)
+
+    def train_step():
+        fwd_train()
+        bwd_saved()
+
+    fwd_train()
+    for _ in range(warmup):
+        bwd_saved()
+    ms_saved, _, _ = timed_calls(bwd_saved, steps, stream, profile=False)
+    for _ in range(warmup):
+        train_step()
+    ms_step, _, _ = timed_calls(train_step, steps, stream, profile=False)
     return {"workload": w.name, "ms_per_call": ms, "tokens_per_s": w.B * w.N / (ms * 1e-3),
             "stages_ms": stage_ms, "algorithmic_bytes_per_call": nbytes, "GBps": gbps,
             "frac_of_peak": gbps / PEAK_HBM_GBPS, "roofline": roof,
-            "kernels": kernels + "; the forward state re-run on the matrix cores"}
+            "kernels": kernels + "; the forward state re-run on the matrix cores",
+            "saved_state": {"ms_per_call": ms_saved,
+                            "training_step_ms": ms_step,
+                            "what": "gla_backward_saved after gla_forward_train (the forward's "
+                                    "S, z kept, no state re-run); training_step_ms: one "
+                                    "gla_forward_train + gla_backward_saved"}}
 
 
 def token_causal_leg(w, x, steps: int, warmup: int, oracle_frames: int = 2):

@@ -245,6 +245,44 @@ gla_status gla_backward_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t
                                         size_t *bytes);
 
 /*
+ * The training pair: a forward that keeps its state, and gradients that take
+ * it instead of re-running the state stage (the same chain rule as
+ * gla_backward; S and z are the sums of "SANA-Video 2.0" Eq. (1) and the
+ * "SANA-Video" notes page, Section 3.2, per temporal block in block-causal
+ * mode as in its Section 3.4).
+ *
+ * saved: caller-owned device memory of gla_saved_state_bytes() bytes,
+ * 256-byte aligned, overlapping no tensor of the call.  Layout: one record
+ * of d*d + d fp32 per (batch, head, temporal block), in that order, b
+ * slowest: S row-major [p][e] (feature p of the rotated key, e of the
+ * value), then z [p]; in block-causal mode a block's record holds the sums
+ * over that block and every earlier one (what the block's outputs read).
+ *
+ * gla_forward_train: gla_forward_ws (workspace may be NULL: taken
+ * stream-ordered on `stream`), which also writes the record of every
+ * (batch, head, block) into `saved`.
+ * gla_backward_saved: gla_backward with the records of a gla_forward_train
+ * call on the same k, v, sizes, frames_per_block and rope_theta (nothing
+ * checks that they match: other contents give the gradients of another
+ * state); enqueues the gradient kernels only.
+ * Both return GLA_ERR_INVALID_ARG for a null, misaligned or overlapping
+ * `saved`, before any launch.
+ */
+gla_status gla_saved_state_bytes(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, int64_t d,
+                                 int64_t frames_per_block, size_t *bytes);
+gla_status gla_forward_train(const void *q, const void *k, const void *v, const void *g, void *out,
+                             int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, int64_t d,
+                             int64_t frames_per_block, float rope_theta, float eps,
+                             gla_dtype dtype, float *saved, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+gla_status gla_backward_saved(const void *q, const void *k, const void *v, const void *g,
+                              const void *dout, void *dq, void *dk, void *dv, void *dg,
+                              const float *saved, int64_t B, int64_t H, int64_t T, int64_t Hs,
+                              int64_t Ws, int64_t d, int64_t frames_per_block, float rope_theta,
+                              float eps, gla_dtype dtype, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Token-causal form ("SANA-Video" notes page, Section 3.4: the causal
  * linear-attention output of token i, the form behind the constant-memory
  * cache): token i of a (batch, head) attends to tokens 0..i of the t-major

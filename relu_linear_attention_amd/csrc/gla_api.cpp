@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <map>
 #include <mutex>
 #include <tuple>
@@ -648,6 +649,25 @@ gla_status check_gates(const Gates &gt, const void *out, size_t bytes, int64_t B
   return GLA_OK;
 }
 
+// Bytes of the saved state of a call: the reduced (S, z) of every (batch,
+// head, temporal block), d*d + d fp32 each.
+size_t saved_state_bytes(int64_t B, int64_t H, int64_t T, int64_t F, int64_t d) {
+  const int64_t nb = F > 0 ? T / F : 1;
+  return (size_t)(B * H * nb) * (size_t)gla::kPartialStride(d) * sizeof(float);
+}
+
+// The saved state buffer: 256-byte aligned (as a workspace), apart from
+// every tensor of the call.
+gla_status check_saved(const void *saved, size_t saved_bytes, size_t tensor_bytes,
+                       std::initializer_list<const void *> tensors) {
+  if (((uintptr_t)saved & 255) != 0)
+    return fail(GLA_ERR_INVALID_ARG, "saved state must be 256-byte aligned");
+  for (const void *t : tensors)
+    if (t != nullptr && ranges_overlap(saved, saved_bytes, t, tensor_bytes))
+      return fail(GLA_ERR_INVALID_ARG, "saved state overlaps a tensor");
+  return GLA_OK;
+}
+
 // Enqueues every stage of the operator on `stream`, with workspace `ws`.
 // With `apply == false` only the state is computed (gla_state, cache-only
 // block steps).
@@ -655,13 +675,16 @@ gla_status check_gates(const Gates &gt, const void *out, size_t bytes, int64_t B
 // not null; may_alloc: the call may allocate the library's cached table and
 // reduce counters.  With one temporal block on the matrix-core path the
 // reduce runs in the state kernel's last workgroups (two launches per call).
+// states_dst: where the reduced states go ([units][d*d + d] fp32), the
+// workspace when null.
 gla_status run_plan(const Plan &P, const void *q, const void *k, const void *v, const void *g,
                     void *out, void *ws, hipStream_t stream, bool apply,
                     const Cache &cache = Cache(), const Gates &gates = Gates(),
-                    bool may_alloc = true, const float2 **tab_used = nullptr) {
+                    bool may_alloc = true, const float2 **tab_used = nullptr,
+                    float *states_dst = nullptr) {
   char *base = (char *)ws;
   float *part = (float *)(base + P.off_part);
-  float *states = (float *)(base + P.off_state);
+  float *states = states_dst != nullptr ? states_dst : (float *)(base + P.off_state);
   uint16_t *frags = P.mfma ? (uint16_t *)(base + P.off_frag) : nullptr;
 
   const float2 *tab = nullptr;
@@ -727,7 +750,7 @@ gla_status forward_impl(const void *q, const void *k, const void *v, const void 
                         int64_t F, float theta, float eps, gla_dtype dtype, void *ws,
                         size_t ws_bytes, bool own_ws, hipStream_t stream,
                         const Step *step = nullptr, const Gates *gates = nullptr,
-                        float rms_eps = 0.f, bool scratch = false) {
+                        float rms_eps = 0.f, bool scratch = false, float *saved = nullptr) {
   g_last_error[0] = '\0';
   gla_status st = check_sizes(B, H, T, Hs, Ws, d, F, dtype);
   if (st != GLA_OK) return st;
@@ -749,6 +772,10 @@ gla_status forward_impl(const void *q, const void *k, const void *v, const void 
   }
   if (!own_ws && !scratch && (ws == nullptr || ((uintptr_t)ws & 255) != 0))
     return fail(GLA_ERR_INVALID_ARG, "workspace must be a non-null, 256-byte aligned pointer");
+  if (saved != nullptr) {
+    st = check_saved(saved, saved_state_bytes(B, H, T, F, d), bytes, {q, k, v, g, out});
+    if (st != GLA_OK) return st;
+  }
   int cus = 0;
   st = device_cus(&cus);
   if (st != GLA_OK) return st;
@@ -786,7 +813,7 @@ gla_status forward_impl(const void *q, const void *k, const void *v, const void 
     if (ws_bytes < P.total_bytes)
       return fail(GLA_ERR_INVALID_ARG, "workspace too small: %zu bytes given, %zu needed", ws_bytes,
                   P.total_bytes);
-    return run_plan(P, q, k, v, g, out, ws, stream, apply, cache, gt);
+    return run_plan(P, q, k, v, g, out, ws, stream, apply, cache, gt, true, nullptr, saved);
   }
   void *mem = nullptr;
   hipError_t e = hipMallocAsync(&mem, P.total_bytes, stream);
@@ -795,9 +822,98 @@ gla_status forward_impl(const void *q, const void *k, const void *v, const void 
     return fail(GLA_ERR_ALLOC, "hipMallocAsync of %zu workspace bytes failed: %s", P.total_bytes,
                 hipGetErrorString(e));
   }
-  st = run_plan(P, q, k, v, g, out, mem, stream, apply, cache, gt);
+  st = run_plan(P, q, k, v, g, out, mem, stream, apply, cache, gt, true, nullptr, saved);
   e = hipFreeAsync(mem, stream);
   if (st == GLA_OK && e != hipSuccess) return hip_fail(e, "hipFreeAsync");
+  return st;
+}
+
+// Gradients; with `saved` (the states a gla_forward_train call kept) the
+// state stage is not re-run.
+gla_status backward_impl(const void *q, const void *k, const void *v, const void *g,
+                         const void *dout, void *dq, void *dk, void *dv, void *dg, int64_t B,
+                         int64_t H, int64_t T, int64_t Hs, int64_t Ws, int64_t d,
+                         int64_t frames_per_block, float rope_theta, float eps, gla_dtype dtype,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream,
+                         const float *saved) {
+  g_last_error[0] = '\0';
+  const int64_t F = frames_per_block;
+  gla_status st = check_sizes(B, H, T, Hs, Ws, d, F, dtype);
+  if (st != GLA_OK) return st;
+  if (!std::isfinite(rope_theta)) return fail(GLA_ERR_INVALID_ARG, "rope_theta must be finite");
+  if (!std::isfinite(eps) || eps < 0.f)
+    return fail(GLA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  const void *ins[5] = {q, k, v, g, dout};
+  const void *outs[4] = {dq, dk, dv, dg};
+  const char *in_names[5] = {"q", "k", "v", "g", "dout"};
+  const char *out_names[4] = {"dq", "dk", "dv", "dg"};
+  for (int i = 0; i < 5; ++i)
+    if (!ins[i]) return fail(GLA_ERR_INVALID_ARG, "null tensor pointer (%s)", in_names[i]);
+  for (int i = 0; i < 4; ++i)
+    if (!outs[i]) return fail(GLA_ERR_INVALID_ARG, "null tensor pointer (%s)", out_names[i]);
+  const size_t bytes = (size_t)(B * T * Hs * Ws * H * d) * (dtype == GLA_BF16 ? 2 : 4);
+  for (int o = 0; o < 4; ++o) {
+    for (int i = 0; i < 5; ++i)
+      if (ranges_overlap(outs[o], bytes, ins[i], bytes))
+        return fail(GLA_ERR_INVALID_ARG, "%s overlaps input %s", out_names[o], in_names[i]);
+    for (int o2 = o + 1; o2 < 4; ++o2)
+      if (ranges_overlap(outs[o], bytes, outs[o2], bytes))
+        return fail(GLA_ERR_INVALID_ARG, "%s overlaps %s", out_names[o], out_names[o2]);
+  }
+  if (workspace != nullptr && ((uintptr_t)workspace & 255) != 0)
+    return fail(GLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (saved != nullptr) {
+    st = check_saved(saved, saved_state_bytes(B, H, T, F, d), bytes,
+                     {q, k, v, g, dout, dq, dk, dv, dg});
+    if (st != GLA_OK) return st;
+  }
+  int cus = 0;
+  st = device_cus(&cus);
+  if (st != GLA_OK) return st;
+  // (the matrix-core kernels move 16-byte pieces of q, k and v and 8-byte
+  // pieces of every tensor)
+  uintptr_t all = 0;
+  for (const void *t : ins) all |= (uintptr_t)t;
+  for (const void *t : outs) all |= (uintptr_t)t;
+  const bool aligned16 = (all & 15) == 0;
+  Plan P;
+  st = make_plan(B, H, T, Hs, Ws, d, F, dtype, rope_theta, eps, cus, aligned16, &P);
+  if (st != GLA_OK) return st;
+  if (workspace != nullptr && workspace_bytes < P.bwd_total_bytes)
+    return fail(GLA_ERR_INVALID_ARG, "workspace too small: %zu bytes given, %zu needed",
+                workspace_bytes, P.bwd_total_bytes);
+  void *mem = workspace;
+  if (mem == nullptr) {
+    hipError_t e = hipMallocAsync(&mem, P.bwd_total_bytes, stream);
+    if (e != hipSuccess || mem == nullptr) {
+      (void)hipGetLastError();
+      return fail(GLA_ERR_ALLOC, "hipMallocAsync of %zu workspace bytes failed", P.bwd_total_bytes);
+    }
+  }
+  // the forward state of the call (re-run, or the saved one), then the
+  // gradient kernels
+  char *base = (char *)mem;
+  const float2 *tab = nullptr;
+  const float *states = saved;
+  if (saved != nullptr) {
+    st = rope_table_for(P, (float2 *)(base + P.off_tab), stream, true, &tab);
+  } else {
+    st = run_plan(P, nullptr, k, v, nullptr, nullptr, mem, stream, false, Cache(), Gates(), true,
+                  &tab);
+    states = (const float *)(base + P.off_state);
+  }
+  if (st == GLA_OK) {
+    st = timed_launch(4, stream, "gradient kernels", [&] {
+      return gla::launch_backward(P, q, k, v, g, dout, states, tab,
+                                  (float *)(base + P.off_bpart), (float *)(base + P.off_grad),
+                                  (float2 *)(base + P.off_dd),
+                                  dq, dk, dv, dg, stream);
+    });
+  }
+  if (workspace == nullptr) {
+    hipError_t e = hipFreeAsync(mem, stream);
+    if (st == GLA_OK && e != hipSuccess) return hip_fail(e, "hipFreeAsync");
+  }
   return st;
 }
 
@@ -939,73 +1055,46 @@ gla_status gla_backward(const void *q, const void *k, const void *v, const void 
                         int64_t H, int64_t T, int64_t Hs, int64_t Ws, int64_t d,
                         int64_t frames_per_block, float rope_theta, float eps, gla_dtype dtype,
                         void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  return backward_impl(q, k, v, g, dout, dq, dk, dv, dg, B, H, T, Hs, Ws, d, frames_per_block,
+                       rope_theta, eps, dtype, workspace, workspace_bytes, stream, nullptr);
+}
+
+gla_status gla_saved_state_bytes(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws,
+                                 int64_t d, int64_t frames_per_block, size_t *bytes) {
   g_last_error[0] = '\0';
-  const int64_t F = frames_per_block;
-  gla_status st = check_sizes(B, H, T, Hs, Ws, d, F, dtype);
+  if (!bytes) return fail(GLA_ERR_INVALID_ARG, "bytes must not be null");
+  gla_status st = check_sizes(B, H, T, Hs, Ws, d, frames_per_block, GLA_F32);
   if (st != GLA_OK) return st;
-  if (!std::isfinite(rope_theta)) return fail(GLA_ERR_INVALID_ARG, "rope_theta must be finite");
-  if (!std::isfinite(eps) || eps < 0.f)
-    return fail(GLA_ERR_INVALID_ARG, "eps must be finite and >= 0");
-  const void *ins[5] = {q, k, v, g, dout};
-  const void *outs[4] = {dq, dk, dv, dg};
-  const char *in_names[5] = {"q", "k", "v", "g", "dout"};
-  const char *out_names[4] = {"dq", "dk", "dv", "dg"};
-  for (int i = 0; i < 5; ++i)
-    if (!ins[i]) return fail(GLA_ERR_INVALID_ARG, "null tensor pointer (%s)", in_names[i]);
-  for (int i = 0; i < 4; ++i)
-    if (!outs[i]) return fail(GLA_ERR_INVALID_ARG, "null tensor pointer (%s)", out_names[i]);
-  const size_t bytes = (size_t)(B * T * Hs * Ws * H * d) * (dtype == GLA_BF16 ? 2 : 4);
-  for (int o = 0; o < 4; ++o) {
-    for (int i = 0; i < 5; ++i)
-      if (ranges_overlap(outs[o], bytes, ins[i], bytes))
-        return fail(GLA_ERR_INVALID_ARG, "%s overlaps input %s", out_names[o], in_names[i]);
-    for (int o2 = o + 1; o2 < 4; ++o2)
-      if (ranges_overlap(outs[o], bytes, outs[o2], bytes))
-        return fail(GLA_ERR_INVALID_ARG, "%s overlaps %s", out_names[o], out_names[o2]);
+  *bytes = saved_state_bytes(B, H, T, frames_per_block, d);
+  return GLA_OK;
+}
+
+gla_status gla_forward_train(const void *q, const void *k, const void *v, const void *g,
+                             void *out, int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws,
+                             int64_t d, int64_t frames_per_block, float rope_theta, float eps,
+                             gla_dtype dtype, float *saved, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  if (saved == nullptr) {
+    g_last_error[0] = '\0';
+    return fail(GLA_ERR_INVALID_ARG, "saved must not be null");
   }
-  if (workspace != nullptr && ((uintptr_t)workspace & 255) != 0)
-    return fail(GLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  int cus = 0;
-  st = device_cus(&cus);
-  if (st != GLA_OK) return st;
-  // (the matrix-core kernels move 16-byte pieces of q, k and v and 8-byte
-  // pieces of every tensor)
-  uintptr_t all = 0;
-  for (const void *t : ins) all |= (uintptr_t)t;
-  for (const void *t : outs) all |= (uintptr_t)t;
-  const bool aligned16 = (all & 15) == 0;
-  Plan P;
-  st = make_plan(B, H, T, Hs, Ws, d, F, dtype, rope_theta, eps, cus, aligned16, &P);
-  if (st != GLA_OK) return st;
-  if (workspace != nullptr && workspace_bytes < P.bwd_total_bytes)
-    return fail(GLA_ERR_INVALID_ARG, "workspace too small: %zu bytes given, %zu needed",
-                workspace_bytes, P.bwd_total_bytes);
-  void *mem = workspace;
-  if (mem == nullptr) {
-    hipError_t e = hipMallocAsync(&mem, P.bwd_total_bytes, stream);
-    if (e != hipSuccess || mem == nullptr) {
-      (void)hipGetLastError();
-      return fail(GLA_ERR_ALLOC, "hipMallocAsync of %zu workspace bytes failed", P.bwd_total_bytes);
-    }
+  return forward_impl(q, k, v, g, out, B, H, T, Hs, Ws, d, frames_per_block, rope_theta, eps,
+                      dtype, workspace, workspace_bytes, workspace == nullptr, stream, nullptr,
+                      nullptr, 0.f, false, saved);
+}
+
+gla_status gla_backward_saved(const void *q, const void *k, const void *v, const void *g,
+                              const void *dout, void *dq, void *dk, void *dv, void *dg,
+                              const float *saved, int64_t B, int64_t H, int64_t T, int64_t Hs,
+                              int64_t Ws, int64_t d, int64_t frames_per_block, float rope_theta,
+                              float eps, gla_dtype dtype, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  if (saved == nullptr) {
+    g_last_error[0] = '\0';
+    return fail(GLA_ERR_INVALID_ARG, "saved must not be null");
   }
-  // the forward state of the call, then the gradient kernels
-  const float2 *tab = nullptr;
-  st = run_plan(P, nullptr, k, v, nullptr, nullptr, mem, stream, false, Cache(), Gates(), true,
-                &tab);
-  if (st == GLA_OK) {
-    char *base = (char *)mem;
-    st = timed_launch(4, stream, "gradient kernels", [&] {
-      return gla::launch_backward(P, q, k, v, g, dout, (const float *)(base + P.off_state), tab,
-                                  (float *)(base + P.off_bpart), (float *)(base + P.off_grad),
-                                  (float2 *)(base + P.off_dd),
-                                  dq, dk, dv, dg, stream);
-    });
-  }
-  if (workspace == nullptr) {
-    hipError_t e = hipFreeAsync(mem, stream);
-    if (st == GLA_OK && e != hipSuccess) return hip_fail(e, "hipFreeAsync");
-  }
-  return st;
+  return backward_impl(q, k, v, g, dout, dq, dk, dv, dg, B, H, T, Hs, Ws, d, frames_per_block,
+                       rope_theta, eps, dtype, workspace, workspace_bytes, stream, saved);
 }
 
 gla_status gla_token_causal_forward(const void *q, const void *k, const void *v, const void *g,

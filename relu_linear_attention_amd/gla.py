@@ -26,7 +26,8 @@ GLA_NUM_STAGES = 6
 EXPORTS = (
     "gla_forward", "gla_block_causal_forward", "gla_workspace_bytes", "gla_forward_ws",
     "gla_forward_noalloc", "gla_state", "gla_block_step", "gla_gated_forward", "gla_backward",
-    "gla_backward_workspace_bytes", "gla_token_causal_forward", "gla_token_causal_workspace_bytes",
+    "gla_backward_workspace_bytes", "gla_saved_state_bytes", "gla_forward_train",
+    "gla_backward_saved", "gla_token_causal_forward", "gla_token_causal_workspace_bytes",
     "gla_status_string", "gla_last_error", "gla_profile_enable",
     "gla_profile_read", "gla_stage_name", "gla_uses_matrix_cores",
 )
@@ -71,13 +72,19 @@ def load():
                                                         ctypes.c_size_t, _vp])
     lib.gla_backward_workspace_bytes.argtypes = sizes6 + [_i64, ctypes.c_int,
                                                           ctypes.POINTER(ctypes.c_size_t)]
+    lib.gla_saved_state_bytes.argtypes = sizes6 + [_i64, ctypes.POINTER(ctypes.c_size_t)]
+    lib.gla_forward_train.argtypes = (tensors5 + sizes6 + [_i64, _f, _f, ctypes.c_int, _vp, _vp,
+                                                           ctypes.c_size_t, _vp])
+    lib.gla_backward_saved.argtypes = ([_vp] * 10 + sizes6 + [_i64, _f, _f, ctypes.c_int, _vp,
+                                                              ctypes.c_size_t, _vp])
     lib.gla_token_causal_forward.argtypes = (tensors5 + sizes6 + [_f, _f, ctypes.c_int, _vp,
                                                                   ctypes.c_size_t, _vp])
     lib.gla_token_causal_workspace_bytes.argtypes = sizes6 + [ctypes.c_int,
                                                               ctypes.POINTER(ctypes.c_size_t)]
     for name in ("gla_forward", "gla_block_causal_forward", "gla_workspace_bytes",
                  "gla_forward_ws", "gla_forward_noalloc", "gla_state", "gla_block_step", "gla_gated_forward",
-                 "gla_backward", "gla_backward_workspace_bytes", "gla_token_causal_forward",
+                 "gla_backward", "gla_backward_workspace_bytes", "gla_saved_state_bytes",
+                 "gla_forward_train", "gla_backward_saved", "gla_token_causal_forward",
                  "gla_token_causal_workspace_bytes", "gla_profile_enable",
                  "gla_profile_read"):
         getattr(lib, name).restype = ctypes.c_int
@@ -257,6 +264,42 @@ def gla_backward_workspace_bytes(B, H, T, Hs, Ws, d, frames_per_block=0, dtype=G
     _check(load().gla_backward_workspace_bytes(B, H, T, Hs, Ws, d, frames_per_block, dtype,
                                                ctypes.byref(n)), "gla_backward_workspace_bytes")
     return n.value
+
+
+def gla_saved_state_bytes(B, H, T, Hs, Ws, d, frames_per_block=0) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().gla_saved_state_bytes(B, H, T, Hs, Ws, d, frames_per_block, ctypes.byref(n)),
+           "gla_saved_state_bytes")
+    return n.value
+
+
+def gla_forward_train(q, k, v, g, out, saved, grid, frames_per_block=0, rope_theta=10000.0,
+                      eps=1e-6, workspace=None, stream=None):
+    """Either operator, which also writes its reduced state (S, z of every
+    (batch, head, block), fp32) into `saved` (a device tensor of
+    gla_saved_state_bytes() bytes) for gla_backward_saved."""
+    _check_tensors(*[t for t in (q, k, v, g, out, saved, workspace) if t is not None])
+    B, H, T, Hs, Ws, d = _sizes(q, grid)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().gla_forward_train(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(out), B, H, T, Hs, Ws,
+                                  d, frames_per_block, rope_theta, eps, _dtype_code(q),
+                                  _ptr(saved), _ptr(workspace), ws_bytes, _stream_handle(stream))
+    _check(st, "gla_forward_train")
+
+
+def gla_backward_saved(q, k, v, g, dout, dq, dk, dv, dg, saved, grid, frames_per_block=0,
+                       rope_theta=10000.0, eps=1e-6, workspace=None, stream=None):
+    """gla_backward given the state a gla_forward_train call kept in `saved`
+    (the state stage is not re-run)."""
+    _check_tensors(*[t for t in (q, k, v, g, dout, dq, dk, dv, dg, saved, workspace)
+                     if t is not None])
+    B, H, T, Hs, Ws, d = _sizes(q, grid)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().gla_backward_saved(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(dout), _ptr(dq),
+                                   _ptr(dk), _ptr(dv), _ptr(dg), _ptr(saved), B, H, T, Hs, Ws, d,
+                                   frames_per_block, rope_theta, eps, _dtype_code(q),
+                                   _ptr(workspace), ws_bytes, _stream_handle(stream))
+    _check(st, "gla_backward_saved")
 
 
 def gla_token_causal_forward(q, k, v, g, out, grid, rope_theta=10000.0, eps=1e-6, workspace=None,

@@ -195,6 +195,41 @@ def test_token_causal_rejects_bad_arguments(lib, kw, needle):
     assert needle in gla.gla_last_error()
 
 
+def test_saved_state_bytes(lib):
+    # one record of d*d + d floats per (batch, head, temporal block)
+    assert gla.gla_saved_state_bytes(2, 3, 6, 4, 5, 64, 0) == 2 * 3 * 1 * (64 * 64 + 64) * 4
+    assert gla.gla_saved_state_bytes(2, 3, 6, 4, 5, 64, 2) == 2 * 3 * 3 * (64 * 64 + 64) * 4
+    n = ctypes.c_size_t(0)
+    assert lib.gla_saved_state_bytes(1, 1, 3, 2, 2, 128, 2, ctypes.byref(n)) == 1
+    assert "divide" in gla.gla_last_error()
+    assert lib.gla_saved_state_bytes(1, 1, 3, 2, 2, 128, 0, None) == 1
+
+
+def _train(lib, saved, ts=(FAKE, FAKE * 3, FAKE * 5, FAKE * 7, FAKE * 9)):
+    p = [ctypes.c_void_p(x) for x in ts]
+    s = ctypes.c_void_p(saved) if saved else None
+    return lib.gla_forward_train(*p, 1, 2, 2, 4, 4, 32, 0, 1e4, 1e-6, gla.GLA_BF16, s, None, 0,
+                                 None)
+
+
+def _bwd_saved(lib, saved):
+    p = [ctypes.c_void_p(FAKE * i) for i in (1, 3, 5, 7, 9, 11, 13, 15, 17)]
+    s = ctypes.c_void_p(saved) if saved else None
+    return lib.gla_backward_saved(*p, s, 1, 2, 2, 4, 4, 32, 0, 1e4, 1e-6, gla.GLA_BF16, None, 0,
+                                  None)
+
+
+@pytest.mark.parametrize("call", [_train, _bwd_saved])
+@pytest.mark.parametrize("saved,needle", [
+    (0, "saved must not be null"),
+    (FAKE * 21 + 16, "256-byte aligned"),
+    (FAKE * 3 + 256, "overlaps"),  # inside k (each fake tensor spans 4 KiB here)
+])
+def test_training_pair_rejects_bad_saved_state(lib, call, saved, needle):
+    assert call(lib, saved) == gla.GLA_ERR_INVALID_ARG
+    assert needle in gla.gla_last_error()
+
+
 def test_workspace_query_rejects_bad_sizes(lib):
     n = ctypes.c_size_t(0)
     assert lib.gla_workspace_bytes(1, 1, 3, 2, 2, 128, 2, 0, ctypes.byref(n)) == 1

@@ -192,8 +192,7 @@ def _quotient_term_scales(q, k, v, g, dout, grid, F, theta=1e4, eps=1e-6):
     T, Hs, Ws = grid
     nb = oracle.num_blocks(T, F)
     L = N // nb
-    S, z = oracle.state(k, v, grid, F, theta)
-    S, z = np.cumsum(S, axis=2), np.cumsum(z, axis=2)  # inclusive over blocks
+    S, z = oracle.state(k, v, grid, F, theta)  # block b: the sums over blocks 0..b
     pos = [(n // (Hs * Ws), (n // Ws) % Hs, n % Ws) for n in range(N)]
     sq = sk = 0.0
     for b in range(B):
