@@ -28,11 +28,43 @@ pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs 
 GRAD_FLOOR = {"f32": 1e-2, "bf16": 1e-3}
 
 
-def grad_err(got, ref, dtype: str = "bf16") -> float:
+def grad_err(got, ref, dtype: str = "bf16", scale: float = 0.0) -> float:
+    """The gradient bar's error; the floor is relative to the larger of the
+    tensor's own scale and `scale` (the magnitude of terms that cancel in it,
+    when known)."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
-    floor = GRAD_FLOOR[dtype] * float(np.max(np.abs(ref)))
+    floor = GRAD_FLOOR[dtype] * max(float(np.max(np.abs(ref))), scale)
     return float(np.max(np.abs(got - ref) / (np.abs(ref) + floor)))
+
+
+def dq_term_scale(x, dout, out, grid, F, theta=1e4, eps=1e-6) -> float:
+    """Largest magnitude of the two quotient-rule terms of dq, S dnum_i and
+    dden_i z (before RoPE^T, which keeps pair norms), from the oracle's block
+    states and its forward output `out` (y = out / sigmoid(g)); vectorised.
+    The output is invariant to scaling q up to eps, so dq is the difference
+    of these terms and can be far smaller than either, while the
+    arithmetic's errors scale with the terms."""
+    q, g, do, o = (np.asarray(a, dtype=np.float64) for a in (x["q"], x["g"], dout, out))
+    B, N, H, d = q.shape
+    S, z = oracle.state(x["k"], x["v"], grid, F, theta)  # block b: sums over blocks 0..b
+    nb = S.shape[2]
+    L = N // nb
+    s = 1.0 / (1.0 + np.exp(-g))
+    y = o / s
+    pq = np.maximum(q, 0.0)
+    scale = 0.0
+    for b in range(B):
+        for h in range(H):
+            for blk in range(nb):
+                sl = slice(blk * L, (blk + 1) * L)
+                den = pq[b, sl, h] @ z[b, h, blk] + eps
+                sd = s[b, sl, h] * do[b, sl, h]
+                dnum = sd / den[:, None]
+                dden = -np.sum(sd * y[b, sl, h], axis=1) / den
+                scale = max(scale, float(np.max(np.abs(dnum @ S[b, h, blk].T))),
+                            float(np.max(np.abs(dden))) * float(np.max(np.abs(z[b, h, blk]))))
+    return scale
 
 
 def _run(dev, dout, grid, F, workspace=None):

@@ -5,7 +5,12 @@ d = 16..128 (vector kernels), non-causal and block-causal.  Each case runs the
 forward (block-causal cases also streamed through the block step), the
 token-causal form, the gradients and the gated mixer (beta and RMSNorm) with
 the bars of their own tests; dq and dk of blocks under four
-tokens are left to test_one_token_blocks_backward (their terms cancel)."""
+tokens are left to test_one_token_blocks_backward (their terms cancel).
+The floor of dq's bar is relative to the larger of max|dq| and its two
+quotient-rule terms (S dnum and dden z), which cancel because the output is
+invariant to scaling q: a d = 16 case whose terms are 37 times max|dq|
+had errors of 7e-8 of the terms (one fp32 rounding), which the tensor-scale
+floor alone scored 2.7e-4 against the bar of 1e-4."""
 import random
 
 import numpy as np
@@ -15,7 +20,7 @@ import oracle
 from relu_linear_attention_amd import gla
 from relu_linear_attention_amd.inputs import host_inputs
 from tests.gpu_util import TOL, have_gpu, max_rel_err
-from tests.test_backward_gpu import grad_err
+from tests.test_backward_gpu import dq_term_scale, grad_err
 from tests.test_gated_gpu import gated_err
 from tests.test_token_causal_gpu import token_causal_err
 
@@ -89,10 +94,12 @@ def test_random_shape(case):
     torch.cuda.synchronize()
     refs = oracle.backward(x["q"], x["k"], x["v"], x["g"], dout, grid, F)
     small_blocks = (F or T) * Hs * Ws < 4
+    # dq's floor also covers its two quotient-rule terms, which cancel
+    sq = dq_term_scale(x, dout, ref_fwd, grid, F)
     for name, a, r in zip(("dq", "dk", "dv", "dg"), grads, refs):
         if small_blocks and name in ("dq", "dk"):
             continue
-        assert grad_err(a.float().cpu().numpy(), r, dtype) <= tol, name
+        assert grad_err(a.float().cpu().numpy(), r, dtype, sq if name == "dq" else 0.0) <= tol, name
 
     rng = np.random.default_rng(9000 + i)
     beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((B, T * Hs * Ws, H))))).astype(np.float32)
