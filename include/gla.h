@@ -50,7 +50,8 @@
  *   nothing.  GLA_ERR_HIP means that the HIP runtime refused a call or a
  *   launch; when it refuses a later launch of a call, earlier kernels of
  *   that call may already be enqueued, and the call's outputs (for
- *   gla_block_step with update also the cache) are then unspecified.
+ *   gla_block_step with update also the cache, for gla_forward_train also
+ *   the saved state) are then unspecified.
  *   gla_last_error() returns a description of the last failure on the
  *   calling thread.  No C++ exception crosses this interface.
  * Library memory.  On each device the library keeps, until the process

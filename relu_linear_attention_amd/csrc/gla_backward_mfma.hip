@@ -192,10 +192,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_kernel(
       store_tile_rows<D>(stage, vals, rdv, row0, row_bytes);
     }
 
-    // ---- dk = [RoPE^T(G v) + Gz] * 1[k > 0], in k's layout: output tile
-    // pt = 2 ks' + half takes A rows nl = G rows 32 ks' + 8 (nl / 4) + 4 half +
-    // nl % 4, so that lane (token, kg) receives features 32 ks' + 8 kg + 0..7,
-    // the features it loaded of k (the mask and the pairs stay in the lane)
+    // ---- dk = [RoPE^T(G v) + Gz] * 1[k > 0], in k's operand layout: output
+    // tile pt = 2 ks' + half takes A rows nl = G rows 32 ks' + 8 (nl / 4) +
+    // 4 half + nl % 4, so that lane (token, kg) receives features 32 ks' +
+    // 8 kg + 0..7, the features of k it holds (the mask and the pairs stay
+    // in the lane); the rows then leave through the staging tile
     {
       uint4 vb[KS];
       to_operand(stage, vr, vb);
