@@ -114,6 +114,26 @@ def test_one_token_frames_match_block_causal_and_last_token_noncausal():
         <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("key", [0, 5, 17, 38, 63, 64, 101, 127])
+def test_single_key_probe(key):
+    # Every key zero but one (token `key` of two 64-token steps): each later
+    # query reads it through exactly one score, on the diagonal tile when
+    # they share a 16-token tile.  A lost accumulation step of a score tile
+    # (a vector read of a matrix-core result issued before the result was
+    # complete) once showed on such probes as 4/3 of the right value.
+    B, T, Hs, Ws, H, d = 1, 2, 8, 8, 2, 128
+    x = host_inputs(B, T, Hs, Ws, H, d, "bf16", seed=53 + key)
+    k = np.zeros_like(x["k"])
+    k[:, key] = np.abs(x["k"][:, key])
+    x["k"] = k
+    got = _run(to_device(x, "bf16"), (T, Hs, Ws))
+    ref = oracle.token_causal(x["q"], x["k"], x["v"], x["g"], (T, Hs, Ws))
+    assert np.max(np.abs(ref[:, key:])) > 1e-2  # the probe reaches the later queries
+    err = max_rel_err(to_host_f32(got), ref)
+    print(f"key {key}: max rel err {err:.3e}", flush=True)
+    assert err <= TOL["bf16"]
+
+
 def test_deterministic_and_caller_workspace():
     import torch
 
