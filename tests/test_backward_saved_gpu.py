@@ -15,7 +15,7 @@ import pytest
 import oracle
 from relu_linear_attention_amd import gla
 from relu_linear_attention_amd.inputs import host_inputs
-from tests.gpu_util import TOL, have_gpu, to_device, to_host_f32
+from tests.gpu_util import TOL, have_gpu, max_rel_err, to_device, to_host_f32
 from tests.test_backward_gpu import _dout, _run, grad_err
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
@@ -125,3 +125,34 @@ def test_training_pair_with_workspaces_and_bad_saved_state():
     with pytest.raises(gla.GlaError):
         gla.gla_backward_saved(dev["q"], dev["k"], dev["v"], dev["g"], ddev, *b, big[4:], grid,
                                F)
+
+
+def test_training_pair_unaligned_tensors():
+    # misaligned tensors take the vector kernels on both sides; the saved
+    # records are the same state, so the gradients still match gla_backward
+    # bit for bit and the oracle to the bar
+    import torch
+
+    from tests.gpu_util import unaligned_copies
+
+    B, T, Hs, Ws, H, d, F = 1, 4, 5, 6, 2, 128, 2
+    grid = (T, Hs, Ws)
+    x = host_inputs(B, T, Hs, Ws, H, d, "bf16", seed=79)
+    dout = _dout(x["q"].shape, "bf16", 80)
+    ts, place = unaligned_copies(dict(x, o=dout))
+    saved = torch.empty(gla.gla_saved_state_bytes(B, H, T, Hs, Ws, d, F) // 4,
+                        dtype=torch.float32, device="cuda")
+    out = place(ts["q"].shape)
+    gla.gla_forward_train(ts["q"], ts["k"], ts["v"], ts["g"], out, saved, grid, F)
+    got = [place(ts["q"].shape) for _ in range(4)]
+    gla.gla_backward_saved(ts["q"], ts["k"], ts["v"], ts["g"], ts["o"], *got, saved, grid, F)
+    full = [place(ts["q"].shape) for _ in range(4)]
+    gla.gla_backward(ts["q"], ts["k"], ts["v"], ts["g"], ts["o"], *full, grid, F)
+    torch.cuda.synchronize()
+    for a, b in zip(got, full):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert max_rel_err(to_host_f32(out), oracle.forward(x["q"], x["k"], x["v"], x["g"], grid, F)) \
+        <= TOL["bf16"]
+    ref = oracle.backward(x["q"], x["k"], x["v"], x["g"], dout, grid, F)
+    for gname, a, r in zip(("dq", "dk", "dv", "dg"), got, ref):
+        assert grad_err(to_host_f32(a), r) <= TOL["bf16"], gname
