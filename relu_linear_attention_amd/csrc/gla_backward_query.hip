@@ -570,20 +570,19 @@ __global__ __launch_bounds__(kDsThreads<D>, 3) void bwd_dstate_mfma_kernel(
         split_bf16x2(x[2], x[3], xh.y, xl.y);
         split_bf16x2(x[4], x[5], xh.z, xl.z);
         split_bf16x2(x[6], x[7], xh.w, xl.w);
-        // dnum = dout s / den; rows past the chunk read den as 0 and must
-        // give dnum = 0 (0 * inf would put NaN into every element of dS)
+        // dnum = dout s / den = dout / (den (1 + exp(-g))); rows past the
+        // chunk read den and dout as 0, and take den = 1 so that their dnum
+        // is 0 (0 / 0 would put NaN into every element of dS)
         const bool valid = n0 + tg < n_end;
-        const float inv_den = valid ? __builtin_amdgcn_rcpf(ddr[j].x) : 0.f;
+        const float den = valid ? ddr[j].x : 1.f;
         const uint32_t gw[4] = {gr[j].x, gr[j].y, gr[j].z, gr[j].w};
         const uint32_t dw[4] = {dr[j].x, dr[j].y, dr[j].z, dr[j].w};
         float dn[8];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const float g0 = lo_bf16(gw[m]), g1 = hi_bf16(gw[m]);
-          const float s0 = __builtin_amdgcn_rcpf(1.f + __expf(-g0));
-          const float s1 = __builtin_amdgcn_rcpf(1.f + __expf(-g1));
-          dn[2 * m] = lo_bf16(dw[m]) * s0 * inv_den;
-          dn[2 * m + 1] = hi_bf16(dw[m]) * s1 * inv_den;
+          const float e0 = __expf(-lo_bf16(gw[m])), e1 = __expf(-hi_bf16(gw[m]));
+          dn[2 * m] = lo_bf16(dw[m]) * __builtin_amdgcn_rcpf(__builtin_fmaf(den, e0, den));
+          dn[2 * m + 1] = hi_bf16(dw[m]) * __builtin_amdgcn_rcpf(__builtin_fmaf(den, e1, den));
         }
         uint4 nh, nlo;
         split_bf16x2(dn[0], dn[1], nh.x, nlo.x);
