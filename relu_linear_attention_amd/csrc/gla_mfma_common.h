@@ -134,9 +134,12 @@ __device__ __forceinline__ uint32_t relu_bf16x2(uint32_t x) {
 // 0xffff in each 16-bit half of x that is nonzero, else 0, for x a packed
 // pair of ReLU results (each half in 0..0x7f80): the mask of the elements
 // with x > 0.  A nonzero half h has -h in 0x8080..0xffff, so the arithmetic
-// shift of -h by 15 gives 0xffff, and 0 gives 0 (two packed 16-bit ops).
+// shift of -h by 15 gives 0xffff, and 0 gives 0: two packed 16-bit ops.  (An
+// empty register-only asm between them keeps the compiler from turning the
+// pair into per-half compares and selects, four to five instructions.)
 __device__ __forceinline__ uint32_t nonzero_mask16(uint32_t x) {
-  const s16x2 neg = s16x2{0, 0} - __builtin_bit_cast(s16x2, x);
+  s16x2 neg = s16x2{0, 0} - __builtin_bit_cast(s16x2, x);
+  asm("" : "+v"(neg));
   return __builtin_bit_cast(uint32_t, neg >> s16x2{15, 15});
 }
 
