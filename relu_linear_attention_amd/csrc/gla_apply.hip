@@ -172,10 +172,11 @@ __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
   // num and den of two 16-token blocks (A, B) that share every S fragment
   // read: per k-step, each pair of S^T fragments (hi, lo) of an output tile
   // feeds six products, three per block (nb2 false: block A alone)
-  auto products = [&](auto nb2, int64_t tA, int64_t tB, const uint4 (&cqA)[KS],
+  auto products = [&](auto nb2, auto row16, int64_t tA, int64_t tB, const uint4 (&cqA)[KS],
                       const uint4 (&cqB)[KS], f32x4 (&accA)[ET], f32x4 (&accB)[ET], float &denA,
                       float &denB) {
     constexpr bool kTwo = decltype(nb2)::value;
+    constexpr bool kRow16 = decltype(row16)::value;
     // An offset the compiler cannot see through (always 0) keeps the
     // loop-invariant S-part reads inside the loop: hoisting all of them
     // would need 256 registers per lane.  It is a register-only asm, so it
@@ -184,11 +185,15 @@ __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
     asm volatile("" : "+v"(opaque));
     const unsigned char *sh = s_sh + opaque, *sl = s_sl + opaque;
     int pA[3], pB[3];
-    {
-      const int64_t nA = tA + nl, nB = tB + nl;
-      token_pos(a, nA < n_end ? nA : n_end - 1, pA[0], pA[1], pA[2]);
-      if (kTwo) token_pos(a, nB < n_end ? nB : n_end - 1, pB[0], pB[1], pB[2]);
-    }
+    block_token_pos<kRow16>(a, tA, n_end, nl, pA[0], pA[1], pA[2]);
+    if (kTwo) block_token_pos<kRow16>(a, tB, n_end, nl, pB[0], pB[1], pB[2]);
+    // Raised wave priority while this wave issues its products: of the two
+    // waves on a SIMD, the one in its product phase then issues first, and
+    // the other's gate and store work fills the gaps (the products phase
+    // mixes matrix-core and vector work, the gate phase is vector work only).
+    // Measured: -4% for this kernel and -2% per call over calls 5-24 at
+    // 720p/81f, where the shader clock is low and the kernels issue-bound.
+    __builtin_amdgcn_s_setprio(1);
     f32x4 adA = {0.f, 0.f, 0.f, 0.f}, adB = adA;
 #pragma unroll
     for (int et = 0; et < ET; ++et) accA[et] = accB[et] = adA;
@@ -235,6 +240,7 @@ __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     denA = adA[0] + adA[1] + a.eps;
     denB = kTwo ? adB[0] + adB[1] + a.eps : 0.f;
   };
@@ -312,71 +318,81 @@ __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  const int64_t kStep = kItem * a.am;
-  int64_t tile = n_begin + slot * kItem + 16 * wave;
-  if constexpr (kPair) {
-    // The workgroup takes the items slot, slot + m, ... of its super-range; a
-    // wave takes the 16-token block 16 wave of two consecutive ones (A, B) at
-    // a time.  q of the next pair is in flight during the current pair's
-    // products and gates; g of a block is refilled right after its gate and
-    // arrives during the next pair's products.  Refills are unconditional
-    // (blocks past the range read as zeros and their stores are dropped):
-    // with a branch around them the compiler waits for every outstanding
-    // load at the join.  With an odd item count the last pair's second block
-    // lies past the range; the plan takes pairs only where that block is
-    // off the critical path or a small share of it.
-    uint4 q0[KS], q1[KS], q2[KS], q3[KS], gA[St::kPasses], gB[St::kPasses];
-    fetch_q(tile, q0);
-    fetch_q(tile + kStep, q1);
-    fetch_g(tile, gA);
-    fetch_g(tile + kStep, gB);
-    asm volatile("" ::: "memory");  // the first pair's loads are issued first
-    auto pair = [&](int64_t t0, const uint4 (&qa)[KS], const uint4 (&qb)[KS], uint4 (&na)[KS],
-                    uint4 (&nb)[KS]) {
-      fetch_q(t0 + 2 * kStep, na);
-      fetch_q(t0 + 3 * kStep, nb);
-      f32x4 accA[ET], accB[ET];
-      float denA, denB;
-      products(std::true_type{}, t0, t0 + kStep, qa, qb, accA, accB, denA, denB);
-      finish(t0, accA, denA, gA);
-      fetch_g(t0 + 2 * kStep, gA);
-      finish(t0 + kStep, accB, denB, gB);
-      fetch_g(t0 + 3 * kStep, gB);
-    };
-    while (tile < n_end) {
-      pair(tile, q0, q1, q2, q3);
-      tile += 2 * kStep;
-      if (tile >= n_end) break;
-      pair(tile, q2, q3, q0, q1);
-      tile += 2 * kStep;
+  // The main loop is compiled twice, for grid rows of at least 16 tokens
+  // (the positions of a block's tokens from its first token's plus one carry
+  // per axis) and for shorter rows (a division per token), so that no branch
+  // on the row length sits inside it.
+  auto run = [&](auto row16) {
+    const int64_t kStep = kItem * a.am;
+    int64_t tile = n_begin + slot * kItem + 16 * wave;
+    if constexpr (kPair) {
+      // The workgroup takes the items slot, slot + m, ... of its super-range; a
+      // wave takes the 16-token block 16 wave of two consecutive ones (A, B) at
+      // a time.  q of the next pair is in flight during the current pair's
+      // products and gates; g of a block is refilled right after its gate and
+      // arrives during the next pair's products.  Refills are unconditional
+      // (blocks past the range read as zeros and their stores are dropped):
+      // with a branch around them the compiler waits for every outstanding
+      // load at the join.  With an odd item count the last pair's second block
+      // lies past the range; the plan takes pairs only where that block is
+      // off the critical path or a small share of it.
+      uint4 q0[KS], q1[KS], q2[KS], q3[KS], gA[St::kPasses], gB[St::kPasses];
+      fetch_q(tile, q0);
+      fetch_q(tile + kStep, q1);
+      fetch_g(tile, gA);
+      fetch_g(tile + kStep, gB);
+      asm volatile("" ::: "memory");  // the first pair's loads are issued first
+      auto pair = [&](int64_t t0, const uint4 (&qa)[KS], const uint4 (&qb)[KS], uint4 (&na)[KS],
+                      uint4 (&nb)[KS]) {
+        fetch_q(t0 + 2 * kStep, na);
+        fetch_q(t0 + 3 * kStep, nb);
+        f32x4 accA[ET], accB[ET];
+        float denA, denB;
+        products(std::true_type{}, row16, t0, t0 + kStep, qa, qb, accA, accB, denA, denB);
+        finish(t0, accA, denA, gA);
+        fetch_g(t0 + 2 * kStep, gA);
+        finish(t0 + kStep, accB, denB, gB);
+        fetch_g(t0 + 3 * kStep, gB);
+      };
+      while (tile < n_end) {
+        pair(tile, q0, q1, q2, q3);
+        tile += 2 * kStep;
+        if (tile >= n_end) break;
+        pair(tile, q2, q3, q0, q1);
+        tile += 2 * kStep;
+      }
+    } else {
+      // One block at a time, two in flight: buffer A holds block i while B
+      // receives block i + 1; once block i is done, A is refilled with block
+      // i + 2 before block i + 1 (in B) is processed, and so on (refills
+      // unconditional, as above).
+      uint4 qa[KS], ga[St::kPasses], qb[KS], gb[St::kPasses];
+      auto single = [&](int64_t t0, const uint4 (&cq)[KS], const uint4 (&cg)[St::kPasses]) {
+        f32x4 acc[ET], unused[ET];
+        float den, unused_den;
+        products(std::false_type{}, row16, t0, t0, cq, cq, acc, unused, den, unused_den);
+        finish(t0, acc, den, cg);
+      };
+      fetch_q(tile, qa);
+      fetch_g(tile, ga);
+      asm volatile("" ::: "memory");  // the first block's loads are issued first
+      fetch_q(tile + kStep, qb);
+      fetch_g(tile + kStep, gb);
+      while (tile < n_end) {
+        single(tile, qa, ga);
+        fetch_q(tile + 2 * kStep, qa);
+        fetch_g(tile + 2 * kStep, ga);
+        if (tile + kStep < n_end) single(tile + kStep, qb, gb);
+        fetch_q(tile + 3 * kStep, qb);
+        fetch_g(tile + 3 * kStep, gb);
+        tile += 2 * kStep;
+      }
     }
-  } else {
-    // One block at a time, two in flight: buffer A holds block i while B
-    // receives block i + 1; once block i is done, A is refilled with block
-    // i + 2 before block i + 1 (in B) is processed, and so on (refills
-    // unconditional, as above).
-    uint4 qa[KS], ga[St::kPasses], qb[KS], gb[St::kPasses];
-    auto single = [&](int64_t t0, const uint4 (&cq)[KS], const uint4 (&cg)[St::kPasses]) {
-      f32x4 acc[ET], unused[ET];
-      float den, unused_den;
-      products(std::false_type{}, t0, t0, cq, cq, acc, unused, den, unused_den);
-      finish(t0, acc, den, cg);
-    };
-    fetch_q(tile, qa);
-    fetch_g(tile, ga);
-    asm volatile("" ::: "memory");  // the first block's loads are issued first
-    fetch_q(tile + kStep, qb);
-    fetch_g(tile + kStep, gb);
-    while (tile < n_end) {
-      single(tile, qa, ga);
-      fetch_q(tile + 2 * kStep, qa);
-      fetch_g(tile + 2 * kStep, ga);
-      if (tile + kStep < n_end) single(tile + kStep, qb, gb);
-      fetch_q(tile + 3 * kStep, qb);
-      fetch_g(tile + 3 * kStep, gb);
-      tile += 2 * kStep;
-    }
-  }
+  };
+  if (a.Ws >= 16)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
   __builtin_amdgcn_s_waitcnt(0);  // prefetches past the range are still in flight
 }
 

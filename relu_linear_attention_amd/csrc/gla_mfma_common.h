@@ -70,10 +70,18 @@ __device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t o
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t *base, int64_t n,
                                                             int64_t n_end, uint32_t row_bytes,
                                                             int D) {
+  // rows = clamp(n_end - n, 0, 16) from the 32-bit halves of the difference,
+  // so that the comparisons stay on the scalar unit (it has no 64-bit
+  // ordered compares; the vector unit's would also pull the multiply below
+  // onto a quarter-rate vector instruction)
   const int64_t left = n_end - n;
-  const uint32_t rows = left <= 0 ? 0u : (left >= 16 ? 16u : (uint32_t)left);
-  const uint32_t bytes = __builtin_amdgcn_readfirstlane(
-      rows == 0 ? 0u : (rows - 1) * row_bytes + 2u * (uint32_t)D);
+  int32_t left_hi = __builtin_amdgcn_readfirstlane((int32_t)(left >> 32));
+  uint32_t left_lo = __builtin_amdgcn_readfirstlane((uint32_t)left);
+  asm("" : "+s"(left_hi), "+s"(left_lo));  // opaque: not folded back into a 64-bit compare
+  const uint32_t rows = left_hi < 0 ? 0u : (left_hi > 0 || left_lo >= 16u ? 16u : left_lo);
+  // (rows - 1) * row_bytes + 2 D, or 0 without rows
+  int32_t bytes = max((int32_t)(rows * row_bytes) - (int32_t)(row_bytes - 2u * (uint32_t)D), 0);
+  asm("" : "+s"(bytes));  // computed and kept on the scalar unit
   const uint64_t addr = (uint64_t)(uintptr_t)base;
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
@@ -114,6 +122,35 @@ __device__ __forceinline__ void token_pos(const MArgs &a, int64_t n, int &t, int
   t = (int)tt;
   h = (int)hh;
   w = (int)(r - hh * a.div_w.d);
+}
+
+// Grid position of this lane's token of the 16-token block that starts at
+// token t0 (lane offset o < 16; tokens past the range take the position of
+// its last token, n_end - 1).  kRow16 (a grid row holds at least 16
+// tokens): the block's first token is divided once on the scalar unit and
+// each lane adds its offset with at most one carry into h and one into t;
+// otherwise each lane divides its own index.  Token indices are below 2^31.
+template <bool kRow16>
+__device__ __forceinline__ void block_token_pos(const MArgs &a, int64_t t0, int64_t n_end, int o,
+                                                int &t, int &h, int &w) {
+  const uint32_t last = (uint32_t)(n_end - 1);
+  const uint32_t f0 = __builtin_amdgcn_readfirstlane((uint32_t)t0);
+  const uint32_t n = min(f0 + (uint32_t)o, last);
+  if constexpr (kRow16) {
+    const uint32_t first = f0 < last ? f0 : last;
+    int t0p, h0p, w0p;
+    token_pos(a, first, t0p, h0p, w0p);
+    const int ws = (int)a.div_w.d, hs = (int)a.Hs;
+    w = w0p + (int)(n - first);
+    const bool cw = w >= ws;
+    w = cw ? w - ws : w;
+    h = h0p + (cw ? 1 : 0);
+    const bool ch = h >= hs;
+    h = ch ? h - hs : h;
+    t = t0p + (ch ? 1 : 0);
+  } else {
+    token_pos(a, n, t, h, w);
+  }
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -190,8 +227,11 @@ struct TabSlice {
   // at the join.
   struct Lookup {
     int base, mt, mh, mw;
+    // 24-bit multiplies (full rate; grid positions and multipliers are far
+    // below 2^24)
     __device__ __forceinline__ int at(int t, int h, int w) const {
-      return base + t * mt + h * mh + w * mw;
+      return base + (int)(__umul24((unsigned)t, (unsigned)mt) + __umul24((unsigned)h, (unsigned)mh) +
+                          __umul24((unsigned)w, (unsigned)mw));
     }
   };
   __device__ __forceinline__ Lookup lookup(int axis, int pia) const {
