@@ -137,6 +137,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_kernel(
       kw[ks][3] = relu_bf16x2(kb[ks].w);
     }
 
+    // raised wave priority while this wave issues matrix-core products (as in
+    // the output stage: the other wave of the SIMD fills the gaps with its
+    // vector work)
+    __builtin_amdgcn_s_setprio(1);
     // ---- dv = RoPE(phi(k)) G
     {
       f32x4 acc[ET];
@@ -217,6 +221,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_mfma_kernel(
         }
       }
       mfma_drain();
+      __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         int axis, pia;

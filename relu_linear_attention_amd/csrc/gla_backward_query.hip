@@ -187,6 +187,10 @@ __global__ __launch_bounds__(kTokThreads) void bwd_token_mfma_kernel(
     int t, h, w;
     token_pos(a, valid ? n : n_end - 1, t, h, w);
 
+    // raised wave priority while this wave issues matrix-core products (as in
+    // the output stage: the other wave of the SIMD fills the gaps with its
+    // vector work)
+    __builtin_amdgcn_s_setprio(1);
     // ---- num = x S and den on the matrix cores
     uint32_t qw[KS][4];  // ReLU(q), packed bf16
     f32x4 acc[ET], accd = {0.f, 0.f, 0.f, 0.f};
@@ -241,6 +245,7 @@ __global__ __launch_bounds__(kTokThreads) void bwd_token_mfma_kernel(
       }
     }
     mfma_drain();
+    __builtin_amdgcn_s_setprio(0);
 
     // ---- y, s, dg, dnum and dout s . y (value i of acc[et]: feature
     // 16 et + 4 kg + i of token nl)
@@ -317,6 +322,7 @@ __global__ __launch_bounds__(kTokThreads) void bwd_token_mfma_kernel(
 
     // ---- S dnum on the matrix cores: A = S rows (16-byte pieces), B =
     // dnum (features 32 ks + 8 kg + 0..7); output tile pt = 2 ks' + half
+    __builtin_amdgcn_s_setprio(1);
     f32x4 acc2[ET];
 #pragma unroll
     for (int pt = 0; pt < ET; ++pt) acc2[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -346,6 +352,7 @@ __global__ __launch_bounds__(kTokThreads) void bwd_token_mfma_kernel(
       }
     }
     mfma_drain();
+    __builtin_amdgcn_s_setprio(0);
 
     // ---- dq = [RoPE^T(S dnum) + dden z] * 1[q > 0], in q's layout: lane
     // (token, kg) holds features 32 ks' + 8 kg + 4 half + i in acc2[2 ks' + half][i]
