@@ -125,7 +125,10 @@ __device__ __forceinline__ void fused_reduce_unit(const FusedReduce &fz, const f
 // the reads alone).
 template <int D>
 constexpr int kStateThreads = D == 128 ? 768 : 384;
-constexpr int kStatePrefetch = 2;  // 64-token steps of k and v in flight per producer thread
+// 64-token steps of k and v in flight per producer thread (three rather than
+// two: -2.5% per call over calls 5-24 at 720p/81f, where the shader clock is
+// low; unchanged at the settled clock)
+constexpr int kStatePrefetch = 3;
 
 template <int D>
 struct StateCfg {
