@@ -35,6 +35,11 @@ CASES = [
     ("bf16_d128_single_token", 1, 1, 1, 1, 3, 128, "bf16", 0, 1e4),
     ("bf16_d128_many_frames", 1, 64, 2, 3, 1, 128, "bf16", 0, 1e4),
     ("bf16_d128_strong_rotation", 1, 3, 4, 5, 2, 128, "bf16", 0, 7.0),
+    # grid rows of at least 16 tokens (the output stage's block positions from
+    # the block's first token plus carries): one-row frames, so 16-token
+    # blocks carry into the frame index; and a block-causal batch of two
+    ("bf16_d128_rows16_frame_carry", 1, 7, 1, 20, 2, 128, "bf16", 0, 1e4),
+    ("bf16_d64_rows16_blocks", 2, 6, 3, 17, 2, 64, "bf16", 3, 1e4),
 ]
 
 
