@@ -176,7 +176,7 @@ __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
                       const uint4 (&cqB)[KS], f32x4 (&accA)[ET], f32x4 (&accB)[ET], float &denA,
                       float &denB) {
     constexpr bool kTwo = decltype(nb2)::value;
-    constexpr bool kRow16 = decltype(row16)::value;
+    constexpr bool kCarry = decltype(row16)::value;
     // An offset the compiler cannot see through (always 0) keeps the
     // loop-invariant S-part reads inside the loop: hoisting all of them
     // would need 256 registers per lane.  It is a register-only asm, so it
@@ -185,8 +185,8 @@ __global__ __launch_bounds__(kApplyThreads) void apply_mfma_kernel(
     asm volatile("" : "+v"(opaque));
     const unsigned char *sh = s_sh + opaque, *sl = s_sl + opaque;
     int pA[3], pB[3];
-    block_token_pos<kRow16>(a, tA, n_end, nl, pA[0], pA[1], pA[2]);
-    if (kTwo) block_token_pos<kRow16>(a, tB, n_end, nl, pB[0], pB[1], pB[2]);
+    block_token_pos<kCarry>(a, tA, n_end, nl, pA[0], pA[1], pA[2]);
+    if (kTwo) block_token_pos<kCarry>(a, tB, n_end, nl, pB[0], pB[1], pB[2]);
     // Raised wave priority while this wave issues its products: of the two
     // waves on a SIMD, the one in its product phase then issues first, and
     // the other's gate and store work fills the gaps (the products phase

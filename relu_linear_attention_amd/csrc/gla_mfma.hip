@@ -253,13 +253,21 @@ __global__ __launch_bounds__(kStateThreads<D>, 3) void state_mfma_kernel(
   // consumer wave 0: the table offsets of step i's 64 tokens along each axis
   // (t, h, w rows; the slice's row bases are added by the reader)
   constexpr int gt = D / 32, gh = 3 * D / 64;  // groups per t row, per h or w row
+  // (rows past the chunk take its last token's position; they read as zero
+  // anyway).  Where a grid row holds at least the step's 64 tokens, the
+  // step's first token is divided on the scalar unit and each lane carries
+  // from it (no quarter-rate multiplies on this wave, whose SIMD also runs
+  // two producers).
   auto write_pos = [&](int64_t i) {
-    int64_t n = n_begin + i * kStateTile + lane;
-    if (n >= n_end) n = n_end - 1;  // rows past the chunk read as zero anyway
+    const int64_t n0 = n_begin + i * kStateTile;
     int t, h, w;
-    token_pos(a, n, t, h, w);
+    if (a.Ws >= kStateTile)
+      block_token_pos<true>(a, n0, n_end, lane, t, h, w);
+    else
+      block_token_pos<false>(a, n0, n_end, lane, t, h, w);
     *reinterpret_cast<int4 *>(s_pos + (int)(i & 1) * Cfg::POS_BYTES + 16 * lane) =
-        make_int4(t * gt, h * gh, w * gh, 0);
+        make_int4((int)__umul24((unsigned)t, gt), (int)__umul24((unsigned)h, gh),
+                  (int)__umul24((unsigned)w, gh), 0);
   };
 
   // The table slice goes to LDS while the first steps' rows are in flight:

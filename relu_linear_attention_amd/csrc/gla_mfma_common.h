@@ -124,19 +124,20 @@ __device__ __forceinline__ void token_pos(const MArgs &a, int64_t n, int &t, int
   w = (int)(r - hh * a.div_w.d);
 }
 
-// Grid position of this lane's token of the 16-token block that starts at
-// token t0 (lane offset o < 16; tokens past the range take the position of
-// its last token, n_end - 1).  kRow16 (a grid row holds at least 16
-// tokens): the block's first token is divided once on the scalar unit and
-// each lane adds its offset with at most one carry into h and one into t;
-// otherwise each lane divides its own index.  Token indices are below 2^31.
-template <bool kRow16>
+// Grid position of the token t0 + o, for a block of tokens that starts at
+// token t0 (uniform across the wave) and a lane offset o (tokens past the
+// range take the position of its last token, n_end - 1).  kCarry (the
+// caller guarantees o < Ws, the tokens of a grid row): the block's first
+// token is divided once on the scalar unit and each lane adds its offset
+// with at most one carry into h and one into t; otherwise each lane divides
+// its own index.  Token indices are below 2^31.
+template <bool kCarry>
 __device__ __forceinline__ void block_token_pos(const MArgs &a, int64_t t0, int64_t n_end, int o,
                                                 int &t, int &h, int &w) {
   const uint32_t last = (uint32_t)(n_end - 1);
   const uint32_t f0 = __builtin_amdgcn_readfirstlane((uint32_t)t0);
   const uint32_t n = min(f0 + (uint32_t)o, last);
-  if constexpr (kRow16) {
+  if constexpr (kCarry) {
     const uint32_t first = f0 < last ? f0 : last;
     int t0p, h0p, w0p;
     token_pos(a, first, t0p, h0p, w0p);
